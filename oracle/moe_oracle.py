@@ -1,0 +1,265 @@
+"""CPU oracle of the DeepSeekMoE layer forward — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  It shares no code with the HIP library and must never be used as
+a fallback for it.
+
+It is a plain, slow, float64 statement of what the layer computes, following
+the page "DeepSeek-V3 技術報告" (xyznot.com/zh-tw/paper/2412.19437),
+section 方法 §2 ("具備無輔助損失平衡機制的 DeepSeekMoE"):
+
+* output:    h'_t = u_t + sum_{i<=N_s} FFN^(s)_i(u_t) + sum_{i<=N_r} g_{i,t} FFN^(r)_i(u_t)
+* affinity:  s_{i,t} = Sigmoid(u_t^T e_i)
+* selection: g'_{i,t} = s_{i,t} if s_{i,t} + b_i is among the K_r largest of
+             {s_{j,t} + b_j}, else 0;  g_{i,t} = g'_{i,t} normalised
+* balance:   at the end of a step b_i <- b_i - gamma if expert i is overloaded,
+             b_i + gamma if underloaded, gamma = 0.001
+and, for the FP8 variant, the tile/block quantisation of the same page's
+核心概念 list (E4M3, 1x128 activation tiles, 128x128 weight blocks).
+
+Readings where the page leaves a step open (each is also listed with the
+other design notes of the repository):
+
+R1  "normalised" g = g' / sum_j g'_{j,t} (sum over the selected experts).
+R2  Topk ties: higher s+b first, then the lower expert index; NaN ranks last.
+R3  s is rounded to fp32 and s+b is an fp32 add before selection (the page fixes
+    no precision; fp32 is the precision of the GPU kernel, so both sides take
+    the integer decision in the same precision).
+R4  over/underloaded is against the step mean T*K_r/N_r, compared exactly in
+    integers as load_i*N_r vs T*K_r; equal loads leave b_i unchanged; the
+    update is one fp32 add of fp32(gamma).
+R5  a step is one routing call over a batch of T tokens.
+R6  FFN_i(x) = (SiLU(x W_gate^T) * (x W_up^T)) W_down^T with SiLU(v) = v*sigmoid(v),
+    no biases; weights stored [out_features, in_features]; all experts,
+    shared ones included, have intermediate width I.
+R7  no normalisation of u_t inside the layer; the residual is u_t as given.
+R8  FP8: scale = fp32(amax / 448) (E4M3FN maximum), amax = 0 -> scale 1,
+    code = E4M3FN round-to-nearest-even of fp32(x / scale), saturating at 448;
+    activations per 1x128 tile along the contraction dimension, weights per
+    128x128 block of the stored [out, in] matrix; both GEMM inputs quantised
+    (u before the gate/up projections, H before the down projection); the
+    residual and gates stay unquantised.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+# ----------------------------------------------------------------------------- routing
+
+def affinity(u: np.ndarray, centroids: np.ndarray) -> np.ndarray:
+    """s[t, i] = Sigmoid(u_t . e_i) in float64 (方法 §2, affinity equation)."""
+    z = np.asarray(u, dtype=np.float64) @ np.asarray(centroids, dtype=np.float64).T
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def selection_scores(s: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """c[t, i] = fp32(fp32(s) + b_i), the key Topk ranks (方法 §2, g' equation; R3)."""
+    return np.asarray(s, dtype=np.float32) + np.asarray(bias, dtype=np.float32)[None, :]
+
+
+def select_topk(c: np.ndarray, k: int):
+    """Indices of the K_r largest c per token, ordered by (c desc, index asc) (R2).
+
+    Returns (idx [T, K] int64, gap [T] float64) where gap is c_(K) - c_(K+1),
+    the margin by which the K-th pick beats the first unpicked expert
+    (+inf when K = N_r).
+    """
+    c = np.asarray(c)
+    order = np.argsort(-c, axis=1, kind="stable")
+    idx = order[:, :k]
+    if k < c.shape[1]:
+        ck = np.take_along_axis(c, order[:, k - 1:k], axis=1)[:, 0].astype(np.float64)
+        ck1 = np.take_along_axis(c, order[:, k:k + 1], axis=1)[:, 0].astype(np.float64)
+        gap = ck - ck1
+    else:
+        gap = np.full(c.shape[0], np.inf)
+    return idx, gap
+
+
+def gates(s: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """g[t, k] = s[t, idx[t,k]] / sum_k' s[t, idx[t,k']] (unbiased s; R1)."""
+    sel = np.take_along_axis(np.asarray(s, dtype=np.float64), idx, axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def expert_load(idx: np.ndarray, n_routed: int) -> np.ndarray:
+    """load[i] = number of (token, slot) assignments to expert i in the step."""
+    return np.bincount(np.asarray(idx).ravel(), minlength=n_routed).astype(np.int64)
+
+
+def route(u, centroids, bias, k: int):
+    """The routing half of the layer: (idx, gate, load, s, c, gap)."""
+    s = affinity(u, centroids)
+    c = selection_scores(s, bias)
+    idx, gap = select_topk(c, k)
+    return idx, gates(s, idx), expert_load(idx, np.asarray(centroids).shape[0]), s, c, gap
+
+
+def update_bias(bias: np.ndarray, load: np.ndarray, total_assignments: int, gamma: float = 0.001) -> np.ndarray:
+    """Auxiliary-loss-free bias update (方法 §2, last paragraph; R4)."""
+    b = np.asarray(bias, dtype=np.float32).copy()
+    n = b.shape[0]
+    ld = np.asarray(load, dtype=np.int64) * n
+    g = np.float32(gamma)
+    over = ld > total_assignments
+    under = ld < total_assignments
+    b[over] = b[over] - g
+    b[under] = b[under] + g
+    return b
+
+
+# ----------------------------------------------------------------------------- experts
+
+def silu(v: np.ndarray) -> np.ndarray:
+    return v / (1.0 + np.exp(-v))
+
+
+def swiglu_ffn(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """One expert FFN (R6): (SiLU(x Wg^T) * (x Wu^T)) Wd^T in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    a = x @ np.asarray(w_gate, dtype=np.float64).T
+    b = x @ np.asarray(w_up, dtype=np.float64).T
+    return (silu(a) * b) @ np.asarray(w_down, dtype=np.float64).T
+
+
+def layer_forward(u, idx, gate, routed, shared, ffn=swiglu_ffn, x=None) -> np.ndarray:
+    """h'_t = u_t + sum_s FFN^(s)_s(u_t) + sum_k gate[t,k] FFN^(r)_{idx[t,k]}(u_t) (方法 §2, h' equation).
+
+    routed: callable e -> (w_gate, w_up, w_down) of routed expert e;
+    shared: sequence of (w_gate, w_up, w_down), one per shared expert.
+    x: what the expert FFNs read (defaults to u; the FP8 variant passes the
+    fake-quantised u here while the residual stays u).
+    Rows of u, idx and gate correspond; pass a subset of rows to evaluate
+    only those tokens (every term is per token).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    x = u if x is None else np.asarray(x, dtype=np.float64)
+    out = u.copy()
+    for wg, wu, wd in shared:
+        out += ffn(x, wg, wu, wd)
+    idx = np.asarray(idx)
+    gate = np.asarray(gate, dtype=np.float64)
+    for e in np.unique(idx):
+        rows, slots = np.nonzero(idx == e)
+        wg, wu, wd = routed(int(e))
+        out[rows] += gate[rows, slots][:, None] * ffn(x[rows], wg, wu, wd)
+    return out
+
+
+def stacked(w_gate, w_up, w_down):
+    """Accessor e -> (w_gate[e], w_up[e], w_down[e]) over stacked [N, ...] arrays."""
+    return lambda e: (w_gate[e], w_up[e], w_down[e])
+
+
+# ----------------------------------------------------------------------------- FP8 (E4M3FN)
+
+def e4m3_round(y: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3FN value, ties to even, saturating at +-448 (R8).
+
+    E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; normal values
+    2^(e-7) * (1 + m/8), e = 1..15 (e = 15, m = 7 is NaN, so 448 is the
+    largest finite value); subnormals m/8 * 2^-6, spacing 2^-9.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    _, ex = np.frexp(a)                      # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)               # unbiased exponent of a, floored at the subnormal range
+    quantum = np.ldexp(1.0, e - 3)           # spacing of the 3-bit mantissa grid at that exponent
+    q = np.round(a / quantum) * quantum      # numpy rounds half to even
+    q = np.minimum(q, E4M3_MAX)
+    return np.copysign(q, y)
+
+
+def e4m3_encode(q: np.ndarray) -> np.ndarray:
+    """Bit patterns (uint8) of E4M3FN values that are already on the grid."""
+    q = np.asarray(q, dtype=np.float64)
+    sign = (np.signbit(q)).astype(np.uint8) << 7
+    a = np.abs(q)
+    code = np.zeros(a.shape, dtype=np.uint8)
+    sub = a < 2.0 ** -6
+    code[sub] = np.round(a[sub] / 2.0 ** -9).astype(np.uint8)
+    nz = ~sub
+    _, ex = np.frexp(a[nz])
+    e = ex - 1
+    m = np.round((a[nz] / np.ldexp(1.0, e) - 1.0) * 8).astype(np.int64)
+    code[nz] = ((e + 7) << 3 | m).astype(np.uint8)
+    return code | sign
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    code = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    s = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return s * v
+
+
+def _quant_block(x32: np.ndarray, axis_len_elems):
+    amax = np.max(np.abs(x32), axis=axis_len_elems)
+    scale = np.where(amax > 0, amax.astype(np.float32) / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    return scale
+
+
+def quantize_act_1x128(x: np.ndarray):
+    """Per-row, per-128-column tile quantisation of an activation matrix [rows, K] (R8).
+
+    Returns (codes uint8 [rows, K], scales fp32 [rows, K/128]).
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    r, k = x32.shape
+    assert k % 128 == 0
+    t = x32.reshape(r, k // 128, 128)
+    scale = _quant_block(t, 2)
+    y = (t / scale[:, :, None]).astype(np.float32)      # one fp32 division per element
+    q = e4m3_round(y)
+    return e4m3_encode(q).reshape(r, k), scale
+
+
+def quantize_weight_128x128(w: np.ndarray):
+    """Per-128x128-block quantisation of a stored [out, in] weight matrix (R8).
+
+    Returns (codes uint8 [out, in], scales fp32 [out/128, in/128]).
+    """
+    w32 = np.asarray(w, dtype=np.float32)
+    n, k = w32.shape
+    assert n % 128 == 0 and k % 128 == 0
+    t = w32.reshape(n // 128, 128, k // 128, 128)
+    scale = _quant_block(t, (1, 3))
+    y = (t / scale[:, None, :, None]).astype(np.float32)
+    q = e4m3_round(y)
+    return e4m3_encode(q).reshape(n, k), scale
+
+
+def dequant_act(codes, scale) -> np.ndarray:
+    r, k = codes.shape
+    return (e4m3_decode(codes).reshape(r, k // 128, 128) * np.asarray(scale, np.float64)[:, :, None]).reshape(r, k)
+
+
+def dequant_weight(codes, scale) -> np.ndarray:
+    n, k = codes.shape
+    v = e4m3_decode(codes).reshape(n // 128, 128, k // 128, 128) * np.asarray(scale, np.float64)[:, None, :, None]
+    return v.reshape(n, k)
+
+
+def swiglu_ffn_fp8(x_deq: np.ndarray, wq_gate, wq_up, wq_down) -> np.ndarray:
+    """Quantisation-faithful expert FFN: inputs already fake-quantised; H is quantised
+    per 1x128 tile along I after SiLU(a)*b, in fp32, before the down projection (R8)."""
+    a = x_deq @ dequant_weight(*wq_gate).T
+    b = x_deq @ dequant_weight(*wq_up).T
+    h = (silu(a) * b).astype(np.float32)
+    hq = dequant_act(*quantize_act_1x128(h))
+    return hq @ dequant_weight(*wq_down).T
+
+
+def layer_forward_fp8(u, idx, gate, routed_q, shared_q) -> np.ndarray:
+    """Quantisation-faithful FP8 layer: u quantised per 1x128 tile, weights per 128x128 block
+    (routed_q(e) / shared_q entries are ((codes, scale) x 3) from quantize_weight_128x128),
+    H quantised per 1x128 tile; float64 arithmetic on the dequantised values (R8)."""
+    u32 = np.asarray(u, dtype=np.float32)
+    x = dequant_act(*quantize_act_1x128(u32))
+    return layer_forward(u32, idx, gate, routed_q, shared_q, ffn=swiglu_ffn_fp8, x=x)
