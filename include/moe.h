@@ -1,0 +1,162 @@
+/* moe.h — C ABI of the MI355X (gfx950) DeepSeekMoE layer-forward library (libmoe.so).
+ *
+ * The layer is the one of the page "DeepSeek-V3 技術報告"
+ * (xyznot.com/zh-tw/paper/2412.19437), section 方法 §2:
+ *
+ *   h'_t = u_t + sum_{i<=N_s} FFN^(s)_i(u_t) + sum_{i<=N_r} g_{i,t} FFN^(r)_i(u_t)
+ *   s_{i,t} = Sigmoid(u_t^T e_i)
+ *   g'_{i,t} = s_{i,t} if s_{i,t} + b_i is among the K_r largest {s_{j,t} + b_j}, else 0
+ *   g_{i,t} = g'_{i,t} / sum_j g'_{j,t}
+ *   end of step: b_i <- b_i - gamma if expert i is overloaded, + gamma if underloaded
+ *
+ * with every expert FFN a bias-free SwiGLU, FFN(x) = (SiLU(x Wg^T) * (x Wu^T)) Wd^T,
+ * and, for MOE_DTYPE_FP8_B128, the FP8 scheme of the same page's 核心概念 list:
+ * E4M3 values with one fp32 scale per 1x128 activation tile and per 128x128
+ * weight block, accumulated in fp32.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *    keeps no hidden state, never allocates device memory, and never
+ *    synchronises: work is enqueued on `stream` and results are valid once the
+ *    stream has completed it.  Scratch memory is the caller's workspace.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is launched and the outputs are untouched.  A failed launch
+ *    returns MOE_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Row-major layouts throughout.  Expert weights are stored like
+ *    nn.Linear weights, [out_features, in_features]:
+ *        gate/up projections  [N, I, d]   (row n of expert e = output feature n)
+ *        down projection      [N, d, I]
+ *  - Results are bit-reproducible run to run (no floating-point atomics).
+ *  - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, negative size, K_r > N_r, ... */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle (see each call) */
+  MOE_ERR_WORKSPACE = 3,    /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_DTYPE_F32 = 0,       /* u, weights, out: fp32 */
+  MOE_DTYPE_BF16 = 1,      /* u, weights, out: bf16 */
+  MOE_DTYPE_FP8_B128 = 2   /* u, out: bf16; weights E4M3 codes + fp32 128x128 block scales */
+} moe_dtype;
+
+/* Layer shape.  Limits: tokens >= 0; 1 <= n_routed <= 1024; 1 <= top_k <= min(n_routed, 32);
+ * 0 <= n_shared <= 64; hidden, inter >= 1 and multiples of 8 (bf16) or of 128 (fp8);
+ * tokens * top_k < 2^31. */
+typedef struct moe_shape {
+  int32_t tokens;    /* T   */
+  int32_t hidden;    /* d   */
+  int32_t n_routed;  /* N_r */
+  int32_t top_k;     /* K_r */
+  int32_t n_shared;  /* N_s */
+  int32_t inter;     /* I   */
+  int32_t dtype;     /* moe_dtype */
+} moe_shape;
+
+/* Expert weights.  Element type: fp32 (F32), bf16 (BF16) or E4M3FN bytes (FP8_B128).
+ * The shared pointers may be NULL when n_shared == 0.  The *_scale pointers are
+ * read only for FP8_B128: one fp32 per 128x128 block of each stored matrix,
+ * laid out [N, out/128, in/128] (as written by moe_quantize_weights). */
+typedef struct moe_weights {
+  const void* w_gate;       /* [N_r, I, d] */
+  const void* w_up;         /* [N_r, I, d] */
+  const void* w_down;       /* [N_r, d, I] */
+  const void* sh_gate;      /* [N_s, I, d] */
+  const void* sh_up;        /* [N_s, I, d] */
+  const void* sh_down;      /* [N_s, d, I] */
+  const float* w_gate_scale;   /* [N_r, I/128, d/128] */
+  const float* w_up_scale;     /* [N_r, I/128, d/128] */
+  const float* w_down_scale;   /* [N_r, d/128, I/128] */
+  const float* sh_gate_scale;  /* [N_s, I/128, d/128] */
+  const float* sh_up_scale;    /* [N_s, I/128, d/128] */
+  const float* sh_down_scale;  /* [N_s, d/128, I/128] */
+} moe_weights;
+
+/* Number of stage boundaries moe_forward_profiled() records events at. */
+#define MOE_FORWARD_EVENTS 6
+
+/* Bytes of device workspace that moe_route and moe_forward need for `shape`
+ * (one buffer serves both).  Never fails for a valid shape. */
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Routing: sigmoid affinities, biased top-K_r selection, normalised gates, per-expert load
+ * (方法 §2: the s_{i,t} and g'_{i,t} equations).
+ *   u          [T, d]     fp32 (F32) or bf16 (BF16, FP8_B128)
+ *   centroids  [N_r, d]   fp32 (e_i)
+ *   bias       [N_r]      fp32 (b_i; only ranks experts, never enters a gate)
+ *   topk_idx   [T, K_r]   int32 out: selected experts ordered by s+b descending, ties to the
+ *                         lower index; NaN scores rank below every number
+ *   topk_gate  [T, K_r]   fp32 out: s_{i,t} / sum of the selected s, in topk_idx order
+ *   expert_load[N_r]      int32 out: number of (token, slot) picks of each expert
+ * Affinities are computed fp32-accurately (the contraction over d is exact products
+ * accumulated in fp32).  T == 0 writes expert_load = 0 and launches nothing else. */
+moe_status moe_route(const moe_shape* shape, const void* u, const float* centroids,
+                     const float* bias, int32_t* topk_idx, float* topk_gate,
+                     int32_t* expert_load, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Expert half of the layer (方法 §2, the h'_t equation): permutes tokens into per-expert
+ * segments, runs every routed expert on its tokens and every shared expert on all tokens
+ * (grouped SwiGLU GEMMs), and combines out_t = u_t + sum_s FFN_s(u_t) + sum_k gate FFN(u_t).
+ *   u          [T, d]     fp32 (F32) or bf16 (BF16, FP8_B128; FP8 quantises it per 1x128 tile)
+ *   topk_idx   [T, K_r]   int32 from moe_route (entries outside [0, N_r) are ignored)
+ *   topk_gate  [T, K_r]   fp32 from moe_route
+ *   out        [T, d]     fp32 (F32) or bf16 (BF16, FP8_B128); may not alias u
+ * FP8_B128 needs d % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED). */
+moe_status moe_forward(const moe_shape* shape, const void* u, const moe_weights* weights,
+                       const int32_t* topk_idx, const float* topk_gate, void* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_forward, recording events[0..MOE_FORWARD_EVENTS) on `stream` at its stage boundaries:
+ * [0] start, [1] after the token->expert permutation, [2] after activation quantisation
+ * (FP8 only; else right after [1]), [3] after the gate/up GEMM with SwiGLU, [4] after the
+ * down GEMM, [5] after the combine.  events must hold MOE_FORWARD_EVENTS created events
+ * (hipEvent_t); they are recorded, never created or destroyed, by the library. */
+moe_status moe_forward_profiled(const moe_shape* shape, const void* u, const moe_weights* weights,
+                                const int32_t* topk_idx, const float* topk_gate, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* events, int32_t n_events);
+
+/* Auxiliary-loss-free bias update (方法 §2, last paragraph), in place on bias[N_r] (fp32):
+ * expert i is overloaded when load_i * N_r > total_assignments (= T * K_r, i.e. above the
+ * step mean), underloaded when below; b_i <- b_i - gamma resp. b_i + gamma as one fp32 add;
+ * equal to the mean: unchanged. */
+moe_status moe_update_bias(int32_t n_routed, int64_t total_assignments, const int32_t* expert_load,
+                           float* bias, float gamma, hipStream_t stream);
+
+/* FP8 weight preparation (核心概念, FP8 item: 128x128 block scaling): quantises a stack of
+ * n_mats bf16 matrices [rows, cols] into E4M3FN codes [n_mats, rows, cols] and fp32 scales
+ * [n_mats, rows/128, cols/128]: scale = amax/448 (1 for an all-zero block), code =
+ * round-to-nearest-even E4M3FN of fp32(x / scale), saturating at 448.
+ * rows and cols must be multiples of 128. */
+moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16,
+                                uint8_t* codes, float* scales, hipStream_t stream);
+
+/* FP8 activation quantisation (核心概念, FP8 item: 1x128 tile scaling), the step moe_forward
+ * runs on u for FP8_B128: x [rows, cols] bf16 -> codes [rows, cols] E4M3FN and scales
+ * [rows, cols/128] fp32, same rounding rule as moe_quantize_weights.  cols % 128 == 0. */
+moe_status moe_quantize_act(int32_t rows, int32_t cols, const void* x_bf16, uint8_t* codes,
+                            float* scales, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* moe_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

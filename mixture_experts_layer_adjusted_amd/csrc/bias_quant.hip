@@ -1,0 +1,151 @@
+// Bias update and FP8 (E4M3FN) quantisers.
+//
+// Bias update: the end-of-step rule of 方法 §2 of "DeepSeek-V3 技術報告"
+// (xyznot.com/zh-tw/paper/2412.19437): an expert above the step's mean load
+// T*K_r/N_r (compared exactly as load*N_r vs T*K_r in 64-bit integers) loses
+// gamma, one below it gains gamma, one exactly at it keeps its bias.
+//
+// Quantisers: the fine-grained FP8 scheme of the same page's 核心概念 list, one
+// fp32 scale per 1x128 activation tile and per 128x128 weight block:
+// scale = amax / 448 (the E4M3FN maximum; 1 for an all-zero tile), code = E4M3FN
+// round-to-nearest-even of the correctly rounded fp32 quotient x / scale,
+// saturating at +-448.  The conversion is done in integer arithmetic from the
+// OCP OFP8 bit layout (bias 7, 3 mantissa bits, S.1111.111 = NaN).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__global__ void update_bias_kernel(int32_t n, int64_t total, const int32_t* __restrict__ load,
+                                   float* __restrict__ bias, float gamma) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int64_t l = (int64_t)load[i] * n;
+  float b = bias[i];
+  if (l > total) b = __fsub_rn(b, gamma);
+  else if (l < total) b = __fadd_rn(b, gamma);
+  bias[i] = b;
+}
+
+__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a != a) return 0x7Fu;                    // NaN
+  uint32_t code;
+  if (a < 0.015625f) {                         // below 2^-6: subnormal grid, spacing 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);   // exact scaling, round half to even; 8 -> min normal
+  } else {
+    const uint32_t ab = bits & 0x7FFFFFFFu;
+    const int e = (int)(ab >> 23) - 127;       // >= -6 here
+    const uint32_t frac = ab & 0x7FFFFFu;
+    uint32_t m = frac >> 20;                   // top 3 mantissa bits
+    const uint32_t rem = frac & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    int ee = e + 7;
+    if (m == 8u) {
+      m = 0u;
+      ++ee;
+    }
+    code = ee > 15 ? 0x7Fu : ((uint32_t)ee << 3) | m;
+    if (code > 0x7Eu) code = 0x7Eu;            // saturate at 448
+  }
+  return sign | code;
+}
+
+// one wavefront per 1x128 tile: each lane handles 2 consecutive elements
+__global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restrict__ x, int64_t rows, int32_t cols,
+                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tiles_per_row = cols / 128;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= rows * tiles_per_row) return;
+  const int64_t r = tile / tiles_per_row, c0 = (tile % tiles_per_row) * 128;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(x + r * cols + c0 + 2 * lane);
+  const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xFFFF0000u);
+  float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float scale = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  const uint32_t q0 = e4m3_from_f32(__fdiv_rn(v0, scale));
+  const uint32_t q1 = e4m3_from_f32(__fdiv_rn(v1, scale));
+  *reinterpret_cast<uint16_t*>(codes + r * cols + c0 + 2 * lane) = (uint16_t)(q0 | (q1 << 8));
+  if (lane == 0) scales[r * tiles_per_row + c0 / 128] = scale;
+}
+
+// one workgroup (256 threads) per 128x128 block: each thread handles 64 elements
+__global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __restrict__ w, int32_t rows,
+                                                           int32_t cols, uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int bc = cols / 128, br = rows / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t mat = blk / ((int64_t)br * bc);
+  const int rb = (int)((blk / bc) % br), cb = (int)(blk % bc);
+  const uint16_t* src = w + mat * (int64_t)rows * cols + (int64_t)rb * 128 * cols + cb * 128;
+  uint8_t* dst = codes + mat * (int64_t)rows * cols + (int64_t)rb * 128 * cols + cb * 128;
+  // thread: row (tid >> 1) , columns 64 * (tid & 1) .. + 64
+  const int r = tid >> 1, c = (tid & 1) * 64;
+  float v[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint4 q = *reinterpret_cast<const uint4*>(src + (int64_t)r * cols + c + 8 * i);
+    uint32_t ww[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(ww[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float scale = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = 16 * i + 4 * j;
+      o[j] = e4m3_from_f32(__fdiv_rn(v[b], scale)) | (e4m3_from_f32(__fdiv_rn(v[b + 1], scale)) << 8) |
+             (e4m3_from_f32(__fdiv_rn(v[b + 2], scale)) << 16) | (e4m3_from_f32(__fdiv_rn(v[b + 3], scale)) << 24);
+    }
+    *reinterpret_cast<uint4*>(dst + (int64_t)r * cols + c + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (tid == 0) scales[blk] = scale;
+}
+
+}  // namespace
+
+hipError_t launch_update_bias(int32_t n, int64_t total, const int32_t* load, float* bias, float gamma,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, n, total, load, bias,
+                     gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_act(int64_t rows, int32_t cols, const void* x, uint8_t* codes, float* scales,
+                               hipStream_t st) {
+  const int64_t tiles = rows * (cols / 128);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)ceil_div(tiles, 4)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w, uint8_t* codes,
+                                   float* scales, hipStream_t st) {
+  const int64_t blocks = (int64_t)n_mats * (rows / 128) * (cols / 128);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(w),
+                     rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,245 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout, and the ordered launch of the kernels of each call.
+#include <new>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_f32_swiglu(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_f32_down(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st);
+
+hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st) {
+  if (dtype == MOE_DTYPE_F32) return launch_gemm_f32_swiglu(g, st);
+  if (dtype == MOE_DTYPE_BF16) return launch_gemm_bf16_swiglu(g, st);
+  return launch_gemm_fp8_swiglu(g, st);
+}
+hipError_t launch_gemm_down(int dtype, const GemmOperands& g, hipStream_t st) {
+  if (dtype == MOE_DTYPE_F32) return launch_gemm_f32_down(g, st);
+  if (dtype == MOE_DTYPE_BF16) return launch_gemm_bf16_down(g, st);
+  return launch_gemm_fp8_down(g, st);
+}
+
+static size_t elem_bytes(int dtype) { return dtype == MOE_DTYPE_F32 ? 4 : 2; }
+
+WorkspacePlan plan_workspace(const moe_shape& s) {
+  WorkspacePlan p{};
+  const int64_t T = s.tokens, d = s.hidden, N = s.n_routed, K = s.top_k, Ns = s.n_shared, I = s.inter;
+  const bool fp8 = s.dtype == MOE_DTYPE_FP8_B128;
+  p.route_blocks = ceil_div(T, kRouteTokens);
+  p.chunks = ceil_div(T, kChunkTokens);
+  // sum_e ceil(load_e / M) <= (T*K + N*(M-1)) / M, plus N_s full-token segments
+  p.max_tiles = (T * K + N * (kTileM - 1)) / kTileM + Ns * ceil_div(T, kTileM);
+  p.max_rows = p.max_tiles * kTileM;
+  const size_t A = 256;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, A);
+    return at;
+  };
+  p.route_partial = take((size_t)p.route_blocks * N * 4);
+  p.route_bytes = o;
+  o = 0;
+  p.chunk_counts = take((size_t)p.chunks * N * 4);
+  p.chunk_base = take((size_t)p.chunks * N * 4);
+  p.seg_off = take((size_t)(N + Ns + 1) * 4);
+  p.seg_rows = take((size_t)(N + Ns) * 4);
+  p.tile_seg = take((size_t)p.max_tiles * 4);
+  p.row_token = take((size_t)p.max_rows * 4);
+  p.perm_row = take((size_t)T * K * 4);
+  p.h = take((size_t)p.max_rows * I * (fp8 ? 1 : elem_bytes(s.dtype)));
+  p.h_scale = take(fp8 ? (size_t)p.max_rows * (I / 128) * 4 : 0);
+  p.y = take((size_t)p.max_rows * d * elem_bytes(s.dtype == MOE_DTYPE_F32 ? MOE_DTYPE_F32 : MOE_DTYPE_BF16));
+  p.u_q = take(fp8 ? (size_t)T * d : 0);
+  p.u_scale = take(fp8 ? (size_t)T * (d / 128) * 4 : 0);
+  p.forward_bytes = o;
+  p.total = p.route_bytes > p.forward_bytes ? p.route_bytes : p.forward_bytes;
+  return p;
+}
+
+static moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->tokens < 0 || s->hidden < 1 || s->inter < 1 || s->n_routed < 1 || s->top_k < 1 || s->n_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->top_k > s->n_routed) return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16 && s->dtype != MOE_DTYPE_FP8_B128)
+    return MOE_ERR_INVALID_ARG;
+  if (s->n_routed > kMaxRouted || s->top_k > kMaxTopK || s->n_shared > kMaxShared) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden % 8 != 0 || s->inter % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype == MOE_DTYPE_FP8_B128 && (s->hidden % 128 != 0 || s->inter % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  const int64_t T = s->tokens, K = s->top_k;
+  if (T * K >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  const int64_t max_tiles = (T * K + (int64_t)s->n_routed * (kTileM - 1)) / kTileM + s->n_shared * ceil_div(T, kTileM);
+  if (max_tiles * kTileM >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+static moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_weights* w, const int32_t* idx,
+                               const float* gate, void* out, void* ws, size_t ws_bytes, hipStream_t st,
+                               hipEvent_t* ev, int32_t n_ev) {
+  moe_status rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  const moe_shape& s = *shape;
+  if (ev && n_ev < MOE_FORWARD_EVENTS) return MOE_ERR_INVALID_ARG;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], st) : hipSuccess; };
+  if (s.tokens == 0) {
+    for (int i = 0; i < (ev ? MOE_FORWARD_EVENTS : 0); ++i)
+      if (mark(i) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+  }
+  if (!u || !w || !idx || !gate || !out || !ws) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = s.dtype == MOE_DTYPE_FP8_B128;
+  if (fp8 && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return MOE_ERR_INVALID_ARG;
+  if (fp8 && s.n_shared > 0 && (!w->sh_gate_scale || !w->sh_up_scale || !w->sh_down_scale))
+    return MOE_ERR_INVALID_ARG;
+  if (out == u) return MOE_ERR_INVALID_ARG;
+  const WorkspacePlan p = plan_workspace(s);
+  if (ws_bytes < p.total) return MOE_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(ws);
+
+  if (mark(0) != hipSuccess) return MOE_ERR_HIP;
+  if ((rc = hip_status(launch_permute(s, idx, p, wsb, st))) != MOE_OK) return rc;
+  if (mark(1) != hipSuccess) return MOE_ERR_HIP;
+  const void* act = u;
+  const float* act_scale = nullptr;
+  if (fp8) {
+    uint8_t* uq = reinterpret_cast<uint8_t*>(wsb + p.u_q);
+    float* us = reinterpret_cast<float*>(wsb + p.u_scale);
+    if ((rc = hip_status(launch_quantize_act(s.tokens, s.hidden, u, uq, us, st))) != MOE_OK) return rc;
+    act = uq;
+    act_scale = us;
+  }
+  if (mark(2) != hipSuccess) return MOE_ERR_HIP;
+
+  GemmOperands g1{};
+  g1.act = act;
+  g1.act_scale = act_scale;
+  g1.row_token = reinterpret_cast<const int32_t*>(wsb + p.row_token);
+  g1.w_routed[0] = w->w_gate;
+  g1.w_routed[1] = w->w_up;
+  g1.w_shared[0] = w->sh_gate;
+  g1.w_shared[1] = w->sh_up;
+  g1.s_routed[0] = w->w_gate_scale;
+  g1.s_routed[1] = w->w_up_scale;
+  g1.s_shared[0] = w->sh_gate_scale;
+  g1.s_shared[1] = w->sh_up_scale;
+  g1.tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
+  g1.n_routed = s.n_routed;
+  g1.K = s.hidden;
+  g1.N = s.inter;
+  g1.max_tiles = p.max_tiles;
+  g1.out = wsb + p.h;
+  g1.out_scale = fp8 ? reinterpret_cast<float*>(wsb + p.h_scale) : nullptr;
+  if ((rc = hip_status(launch_gemm_swiglu(s.dtype, g1, st))) != MOE_OK) return rc;
+  if (mark(3) != hipSuccess) return MOE_ERR_HIP;
+
+  GemmOperands g2{};
+  g2.act = wsb + p.h;
+  g2.act_scale = g1.out_scale;
+  g2.row_token = nullptr;
+  g2.w_routed[0] = w->w_down;
+  g2.w_shared[0] = w->sh_down;
+  g2.s_routed[0] = w->w_down_scale;
+  g2.s_shared[0] = w->sh_down_scale;
+  g2.tile_seg = g1.tile_seg;
+  g2.n_routed = s.n_routed;
+  g2.K = s.inter;
+  g2.N = s.hidden;
+  g2.max_tiles = p.max_tiles;
+  g2.out = wsb + p.y;
+  if ((rc = hip_status(launch_gemm_down(s.dtype, g2, st))) != MOE_OK) return rc;
+  if (mark(4) != hipSuccess) return MOE_ERR_HIP;
+
+  if ((rc = hip_status(launch_combine(s, u, gate, p, wsb, out, st))) != MOE_OK) return rc;
+  if (mark(5) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = plan_workspace(*shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* shape, const void* u, const float* centroids, const float* bias,
+                     int32_t* topk_idx, float* topk_gate, int32_t* expert_load, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  moe_status rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!expert_load) return MOE_ERR_INVALID_ARG;
+  if (shape->tokens > 0 && (!u || !centroids || !bias || !topk_idx || !topk_gate || !workspace))
+    return MOE_ERR_INVALID_ARG;
+  const WorkspacePlan p = plan_workspace(*shape);
+  if (shape->tokens > 0 && workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  int32_t* partial = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.route_partial);
+  return hip_status(launch_route(*shape, u, centroids, bias, topk_idx, topk_gate, expert_load, partial,
+                                 p.route_blocks, stream));
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* u, const moe_weights* weights, const int32_t* topk_idx,
+                       const float* topk_gate, void* out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return forward_impl(shape, u, weights, topk_idx, topk_gate, out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_forward_profiled(const moe_shape* shape, const void* u, const moe_weights* weights,
+                                const int32_t* topk_idx, const float* topk_gate, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  return forward_impl(shape, u, weights, topk_idx, topk_gate, out, workspace, workspace_bytes, stream, events,
+                      n_events);
+}
+
+moe_status moe_update_bias(int32_t n_routed, int64_t total_assignments, const int32_t* expert_load, float* bias,
+                           float gamma, hipStream_t stream) {
+  if (n_routed < 1 || total_assignments < 0 || !expert_load || !bias) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_update_bias(n_routed, total_assignments, expert_load, bias, gamma, stream));
+}
+
+moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w_bf16, uint8_t* codes,
+                                float* scales, hipStream_t stream) {
+  if (n_mats < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (rows % 128 != 0 || cols % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)n_mats * rows * cols == 0) return MOE_OK;
+  if (!w_bf16 || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_weights(n_mats, rows, cols, w_bf16, codes, scales, stream));
+}
+
+moe_status moe_quantize_act(int32_t rows, int32_t cols, const void* x_bf16, uint8_t* codes, float* scales,
+                            hipStream_t stream) {
+  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (cols % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)rows * cols == 0) return MOE_OK;
+  if (!x_bf16 || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_act(rows, cols, x_bf16, codes, scales, stream));
+}
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal declarations shared by the host API (moe_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Rows per M-tile of the grouped GEMMs.  Every expert segment of the permuted
+// layout starts on a multiple of kTileM rows.
+constexpr int kTileM = 128;
+// Tokens per routing workgroup, and per permutation chunk.
+constexpr int kRouteTokens = 32;
+constexpr int kChunkTokens = 256;
+constexpr int kMaxRouted = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxShared = 64;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+// Byte offsets of every buffer inside the caller's workspace.
+struct WorkspacePlan {
+  // routing
+  size_t route_partial;     // int32 [route_blocks, N_r]
+  // forward
+  size_t chunk_counts;      // int32 [chunks, N_r]
+  size_t chunk_base;        // int32 [chunks, N_r]
+  size_t seg_off;           // int32 [N_r + N_s + 1]   first padded row of each segment
+  size_t seg_rows;          // int32 [N_r + N_s]       real rows of each segment
+  size_t tile_seg;          // int32 [max_tiles]       segment of each M-tile, -1 past the end
+  size_t row_token;         // int32 [max_rows]        token of each permuted row, -1 for padding
+  size_t perm_row;          // int32 [T, K_r]          permuted row of each (token, slot), -1 if skipped
+  size_t h;                 // [max_rows, I]  bf16 / fp32 / e4m3
+  size_t h_scale;           // fp32 [max_rows, I/128]  (fp8)
+  size_t y;                 // [max_rows, d]  bf16 / fp32
+  size_t u_q;               // e4m3 [T, d]             (fp8)
+  size_t u_scale;           // fp32 [T, d/128]         (fp8)
+  size_t route_bytes, forward_bytes, total;
+  int64_t route_blocks, chunks, max_tiles, max_rows;
+};
+
+WorkspacePlan plan_workspace(const moe_shape& s);
+
+// ---- launchers (return hipSuccess or the launch error) ----
+hipError_t launch_route(const moe_shape& s, const void* u, const float* centroids, const float* bias,
+                        int32_t* idx, float* gate, int32_t* load, int32_t* partial, int64_t blocks,
+                        hipStream_t st);
+
+hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const WorkspacePlan& p, char* ws,
+                          hipStream_t st);
+
+struct GemmOperands {
+  const void* act;           // activation rows (gathered through row_token when non-null)
+  const float* act_scale;    // fp8 only: [rows, K/128]
+  const int32_t* row_token;  // gate/up GEMM: token of each permuted row; down GEMM: nullptr
+  const void* w_routed[2];   // [N_r, N, K] gate & up (SwiGLU) or down
+  const void* w_shared[2];   // [N_s, N, K]
+  const float* s_routed[2];  // fp8 block scales [N_r, N/128, K/128]
+  const float* s_shared[2];
+  const int32_t* tile_seg;
+  int n_routed;
+  int K, N;                  // contraction length, output features per expert
+  int64_t max_tiles;
+  void* out;                 // [max_rows, N]
+  float* out_scale;          // fp8 SwiGLU output: [max_rows, N/128]
+};
+
+hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_down(int dtype, const GemmOperands& g, hipStream_t st);
+
+hipError_t launch_combine(const moe_shape& s, const void* u, const float* gate, const WorkspacePlan& p,
+                          const char* ws, void* out, hipStream_t st);
+
+hipError_t launch_update_bias(int32_t n, int64_t total, const int32_t* load, float* bias, float gamma,
+                              hipStream_t st);
+
+hipError_t launch_quantize_act(int64_t rows, int32_t cols, const void* x, uint8_t* codes, float* scales,
+                               hipStream_t st);
+hipError_t launch_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, const void* w,
+                                   uint8_t* codes, float* scales, hipStream_t st);
+
+}  // namespace moe

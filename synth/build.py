@@ -12,7 +12,7 @@ def build(verbose: bool = False) -> None:
     src = os.path.join(_HERE, "csrc")
     host_cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC",
                 os.path.join(src, "synth_host.c"), "-o", os.path.join(_HERE, "_synth_host.so")]
-    dev_cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-ffp-contract=off", "-shared", "-fPIC",
+    dev_cmd = [HIPCC, "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-ffp-contract=off", "-shared", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                os.path.join(src, "synth_fill.hip"), "-o", os.path.join(_HERE, "_synth_fill.so")]
     for cmd in (host_cmd, dev_cmd):

@@ -28,6 +28,7 @@ def device_lib():
     """The HIP filler; raises if it has not been built."""
     global _device
     if _device is None:
+        import torch  # noqa: F401  (map torch's HIP runtime first, so the filler binds to it)
         if not os.path.exists(DEVICE_LIB):
             raise RuntimeError(f"device filler not built: {DEVICE_LIB} (run __graft_entry__.build())")
         lib = ctypes.CDLL(DEVICE_LIB)

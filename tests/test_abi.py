@@ -1,0 +1,115 @@
+"""The C-ABI library: it loads, exports every entry point include/moe.h declares, and its
+host-side validation returns the documented status codes (no GPU work is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_adjusted_amd as moe
+from mixture_experts_layer_adjusted_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("moe_route", "moe_forward", "moe_update_bias", "moe_workspace_size", "moe_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert sorted(binding.exported_symbols()) == _declared()
+
+
+def test_status_strings():
+    assert moe.moe_status_string(0) == "ok"
+    assert moe.moe_status_string(3) == "workspace too small"
+    assert moe.moe_status_string(99) == "unknown status"
+
+
+def _ws(*a):
+    return moe.moe_workspace_size(moe.make_shape(*a))
+
+
+def test_workspace_size_valid_and_monotone():
+    a = _ws(256, 7168, 256, 8, 1, 2048, moe.MOE_DTYPE_BF16)
+    b = _ws(16384, 7168, 256, 8, 1, 2048, moe.MOE_DTYPE_BF16)
+    assert 0 < a < b
+    assert _ws(0, 128, 16, 4, 1, 64, moe.MOE_DTYPE_F32) >= 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((64, 128, 16, 17, 1, 64, 0), 1),             # K_r > N_r
+    ((-1, 128, 16, 4, 1, 64, 0), 1),              # negative T
+    ((64, 128, 16, 4, 1, 64, 7), 1),              # unknown dtype
+    ((64, 100, 16, 4, 1, 64, 1), 2),              # d not a multiple of 8
+    ((64, 1024, 16, 4, 1, 192, 2), 2),            # fp8 with I % 128 != 0
+    ((64, 128, 2048, 4, 1, 64, 1), 2),            # N_r above the router's limit
+    ((64, 128, 64, 40, 1, 64, 1), 2),             # K_r above 32
+])
+def test_invalid_shapes_are_rejected(args, status):
+    with pytest.raises(moe.MoeError) as ei:
+        _ws(*args)
+    assert ei.value.status == status
+
+
+def test_null_and_workspace_errors_before_launch():
+    lib = binding.raw_lib()
+    s = moe.make_shape(64, 128, 16, 4, 1, 64, moe.MOE_DTYPE_F32)
+    # null output pointers -> invalid argument
+    rc = lib.moe_route(ctypes.byref(s), None, None, None, None, None, None, None, 0, None)
+    assert rc == 1
+    # plausible (never dereferenced) pointers with a too-small workspace -> workspace error, nothing launched
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.moe_route(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 16, None)
+    assert rc == 3
+    w = moe.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    rc = lib.moe_forward(ctypes.byref(s), fake, ctypes.byref(w), fake, fake, ctypes.c_void_p(0x2000), fake, 16, None)
+    assert rc == 3
+    # out aliasing u is rejected
+    rc = lib.moe_forward(ctypes.byref(s), fake, ctypes.byref(w), fake, fake, fake, fake, 1 << 40, None)
+    assert rc == 1
+    # missing shared weights with N_s > 0
+    w2 = moe.Weights(0x1000, 0x1000, 0x1000, None, None, None)
+    rc = lib.moe_forward(ctypes.byref(s), fake, ctypes.byref(w2), fake, fake, ctypes.c_void_p(0x2000), fake,
+                         1 << 40, None)
+    assert rc == 1
+    assert lib.moe_update_bias(0, 10, fake, fake, ctypes.c_float(0.001), None) == 1
+    assert lib.moe_quantize_weights(1, 100, 128, fake, fake, fake, None) == 2
+    assert lib.moe_quantize_act(4, 130, fake, fake, fake, None) == 2
+
+
+def test_zero_tokens_forward_is_a_noop():
+    lib = binding.raw_lib()
+    s = moe.make_shape(0, 128, 16, 4, 1, 64, moe.MOE_DTYPE_F32)
+    w = moe.Weights()
+    assert lib.moe_forward(ctypes.byref(s), None, ctypes.byref(w), None, None, None, None, 0, None) == 0
+
+
+def test_library_does_not_reference_the_oracle():
+    csrc = os.path.join(ROOT, "mixture_experts_layer_adjusted_amd")
+    for dirpath, _, files in os.walk(csrc):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower().replace("oracle-free", ""), f
+
+
+def test_single_hip_runtime_in_process():
+    # torch bundles a HIP runtime with the same soname as ROCm's; the binding maps
+    # torch's first so that libmoe.so (and the device filler) bind to that one copy
+    import synth.native
+    synth.native.device_lib()
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    hsa = {ln.split()[-1] for ln in maps if "libhsa-runtime64" in ln}
+    assert len(hip) == 1 and len(hsa) <= 1, (hip, hsa)

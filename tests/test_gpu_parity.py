@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 CPU oracle.
+
+Every input is drawn from the seeded streams of synth/ (host copies for the
+oracle, device copies for the library), never from the library's output.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe_oracle as O
+from synth import bf16_bits_to_f32, host
+from synth.configs import CONFIGS, LayerConfig
+from synth.device import fill_normal_, host_to_device, make_device_inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from helpers import TOL, Runner, check_routing, quantize_fp8_weights, rel_err, to_host_f32
+
+
+def _f(a):
+    return bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, np.float32)
+
+
+def _host_layer(cfg):
+    h = host.make_host_inputs(cfg)
+    return h, {k: _f(v) for k, v in h.items()}
+
+
+def _edge(name, T, d, N, K, Ns, I, dtype="bf16", bias="uniform0.01", cid=50):
+    return LayerConfig(cid, name, T, d, N, K, Ns, I, dtype, bias)
+
+
+def _oracle_forward_full(hf, cfg, idx, gate):
+    shared = list(zip(hf["sh_gate"], hf["sh_up"], hf["sh_down"]))
+    return O.layer_forward(hf["u"], idx, gate, O.stacked(hf["w_gate"], hf["w_up"], hf["w_down"]), shared)
+
+
+def _run_and_check_small(cfg, bias_override=None, check_forward=True):
+    h, hf = _host_layer(cfg)
+    if bias_override is not None:
+        h["bias"] = bias_override.astype(np.float32)
+        hf["bias"] = h["bias"]
+    dev = host_to_device(h)
+    r = Runner(cfg, dev)
+    r.route()
+    r.forward()
+    torch.cuda.synchronize()
+    idx_g = r.idx.cpu().numpy()
+    gate_g = r.gate.cpu().numpy()
+    load_g = r.load.cpu().numpy()
+    idx_o, g_o, load_o, s_o, c_o, gap_o = O.route(hf["u"], hf["centroids"], hf["bias"], cfg.top_k)
+    exempt = check_routing(idx_g, gate_g, load_g, s_o, c_o, idx_o, gap_o, cfg.n_routed)
+    if check_forward:
+        y_ref = _oracle_forward_full(hf, cfg, idx_g.astype(np.int64), O.gates(s_o, idx_g.astype(np.int64)))
+        y = to_host_f32(r.out)
+        e_all, e_exp = rel_err(y, y_ref, hf["u"])
+        tol = TOL[cfg.dtype]
+        assert e_all <= tol and e_exp <= tol, (e_all, e_exp)
+    return r, exempt
+
+
+# ----------------------------------------------------------------------------- generator
+
+def test_device_filler_matches_numpy():
+    key = synth.stream_key(0, 3, synth.TAG_W_UP, 9)
+    for dt in (torch.float32, torch.bfloat16):
+        t = fill_normal_(torch.empty(100003, dtype=dt, device="cuda"), key, 0.05, start=777777)
+        v = synth.normal_f32(key, 100003, 0.05, 777777)
+        want = synth.f32_to_bf16_bits(v) if dt == torch.bfloat16 else v
+        got = t.view(torch.int16).cpu().numpy().view(np.uint16) if dt == torch.bfloat16 else t.cpu().numpy()
+        assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- configurations 0 and 1
+
+@pytest.mark.parametrize("cid", [0, 1])
+def test_layer_parity_small_configs(cid):
+    _run_and_check_small(CONFIGS[cid])
+
+
+def test_config0_bias_update_bit_exact():
+    cfg = CONFIGS[0]
+    h, hf = _host_layer(cfg)
+    dev = host_to_device(h)
+    r = Runner(cfg, dev)
+    r.route()
+    bias = dev["bias"].clone()
+    r.update_bias(bias)
+    torch.cuda.synchronize()
+    want = O.update_bias(hf["bias"], r.load.cpu().numpy(), cfg.tokens * cfg.top_k, cfg.gamma)
+    assert np.array_equal(bias.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_determinism_bitwise():
+    cfg = CONFIGS[1]
+    h, _ = _host_layer(cfg)
+    dev = host_to_device(h)
+    r = Runner(cfg, dev)
+    outs = []
+    for _ in range(2):
+        r.route()
+        r.forward()
+        outs.append((r.idx.clone(), r.gate.clone(), r.load.clone(), r.out.clone()))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("cfg", [
+    _edge("one-token", 1, 256, 16, 4, 1, 128),
+    _edge("ragged-tokens", 300, 256, 16, 4, 1, 128),
+    _edge("no-shared", 200, 256, 16, 4, 0, 128),
+    _edge("k-equals-n", 70, 128, 8, 8, 1, 64),
+    _edge("small-inter", 150, 128, 16, 2, 1, 64),
+    _edge("ragged-k-tail", 140, 136, 16, 3, 2, 72),
+    _edge("many-experts", 96, 128, 512, 8, 1, 64),
+    _edge("fp32-ragged", 77, 96, 12, 3, 2, 40, dtype="f32"),
+])
+def test_edge_shapes(cfg):
+    _run_and_check_small(cfg)
+
+
+def test_expert_with_zero_load_and_spiked_experts():
+    cfg = _edge("bias-spike", 256, 256, 32, 4, 1, 128)
+    b = host.bias_vector(cfg).copy()
+    b[5] = -10.0            # never picked
+    b[[1, 7, 9]] = 10.0     # picked by every token
+    r, _ = _run_and_check_small(cfg, bias_override=b)
+    load = r.load.cpu().numpy()
+    assert load[5] == 0 and load[1] == load[7] == load[9] == 256
+
+
+# ----------------------------------------------------------------------------- fp8 quantisers
+
+def test_quantize_act_bit_exact():
+    rows, cols = 300, 1024
+    x = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    fill_normal_(x, synth.stream_key(0, 4, synth.TAG_U, 0), 3.0)
+    x[7, 128:256] = 0
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda")
+    import mixture_experts_layer_adjusted_amd as moe
+    moe.moe_quantize_act(rows, cols, x, codes, scales)
+    torch.cuda.synchronize()
+    c_o, s_o = O.quantize_act_1x128(to_host_f32(x))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), c_o)
+
+
+def test_quantize_weights_bit_exact():
+    n, rows, cols = 3, 256, 640
+    w = torch.empty((n, rows, cols), dtype=torch.bfloat16, device="cuda")
+    fill_normal_(w, synth.stream_key(0, 4, synth.TAG_W_GATE, 3), 0.02)
+    w[1, :128, 128:256] = 0
+    codes = torch.empty((n, rows, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, rows // 128, cols // 128), dtype=torch.float32, device="cuda")
+    import mixture_experts_layer_adjusted_amd as moe
+    moe.moe_quantize_weights(n, rows, cols, w, codes, scales)
+    torch.cuda.synchronize()
+    wf = to_host_f32(w)
+    for i in range(n):
+        c_o, s_o = O.quantize_weight_128x128(wf[i])
+        assert np.array_equal(scales[i].cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+        assert np.array_equal(codes[i].cpu().numpy(), c_o)
+
+
+# ----------------------------------------------------------------------------- V3 shapes (sampled outputs)
+
+class _HostExperts:
+    """Host (oracle-side) copies of expert weights, regenerated from the seeded streams."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+
+    def routed(self, e):
+        return tuple(_f(w) for w in host.expert_weights(self.cfg, e))
+
+    def shared(self):
+        return [tuple(_f(w) for w in host.expert_weights(self.cfg, s, shared=True))
+                for s in range(self.cfg.n_shared)]
+
+
+def _v3_check(cfg, sample_tokens, steps=1):
+    dev = make_device_inputs(cfg)
+    r = Runner(cfg, dev)
+    u_host = _f(host.token_rows(cfg))
+    c_host = host.centroids(cfg)
+    s_or = O.affinity(u_host, c_host)
+    bias_h = host.bias_vector(cfg)
+    bias_d = dev["bias"].clone()
+    ratios = []
+    for step in range(steps):
+        r.route(bias_d)
+        if step == 0:
+            r.forward()
+        torch.cuda.synchronize()
+        idx_g = r.idx.cpu().numpy()
+        load_g = r.load.cpu().numpy()
+        c_or = O.selection_scores(s_or, bias_h)
+        idx_o, gap_o = O.select_topk(c_or, cfg.top_k)
+        check_routing(idx_g, r.gate.cpu().numpy(), load_g, s_or, c_or, idx_o, gap_o, cfg.n_routed)
+        ratios.append(load_g.max() / load_g.mean())
+        if step == 0:
+            ex = _HostExperts(cfg)
+            toks = np.asarray(sample_tokens)
+            idx_s = idx_g[toks].astype(np.int64)
+            y_ref = O.layer_forward(u_host[toks], idx_s, O.gates(s_or[toks], idx_s), ex.routed, ex.shared())
+            y = to_host_f32(r.out)[toks]
+            e_all, e_exp = rel_err(y, y_ref, u_host[toks])
+            assert e_all <= TOL[cfg.dtype] and e_exp <= TOL[cfg.dtype], (e_all, e_exp)
+        r.update_bias(bias_d)
+        torch.cuda.synchronize()
+        want = O.update_bias(bias_h, load_g, cfg.tokens * cfg.top_k, cfg.gamma)
+        assert np.array_equal(bias_d.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        bias_h = want
+    return ratios
+
+
+def test_config2_decode_shape():
+    cfg = CONFIGS[2]
+    _v3_check(cfg, np.arange(0, 256, 37))
+
+
+def test_config3_prefill_20_steps():
+    cfg = CONFIGS[3]
+    rng = np.random.default_rng(3)
+    ratios = _v3_check(cfg, rng.choice(cfg.tokens, 6, replace=False), steps=cfg.steps)
+    print("load max/mean per step:", [round(float(x), 3) for x in ratios])
+    assert ratios[0] > 4.0   # the Zipf-scaled centroids skew the load
