@@ -117,7 +117,12 @@ def moe_forward(shape, u, weights: Weights, topk_idx, topk_gate, out, workspace,
 
 
 def moe_forward_profiled(shape, u, weights: Weights, topk_idx, topk_gate, out, workspace, events, stream=None):
-    """events: MOE_FORWARD_EVENTS torch.cuda.Event(enable_timing=True) objects, recorded in order."""
+    """events: MOE_FORWARD_EVENTS torch.cuda.Event(enable_timing=True) objects, recorded in order.
+
+    torch creates an event's HIP handle on its first record(); record each event once
+    beforehand so that a handle exists."""
+    if any(not e.cuda_event for e in events):
+        raise ValueError("moe_forward_profiled: an event has no HIP handle yet (record it once first)")
     arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     _check("moe_forward_profiled", _lib.moe_forward_profiled(
         ctypes.byref(shape), _ptr(u), ctypes.byref(weights), _ptr(topk_idx), _ptr(topk_gate), _ptr(out),
