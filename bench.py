@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--workload", default="v3-prefill-bf16-zipf", choices=sorted(WORKLOADS))
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return p.parse_args()
 
 
@@ -87,6 +89,12 @@ def main():
 
     cfg = CONFIGS[WORKLOADS[args.workload]]
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     dev = make_device_inputs(cfg)
     T, d, N, K, Ns, I = cfg.tokens, cfg.hidden, cfg.n_routed, cfg.top_k, cfg.n_shared, cfg.inter
     dtype = {"f32": moe.MOE_DTYPE_F32, "bf16": moe.MOE_DTYPE_BF16, "fp8": moe.MOE_DTYPE_FP8_B128}[cfg.dtype]

@@ -15,9 +15,21 @@
 // (16 KB activations + 32 KB weights per stage).  Each wavefront computes 64 rows x
 // 4 blocks of 32 weight rows with 8 MFMA accumulators; the MFMA's A operand is the
 // weight tile and its B operand the activation tile, so each lane ends up holding
-// four runs of 4 consecutive output features of one row.  LDS rows are 128 bytes;
-// the 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so the 8 lanes of a
-// fragment read that share a chunk index hit 8 different bank groups.
+// four runs of 4 consecutive output features of one row.  LDS rows are 128 bytes,
+// XOR-swizzled in 16-byte chunks so that fragment reads are free of bank conflicts.
+//
+// Two variants share that tiling:
+//  * the streaming kernel (contraction length a multiple of 64; 8 wavefronts on a
+//    128 x 512 tile) fills two LDS stages with direct global->LDS loads
+//    (global_load_lds_dwordx4) one K-step ahead of the MFMAs, and takes its tile
+//    from an XCD-aware order: the 8 XCDs
+//    of MI355X each receive workgroups round-robin, so workgroup b runs on XCD
+//    b % 8; logical tiles are handed out so that the 32 workgroups an XCD holds at
+//    once form one block of 4 M-tiles x 8 N-tiles of the same expert (operands
+//    reused through that XCD's L2), and tiles are ordered expert by expert (each
+//    expert's weights pass through the shared last-level cache about once);
+//  * the register-staged kernel (any contraction length that is a multiple of 8)
+//    loads through registers with zero fill of the K tail, in plain grid order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,11 +40,23 @@ constexpr int kBK = 64;
 constexpr int kWRows = 256;
 constexpr int kStageElems = (kTileM + kWRows) * kBK;  // bf16 elements per LDS stage
 
+#ifndef MOE_STREAM_BK
+#define MOE_STREAM_BK 64
+#endif
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 4
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// LDS rows are 128 bytes (64 bf16).  The 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7):
+// a ds_read_b128 is served 16 lanes per pass by 64 four-byte banks (256 bytes), and the 16 lanes
+// of a fragment read (rows r..r+15, one logical chunk) then cover all 64 banks exactly once
+// (rows 2j and 2j+1 share a chunk slot but sit in opposite bank halves).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ swz(row)) << 3); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   uint32_t b = __float_as_uint(v);
@@ -40,6 +64,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+
+// Epilogue: the lane holds, for row r0 + 32 mb + l32, features 8 q + 4 khalf + (0..3) of each
+// 32-feature block; SwiGLU pairs gate block nb with up block nb + 2.
+template <bool SWIGLU>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[2][4], uint16_t* out, int64_t r0, int fbase,
+                                           int N, int l32, int khalf) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    uint16_t* orow = out + (r0 + mb * 32 + l32) * N;
+#pragma unroll
+    for (int nb = 0; nb < (SWIGLU ? 2 : 4); ++nb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = fbase + nb * 32 + q * 8 + khalf * 4;
+        uint16_t h[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          h[v] = SWIGLU ? f32_to_bf16(silu(acc[mb][nb][q * 4 + v]) * acc[mb][nb + 2][q * 4 + v])
+                        : f32_to_bf16(acc[mb][nb][q * 4 + v]);
+        if (f + 3 < N) {
+          *reinterpret_cast<uint2*>(orow + f) =
+              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (f + v < N) orow[f + v] = h[v];
+        }
+      }
+    }
+  }
+}
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kThreads) grouped_gemm_bf16_kernel(GemmOperands g) {
@@ -149,56 +205,214 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_bf16_kernel(GemmOperand
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds row (l32) and features 8 q + 4 khalf + (0..3) of each 32-block
-  uint16_t* out = static_cast<uint16_t*>(g.out);
+  store_tile<SWIGLU>(acc, static_cast<uint16_t*>(g.out), m0 + wm * 64, n0 + (SWIGLU ? wn * 64 : wn * 128), N, l32,
+                     khalf);
+}
+
+
+// ---------------------------------------------------------------------------- streaming variant
+//
+// 512 threads (8 wavefronts, two per SIMD) own 128 rows x 512 weight rows (gate/up: 256 gate +
+// the matching 256 up features; down: 512 output features); wavefront (wm, wn) of the 2 x 4
+// grid computes 64 rows x 128 weight rows as above.  The K-step BK sets the LDS stage size,
+// (128 + 512) * BK * 2 bytes, and the 160 KB of LDS holds 163840 / that many stages; direct
+// global->LDS loads run (stages - 1) K-steps ahead of the MFMAs.
+
+constexpr int kThreadsS = 512;
+constexpr int kWRowsS = 512;
+constexpr int kLdsBytes = 163840;
+constexpr int kXcds = 8;          // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
+constexpr int kXcdChunk = 32;     // consecutive logical tiles one XCD receives
+constexpr int kGroupM = MOE_GROUP_M;  // M-tiles per block of the within-expert order
+
+template <int BK>
+struct StreamCfg {
+  static constexpr int kRowBytes = BK * 2;
+  static constexpr int kChunks = BK / 8;                       // 16-byte chunks per LDS row
+  static constexpr int kRowsPer256 = 256 / kRowBytes;          // rows sharing one pass of the 64 banks
+  static constexpr int kStageElems = (kTileM + kWRowsS) * BK;
+  static constexpr int kStages = kLdsBytes / (kStageElems * 2);
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;          // rows one wave-wide 1 KB load fills
+  static constexpr int kADma = kTileM / kRowsPerDma / 8;        // activation loads per wave per stage
+  static constexpr int kWDma = kWRowsS / kRowsPerDma / 8;       // weight loads per wave per stage
+  static constexpr int kDmaPerStage = kADma + kWDma;
+  // chunk c of row r sits at slot c ^ swz(r): the 16 rows of a 16-lane read pass then cover all
+  // 64 banks once (rows in one 256-byte bank span differ in their bank offset, rows in different
+  // spans in their slot)
+  __device__ static __forceinline__ int swz(int r) { return (r / kRowsPer256) % kChunks; }
+  __device__ static __forceinline__ int off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void lds_dma16(const void* src, uint16_t* lds_base) {
+  // each lane's 16 bytes land at lds_base + 16 * lane (the destination is wave-uniform)
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_base), 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = N (split field on gfx9: bits 3:0 and 15:14), expcnt and lgkmcnt not waited
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait until at most `ahead` stages of this wave's loads are still in flight
+template <int PER, int MAXAHEAD>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (MAXAHEAD >= 3) {
+    if (ahead >= 3) { wait_vmcnt<3 * PER>(); return; }
+  }
+  if constexpr (MAXAHEAD >= 2) {
+    if (ahead == 2) { wait_vmcnt<2 * PER>(); return; }
+  }
+  if (ahead == 1) { wait_vmcnt<PER>(); return; }
+  wait_vmcnt<0>();
+}
+
+template <bool SWIGLU, int BK>
+__global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(GemmOperands g, int NT) {
+  using C = StreamCfg<BK>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  // ---- logical tile of this workgroup (see the file comment)
+  const int b = blockIdx.x;
+  const int64_t L = (int64_t)(b / (kXcds * kXcdChunk)) * (kXcds * kXcdChunk) + (b % kXcds) * kXcdChunk +
+                    (b / kXcds) % kXcdChunk;
+  const int64_t mt_glob = L / NT;
+  if (mt_glob >= g.max_tiles) return;
+  const int seg = g.tile_seg[mt_glob];
+  if (seg < 0) return;
+  const int seg_m0 = g.seg_off[seg] / kTileM;
+  const int seg_mt = g.seg_off[seg + 1] / kTileM - seg_m0;
+  const int64_t lam = L - (int64_t)seg_m0 * NT;
+  const int grp = (int)(lam / (kGroupM * NT));
+  const int gm = min(kGroupM, seg_mt - grp * kGroupM);
+  const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
+  const int mt = seg_m0 + grp * kGroupM + rem % gm;
+  const int nt = rem / gm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int K = g.K, N = g.N;
+  const int64_t m0 = (int64_t)mt * kTileM;
+  const int n0 = nt * (SWIGLU ? kWRowsS / 2 : kWRowsS);
+  const bool shared = seg >= g.n_routed;
+  const int e = shared ? seg - g.n_routed : seg;
+  const size_t wstride = (size_t)N * K;
+  const uint16_t* W0 = static_cast<const uint16_t*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride;
+  const uint16_t* W1 = SWIGLU ? static_cast<const uint16_t*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride
+                              : nullptr;
+  const uint16_t* act = static_cast<const uint16_t*>(g.act);
+
+  // ---- per-lane sources: wave w fills activation rows [w * 128/8, +128/8) and weight-tile rows
+  // [w * 64, +64), kRowsPerDma rows per load; lane l covers row l / kChunks of its load and slot
+  // l % kChunks, which holds logical chunk slot ^ swz(row)
+  const int lrow = lane / C::kChunks;
+  const int lslot = lane % C::kChunks;
+  const uint16_t* asrc[C::kADma];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int64_t row = m0 + wm * 64 + mb * 32 + l32;
-    uint16_t* orow = out + row * N;
+  for (int i = 0; i < C::kADma; ++i) {
+    const int row = wave * (kTileM / 8) + i * C::kRowsPerDma + lrow;
+    int64_t tok = g.row_token ? (int64_t)g.row_token[m0 + row] : m0 + row;
+    if (tok < 0) tok = 0;  // padding row: any valid row (its outputs are never read)
+    asrc[i] = act + tok * K + ((lslot ^ C::swz(row)) << 3);
+  }
+  const uint16_t* wsrc[C::kWDma];
+#pragma unroll
+  for (int i = 0; i < C::kWDma; ++i) {
+    const int r = wave * (kWRowsS / 8) + i * C::kRowsPerDma + lrow;  // 0..511 within the weight tile
+    const uint16_t* base;
+    int n;
     if (SWIGLU) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = n0 + wn * 64 + nb * 32 + q * 8 + khalf * 4;
-          uint16_t h[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) h[v] = f32_to_bf16(silu(acc[mb][nb][q * 4 + v]) * acc[mb][nb + 2][q * 4 + v]);
-          if (f + 3 < N) {
-            *reinterpret_cast<uint2*>(orow + f) =
-                make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-          } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (f + v < N) orow[f + v] = h[v];
-          }
-        }
-      }
+      base = r < kWRowsS / 2 ? W0 : W1;
+      n = n0 + (r & (kWRowsS / 2 - 1));
     } else {
+      base = W0;
+      n = n0 + r;
+    }
+    if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
+    wsrc[i] = base + (size_t)n * K + ((lslot ^ C::swz(kTileM + r)) << 3);
+  }
+  auto issue_stage = [&](int kt) {
+    uint16_t* st = lds + (kt % C::kStages) * C::kStageElems;
+    const int k0 = kt * BK;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+    for (int i = 0; i < C::kADma; ++i)
+      lds_dma16(asrc[i] + k0, st + (wave * (kTileM / 8) + i * C::kRowsPerDma) * BK);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = n0 + wn * 128 + nb * 32 + q * 8 + khalf * 4;
-          uint16_t h[4];
+    for (int i = 0; i < C::kWDma; ++i)
+      lds_dma16(wsrc[i] + k0, st + (kTileM + wave * (kWRowsS / 8) + i * C::kRowsPerDma) * BK);
+  };
+
+  f32x16 acc[2][4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) h[v] = f32_to_bf16(acc[mb][nb][q * 4 + v]);
-          if (f + 3 < N) {
-            *reinterpret_cast<uint2*>(orow + f) =
-                make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-          } else {
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (f + v < N) orow[f + v] = h[v];
-          }
-        }
-      }
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+  int wrow[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    wrow[nb] = SWIGLU ? ((nb >> 1) * (kWRowsS / 2) + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
+  const int l32 = lane & 31, khalf = lane >> 5;
+
+  const int nk = K / BK;
+  constexpr int kAhead = C::kStages - 1;
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s)
+    if (s < nk) issue_stage(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt have landed once only the later issued stages are in flight
+    wait_stages<C::kDmaPerStage, kAhead - 1>(min(kAhead - 1, nk - 1 - kt));
+    // a bare barrier: after it all of stage kt is in LDS and every wave is done reading stage
+    // kt-1, whose buffer the next loads overwrite (__syncthreads() would add a memory fence
+    // that also drains the loads still in flight)
+    __builtin_amdgcn_s_barrier();
+    if (kt + kAhead < nk) issue_stage(kt + kAhead);
+    const uint16_t* st = lds + (kt % C::kStages) * C::kStageElems;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + khalf;
+      bf16x8 xf[2], wf[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        xf[mb] = *reinterpret_cast<const bf16x8*>(st + C::off(wm * 64 + mb * 32 + l32, c));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        wf[nb] = *reinterpret_cast<const bf16x8*>(st + C::off(kTileM + wrow[nb] + l32, c));
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
     }
   }
+  store_tile<SWIGLU>(acc, static_cast<uint16_t*>(g.out), m0 + wm * 64, n0 + (SWIGLU ? wn * 64 : wn * 128), N, l32,
+                     khalf);
 }
 
 template <bool SWIGLU>
 hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
+  constexpr int SBK = MOE_STREAM_BK;
+  if (g.K % SBK == 0) {
+    const int NT = (int)ceil_div(g.N, SWIGLU ? kWRowsS / 2 : kWRowsS);
+    const size_t lds_bytes = StreamCfg<SBK>::kStages * StreamCfg<SBK>::kStageElems * sizeof(uint16_t);
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_stream_kernel<SWIGLU, SBK>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+    const int64_t tiles = g.max_tiles * NT;
+    const int64_t grid = ceil_div(tiles, kXcds * kXcdChunk) * (kXcds * kXcdChunk);
+    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<SWIGLU, SBK>), dim3((unsigned)grid), dim3(kThreadsS), lds_bytes,
+                       st, g, NT);
+    return hipGetLastError();
+  }
   const size_t lds_bytes = 2 * kStageElems * sizeof(uint16_t);
   static bool attr_set = false;
   if (!attr_set) {
@@ -207,8 +421,7 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  const int ntile = SWIGLU ? kWRows / 2 : kWRows;
-  dim3 grid((unsigned)g.max_tiles, (unsigned)ceil_div(g.N, ntile));
+  dim3 grid((unsigned)g.max_tiles, (unsigned)ceil_div(g.N, SWIGLU ? kWRows / 2 : kWRows));
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<SWIGLU>, grid, dim3(kThreads), lds_bytes, st, g);
   return hipGetLastError();
 }

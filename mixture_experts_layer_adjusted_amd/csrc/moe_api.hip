@@ -133,6 +133,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.s_shared[0] = w->sh_gate_scale;
   g1.s_shared[1] = w->sh_up_scale;
   g1.tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
+  g1.seg_off = reinterpret_cast<const int32_t*>(wsb + p.seg_off);
   g1.n_routed = s.n_routed;
   g1.K = s.hidden;
   g1.N = s.inter;
@@ -151,6 +152,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g2.s_routed[0] = w->w_down_scale;
   g2.s_shared[0] = w->sh_down_scale;
   g2.tile_seg = g1.tile_seg;
+  g2.seg_off = g1.seg_off;
   g2.n_routed = s.n_routed;
   g2.K = s.inter;
   g2.N = s.hidden;

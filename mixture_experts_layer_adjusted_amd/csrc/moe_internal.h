@@ -62,6 +62,7 @@ struct GemmOperands {
   const float* s_routed[2];  // fp8 block scales [N_r, N/128, K/128]
   const float* s_shared[2];
   const int32_t* tile_seg;
+  const int32_t* seg_off;    // [N_r + N_s + 1] first padded row of each segment
   int n_routed;
   int K, N;                  // contraction length, output features per expert
   int64_t max_tiles;
