@@ -42,7 +42,14 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
     o = align_up(o + bytes, A);
     return at;
   };
-  p.route_partial = take((size_t)p.route_blocks * N * 4);
+  const bool mfma_route = route_uses_mfma(s);
+  const int64_t route_rows = mfma_route ? route_mfma_blocks(s) : p.route_blocks;
+  const int64_t n_pad = ceil_div(N, 128) * 128;
+  p.route_partial = take((size_t)route_rows * N * 4);
+  p.route_e_hi = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
+  p.route_e_mid = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
+  p.route_e_lo = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
+  p.route_scores = take(mfma_route ? (size_t)T * N * 4 : 0);
   p.route_bytes = o;
   o = 0;
   p.chunk_counts = take((size_t)p.chunks * N * 4);
@@ -190,9 +197,11 @@ moe_status moe_route(const moe_shape* shape, const void* u, const float* centroi
     return MOE_ERR_INVALID_ARG;
   const WorkspacePlan p = plan_workspace(*shape);
   if (shape->tokens > 0 && workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
-  int32_t* partial = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.route_partial);
-  return hip_status(launch_route(*shape, u, centroids, bias, topk_idx, topk_gate, expert_load, partial,
-                                 p.route_blocks, stream));
+  char* wsb = static_cast<char*>(workspace);
+  RouteWorkspace rw{reinterpret_cast<int32_t*>(wsb + p.route_partial), reinterpret_cast<uint16_t*>(wsb + p.route_e_hi),
+                    reinterpret_cast<uint16_t*>(wsb + p.route_e_mid), reinterpret_cast<uint16_t*>(wsb + p.route_e_lo),
+                    reinterpret_cast<float*>(wsb + p.route_scores)};
+  return hip_status(launch_route(*shape, u, centroids, bias, topk_idx, topk_gate, expert_load, rw, stream));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* u, const moe_weights* weights, const int32_t* topk_idx,

@@ -25,7 +25,9 @@ inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 // Byte offsets of every buffer inside the caller's workspace.
 struct WorkspacePlan {
   // routing
-  size_t route_partial;     // int32 [route_blocks, N_r]
+  size_t route_partial;     // int32 [route_blocks, N_r]  per-workgroup pick counts
+  size_t route_e_hi, route_e_mid, route_e_lo;  // bf16 [N_pad, d]  exact 3-way split of the centroids
+  size_t route_scores;      // fp32 [T, N_r]  affinities s (MFMA path)
   // forward
   size_t chunk_counts;      // int32 [chunks, N_r]
   size_t chunk_base;        // int32 [chunks, N_r]
@@ -45,10 +47,17 @@ struct WorkspacePlan {
 
 WorkspacePlan plan_workspace(const moe_shape& s);
 
+struct RouteWorkspace {
+  int32_t* partial;
+  uint16_t *e_hi, *e_mid, *e_lo;
+  float* scores;
+};
+
 // ---- launchers (return hipSuccess or the launch error) ----
+bool route_uses_mfma(const moe_shape& s);
+int64_t route_mfma_blocks(const moe_shape& s);
 hipError_t launch_route(const moe_shape& s, const void* u, const float* centroids, const float* bias,
-                        int32_t* idx, float* gate, int32_t* load, int32_t* partial, int64_t blocks,
-                        hipStream_t st);
+                        int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w, hipStream_t st);
 
 hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const WorkspacePlan& p, char* ws,
                           hipStream_t st);

@@ -5,7 +5,22 @@
 // entering the ranking only and the gate normalised over the selected unbiased
 // affinities.
 //
-// One workgroup (256 threads) owns kRouteTokens tokens:
+// Two implementations:
+//
+// MFMA path (bf16 tokens, d a multiple of 64, N_r <= 512):
+//  1. split: every fp32 centroid element is written exactly as hi + mid + lo, three bf16 values
+//     holding consecutive 8-bit slices of its 24-bit significand, so u . e = u . hi + u . mid +
+//     u . lo with every bf16 x bf16 product exact in fp32;
+//  2. logits: one bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16) over tokens x experts with the three
+//     parts as three B operands, 128 x 128 tiles, LDS stages filled by direct global->LDS loads;
+//     each 64-wide K-step starts a fresh accumulator that is then added to an fp32 running sum
+//     (blocked summation keeps the logit error near 1e-7 of the sum of |terms|); s = sigmoid(z)
+//     is written to the workspace;
+//  3. top-K: one wavefront per token on s + b, as in step 3 below, plus per-workgroup counts;
+//  4. counts: a fixed-order reduction of the per-workgroup counts into expert_load.
+//
+// Fused VALU path (fp32 tokens, or any other shape).  One workgroup (256 threads) owns
+// kRouteTokens tokens:
 //  1. logits z = u . e_i for its tokens and all experts, fp32 FMAs over LDS-staged
 //     32-wide slices of d; each slice is summed in a fresh register and then added
 //     to the running total (blocked summation keeps the rounding error of the
@@ -187,18 +202,252 @@ __global__ void __launch_bounds__(kThreads) route_kernel(const TIn* __restrict__
   }
 }
 
-__global__ void __launch_bounds__(kThreads) load_reduce_kernel(const int32_t* __restrict__ partial, int64_t blocks,
-                                                               int N, int32_t* __restrict__ load) {
-  int e = blockIdx.x * kThreads + threadIdx.x;
-  if (e >= N) return;
+// one 64-lane workgroup per expert: lane j sums partial rows j, j+64, ...; then a fixed
+// butterfly over the lanes (integer sums, so the order does not change the result anyway)
+__global__ void __launch_bounds__(64) load_reduce_kernel(const int32_t* __restrict__ partial, int64_t blocks, int N,
+                                                         int32_t* __restrict__ load) {
+  const int e = blockIdx.x;
   int32_t s = 0;
-  for (int64_t b = 0; b < blocks; ++b) s += partial[b * N + e];
-  load[e] = s;
+  for (int64_t b = threadIdx.x; b < blocks; b += 64) s += partial[b * N + e];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (threadIdx.x == 0) load[e] = s;
 }
 
 __global__ void zero_kernel(int32_t* p, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
+}
+
+
+// ---------------------------------------------------------------------------- MFMA path
+
+constexpr int kLT = 128;           // tokens per logits tile
+constexpr int kLE = 128;           // experts per logits tile
+constexpr int kLBK = 64;           // contraction per K-step
+constexpr int kLStageElems = (kLT + 3 * kLE) * kLBK;  // 64 KB
+constexpr int kTopkTokens = 64;    // tokens per top-K workgroup
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int roff(int r, int c) { return r * kLBK + ((c ^ rswz(r)) << 3); }
+
+// e = hi + mid + lo exactly: hi keeps the sign, exponent and top 7 stored significand bits;
+// the two remainders are exact fp32 differences with at most 16 and 8 significant bits
+__global__ void split_centroids_kernel(const float* __restrict__ E, int64_t n_elems, int64_t n_pad_elems,
+                                       uint16_t* __restrict__ hi, uint16_t* __restrict__ mid,
+                                       uint16_t* __restrict__ lo) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_pad_elems;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float x = i < n_elems ? E[i] : 0.0f;
+    uint32_t h = __float_as_uint(x) & 0xFFFF0000u;
+    float r1 = __fsub_rn(x, __uint_as_float(h));
+    uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+    float r2 = __fsub_rn(r1, __uint_as_float(m));
+    hi[i] = (uint16_t)(h >> 16);
+    mid[i] = (uint16_t)(m >> 16);
+    lo[i] = (uint16_t)(__float_as_uint(r2) >> 16);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// logits tile: 256 threads, waves (wm, wn) in 2 x 2 own 64 tokens x 64 experts; two LDS stages
+__global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __restrict__ u,
+                                                            const uint16_t* __restrict__ ehi,
+                                                            const uint16_t* __restrict__ emid,
+                                                            const uint16_t* __restrict__ elo, int T, int d, int N,
+                                                            float* __restrict__ s_out) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
+  const int lrow = lane >> 3, lslot = lane & 7;
+  // DMA sources: wave w fills token rows [32w, 32w+32) and, for each part, expert rows [32w, 32w+32)
+  const uint16_t* src[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wave * 32 + i * 8 + lrow;
+    const int t = min(t0 + row, T - 1);  // rows past T: any valid row (outputs discarded)
+    src[i] = u + (int64_t)t * d + ((lslot ^ rswz(row)) << 3);
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const uint16_t* base = p == 0 ? ehi : (p == 1 ? emid : elo);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave * 32 + i * 8 + lrow;         // expert row within the part
+      const int lrow_lds = kLT + p * kLE + row;          // LDS row
+      src[4 + p * 4 + i] = base + (int64_t)(e0 + row) * d + ((lslot ^ rswz(lrow_lds)) << 3);
+    }
+  }
+  auto issue = [&](int kt) {
+    uint16_t* st = lds + (kt & 1) * kLStageElems;
+    const int k0 = kt * kLBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(src[i] + k0, (lds_void_t*)(st + (wave * 32 + i * 8) * kLBK), 16, 0, 0);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(src[4 + p * 4 + i] + k0,
+                                         (lds_void_t*)(st + (kLT + p * kLE + wave * 32 + i * 8) * kLBK), 16, 0, 0);
+  };
+  float zsum[2][2][16];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) zsum[a][b][v] = 0.0f;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int nk = d / kLBK;
+  issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // stage kt landed for every wave; stage kt-1 no longer read
+    if (kt + 1 < nk) issue(kt + 1);
+    const uint16_t* st = lds + (kt & 1) * kLStageElems;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < kLBK / 16; ++kk) {
+      const int c = kk * 2 + khalf;
+      bf16x8 tf[2], ef[3][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) tf[mb] = *reinterpret_cast<const bf16x8*>(st + roff(wm * 64 + mb * 32 + l32, c));
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          ef[p][nb] = *reinterpret_cast<const bf16x8*>(st + roff(kLT + p * kLE + wn * 64 + nb * 32 + l32, c));
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[p][nb], tf[mb], acc[mb][nb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) zsum[a][b][v] += acc[a][b][v];
+  }
+  // lane holds token t0 + 64 wm + 32 mb + l32 and experts e0 + 64 wn + 32 nb + 8 q + 4 khalf + (0..3)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int t = t0 + wm * 64 + mb * 32 + l32;
+    if (t >= T) continue;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + wn * 64 + nb * 32 + q * 8 + khalf * 4;
+        float4 o;
+        o.x = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 0]));
+        o.y = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 1]));
+        o.z = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 2]));
+        o.w = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 3]));
+        if (e + 3 < N && (N & 3) == 0) {
+          *reinterpret_cast<float4*>(s_out + (int64_t)t * N + e) = o;
+        } else {
+          const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (e + v < N) s_out[(int64_t)t * N + e + v] = ov[v];
+        }
+      }
+  }
+}
+
+// top-K over precomputed affinities: one wavefront per token, kTopkTokens tokens per workgroup
+template <int CPL>
+__global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict__ s_in, const float* __restrict__ bias,
+                                                        int T, int N, int K, int32_t* __restrict__ idx_out,
+                                                        float* __restrict__ gate_out, int32_t* __restrict__ partial) {
+  __shared__ int32_t picks[kTopkTokens * kMaxTopK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kTopkTokens;
+  for (int q = tid; q < kTopkTokens * kMaxTopK; q += kThreads) picks[q] = -1;
+  float bl[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    int e = lane + 64 * j;
+    bl[j] = e < N ? bias[e] : 0.0f;
+  }
+  __syncthreads();
+  for (int tt = wave; tt < kTopkTokens; tt += kThreads / 64) {
+    const int t = t0 + tt;
+    if (t >= T) break;
+    const float* srow = s_in + (int64_t)t * N;
+    float sv[CPL];
+    uint64_t key[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      int e = lane + 64 * j;
+      sv[j] = e < N ? srow[e] : 0.0f;
+      key[j] = e < N ? score_key(sv[j] + bl[j], e) : 0ull;
+    }
+    uint32_t taken = 0;
+    float mys = 0.0f, sum = 0.0f;
+    int myidx = -1;
+    for (int k = 0; k < K; ++k) {
+      uint64_t best = 0ull;
+      int bj = -1;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        int e = lane + 64 * j;
+        if (e < N && !((taken >> j) & 1u) && (bj < 0 || key[j] > best)) {
+          best = key[j];
+          bj = j;
+        }
+      }
+      uint64_t win = wave_max_u64(bj < 0 ? 0ull : best);
+      int we = (int)(~(uint32_t)win);
+      float sw = 0.0f;
+      if (bj >= 0 && best == win) {
+        taken |= 1u << bj;
+      }
+      // the winner's affinity, broadcast from the lane that holds it
+      const int owner = we & 63, oj = we >> 6;
+      float cand = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        if (j == oj) cand = sv[j];
+      sw = __shfl(cand, owner, 64);
+      sum += sw;
+      if (lane == k) {
+        mys = sw;
+        myidx = we;
+      }
+    }
+    if (lane < K) {
+      idx_out[(int64_t)t * K + lane] = myidx;
+      gate_out[(int64_t)t * K + lane] = mys / sum;
+      picks[tt * K + lane] = myidx;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += kThreads) {
+    int c = 0;
+    for (int q = 0; q < kTopkTokens * K; ++q) c += (picks[q] == e);
+    partial[(int64_t)blockIdx.x * N + e] = c;
+  }
 }
 
 template <typename TIn>
@@ -217,16 +466,57 @@ hipError_t launch_route_t(const moe_shape& s, const TIn* u, const float* centroi
 #undef MOE_ROUTE_CASE
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(load_reduce_kernel, dim3((unsigned)ceil_div(N, kThreads)), block, 0, st, partial, blocks, N,
-                     load);
+  hipLaunchKernelGGL(load_reduce_kernel, dim3((unsigned)N), dim3(64), 0, st, partial, blocks, N, load);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float* centroids, const float* bias,
+                             int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w, hipStream_t st) {
+  const int T = s.tokens, d = s.hidden, N = s.n_routed;
+  const int64_t npad = ceil_div(N, kLE) * kLE;
+  hipLaunchKernelGGL(split_centroids_kernel, dim3(1024), dim3(256), 0, st, centroids, (int64_t)N * d, npad * d,
+                     w.e_hi, w.e_mid, w.e_lo);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds_bytes = 2 * kLStageElems * sizeof(uint16_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(router_logits_kernel, dim3((unsigned)ceil_div(T, kLT), (unsigned)(npad / kLE)), dim3(256),
+                     lds_bytes, st, u, w.e_hi, w.e_mid, w.e_lo, T, d, N, w.scores);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int64_t blocks = ceil_div(T, kTopkTokens);
+  dim3 grid((unsigned)blocks), block(kThreads);
+#define MOE_TOPK_CASE(C) \
+  hipLaunchKernelGGL((topk_kernel<C>), grid, block, 0, st, w.scores, bias, T, N, s.top_k, idx, gate, w.partial)
+  if (N <= 64) MOE_TOPK_CASE(1);
+  else if (N <= 128) MOE_TOPK_CASE(2);
+  else if (N <= 256) MOE_TOPK_CASE(4);
+  else MOE_TOPK_CASE(8);
+#undef MOE_TOPK_CASE
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(load_reduce_kernel, dim3((unsigned)N), dim3(64), 0, st, w.partial, blocks, N, load);
   return hipGetLastError();
 }
 
 }  // namespace
 
+bool route_uses_mfma(const moe_shape& s) {
+  return s.dtype != MOE_DTYPE_F32 && s.hidden % kLBK == 0 && s.n_routed <= kMaxRouted;
+}
+
+int64_t route_mfma_blocks(const moe_shape& s) { return ceil_div(s.tokens, kTopkTokens); }
+
 hipError_t launch_route(const moe_shape& s, const void* u, const float* centroids, const float* bias,
-                        int32_t* idx, float* gate, int32_t* load, int32_t* partial, int64_t blocks,
-                        hipStream_t st) {
+                        int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w, hipStream_t st) {
+  if (s.tokens > 0 && route_uses_mfma(s))
+    return launch_route_mfma(s, static_cast<const uint16_t*>(u), centroids, bias, idx, gate, load, w, st);
+  int32_t* partial = w.partial;
+  const int64_t blocks = ceil_div(s.tokens, kRouteTokens);
   if (s.tokens == 0) {
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)ceil_div(s.n_routed, 256)), dim3(256), 0, st, load, s.n_routed);
     return hipGetLastError();
