@@ -11,6 +11,7 @@
 // round-to-nearest-even of the correctly rounded fp32 quotient x / scale,
 // saturating at +-448.  The conversion is done in integer arithmetic from the
 // OCP OFP8 bit layout (bias 7, 3 mantissa bits, S.1111.111 = NaN).
+#include "fp8_codec.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -25,32 +26,6 @@ __global__ void update_bias_kernel(int32_t n, int64_t total, const int32_t* __re
   if (l > total) b = __fsub_rn(b, gamma);
   else if (l < total) b = __fadd_rn(b, gamma);
   bias[i] = b;
-}
-
-__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
-  const uint32_t bits = __float_as_uint(y);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fabsf(y);
-  if (a != a) return 0x7Fu;                    // NaN
-  uint32_t code;
-  if (a < 0.015625f) {                         // below 2^-6: subnormal grid, spacing 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);   // exact scaling, round half to even; 8 -> min normal
-  } else {
-    const uint32_t ab = bits & 0x7FFFFFFFu;
-    const int e = (int)(ab >> 23) - 127;       // >= -6 here
-    const uint32_t frac = ab & 0x7FFFFFu;
-    uint32_t m = frac >> 20;                   // top 3 mantissa bits
-    const uint32_t rem = frac & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
-    int ee = e + 7;
-    if (m == 8u) {
-      m = 0u;
-      ++ee;
-    }
-    code = ee > 15 ? 0x7Fu : ((uint32_t)ee << 3) | m;
-    if (code > 0x7Eu) code = 0x7Eu;            // saturate at 448
-  }
-  return sign | code;
 }
 
 // one wavefront per 1x128 tile: each lane handles 2 consecutive elements

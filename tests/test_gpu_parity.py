@@ -236,3 +236,75 @@ def test_config3_prefill_20_steps():
     ratios = _v3_check(cfg, rng.choice(cfg.tokens, 6, replace=False), steps=cfg.steps)
     print("load max/mean per step:", [round(float(x), 3) for x in ratios])
     assert ratios[0] > 4.0   # the Zipf-scaled centroids skew the load
+
+
+# ----------------------------------------------------------------------------- FP8 layer
+
+def _q3(wg, wu, wd):
+    return (O.quantize_weight_128x128(wg), O.quantize_weight_128x128(wu), O.quantize_weight_128x128(wd))
+
+
+def _check_fp8_outputs(y, u, idx, gate, routed_f, shared_f):
+    """y against the quantisation-faithful oracle (2e-2) and the unquantised one.
+
+    At small contraction lengths E4M3 rounding alone moves the layer output by more
+    than 6e-2 (few terms average it out), so against the unquantised oracle the
+    bound is the oracle's own quantisation error plus the 2e-2 kernel tolerance
+    (triangle inequality), computed per metric."""
+    y_i = O.layer_forward(u, idx, gate, routed_f, shared_f)
+    e_i = rel_err(y, y_i, u)
+    rq = lambda e: _q3(*routed_f(e))  # noqa: E731
+    y_ii = O.layer_forward_fp8(u, idx, gate, rq, [_q3(*w) for w in shared_f])
+    e_ii = rel_err(y, y_ii, u)
+    e_q = rel_err(y_ii, y_i, u)   # quantisation error of the oracle itself
+    print("fp8: rel err (all, expert part) vs unquantised", e_i, "vs quantisation-faithful", e_ii,
+          "oracle's own quantisation error", e_q, flush=True)
+    assert max(e_ii) <= TOL["fp8_faithful"], e_ii
+    assert e_i[0] <= e_q[0] + TOL["fp8_faithful"] and e_i[1] <= e_q[1] + TOL["fp8_faithful"], (e_i, e_q)
+    return e_i, e_ii
+
+
+def test_fp8_small_layer():
+    cfg = _edge("fp8-small", 200, 256, 16, 4, 1, 128, dtype="fp8", bias="normal_var0.01")
+    h, hf = _host_layer(cfg)
+    dev = quantize_fp8_weights(host_to_device(h), cfg)
+    r = Runner(cfg, dev)
+    r.route()
+    r.forward()
+    torch.cuda.synchronize()
+    idx_g = r.idx.cpu().numpy()
+    idx_o, g_o, load_o, s_o, c_o, gap_o = O.route(hf["u"], hf["centroids"], hf["bias"], cfg.top_k)
+    check_routing(idx_g, r.gate.cpu().numpy(), r.load.cpu().numpy(), s_o, c_o, idx_o, gap_o, cfg.n_routed)
+    ig = idx_g.astype(np.int64)
+    e_i, e_ii = _check_fp8_outputs(to_host_f32(r.out), hf["u"], ig, O.gates(s_o, ig),
+                                   O.stacked(hf["w_gate"], hf["w_up"], hf["w_down"]),
+                                   list(zip(hf["sh_gate"], hf["sh_up"], hf["sh_down"])))
+    print("fp8 small: rel err vs unquantised", e_i, "vs quantisation-faithful", e_ii)
+
+
+def test_config4_fp8_prefill():
+    cfg = CONFIGS[4]
+    dev = quantize_fp8_weights(make_device_inputs(cfg), cfg)
+    r = Runner(cfg, dev)
+    r.route()
+    r.forward()
+    torch.cuda.synchronize()
+    u_host = _f(host.token_rows(cfg))
+    s_or = O.affinity(u_host, host.centroids(cfg))
+    c_or = O.selection_scores(s_or, host.bias_vector(cfg))
+    idx_o, gap_o = O.select_topk(c_or, cfg.top_k)
+    idx_g = r.idx.cpu().numpy()
+    check_routing(idx_g, r.gate.cpu().numpy(), r.load.cpu().numpy(), s_or, c_or, idx_o, gap_o, cfg.n_routed)
+    ex = _HostExperts(cfg)
+    y = to_host_f32(r.out)
+    # layer output against the unquantised oracle on a few sampled tokens (6e-2)
+    toks = np.array([11, 4097, 8191])
+    ig = idx_g[toks].astype(np.int64)
+    y_i = O.layer_forward(u_host[toks], ig, O.gates(s_or[toks], ig), ex.routed, ex.shared())
+    e_i = rel_err(y[toks], y_i)
+    assert e_i <= TOL["fp8"], e_i
+    # one token (its 8 routed experts + the shared one) against the quantisation-faithful oracle
+    t = np.array([4097])
+    ig1 = idx_g[t].astype(np.int64)
+    e_i1, e_ii = _check_fp8_outputs(y[t], u_host[t], ig1, O.gates(s_or[t], ig1), ex.routed, ex.shared())
+    print("fp8 V3 prefill: rel err vs unquantised", e_i, "vs quantisation-faithful", e_ii)
