@@ -24,6 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 WORKLOADS = {"v3-prefill-bf16-zipf": 3, "v3-prefill-fp8": 4, "v3-decode-bf16": 2, "mid-bf16": 1}
+# counter summaries of the gate/up GEMM (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)
+TRAFFIC = {"v3-prefill-bf16-zipf": "profiles/traffic_gemm_gate_up_v3_prefill_bf16.json",
+           "v3-prefill-fp8": "profiles/traffic_gemm_gate_up_v3_prefill_fp8.json"}
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
@@ -39,6 +42,22 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return p.parse_args()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter summary, or None
+    when there is none or the kernel's source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, TRAFFIC.get(workload, ""))
+    if workload not in TRAFFIC or not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    h = hashlib.sha256()
+    for f in t["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != t["source_sha256"]:
+        return None
+    return t["hbm_bytes_per_launch"]
 
 
 def cpu_baseline(cfg, n_tokens):
@@ -175,6 +194,8 @@ def main():
     combine_bytes = T * d * elem * (K + Ns + 2) + T * K * 8
     result = {
         "metric": "MoE layer fwd tokens/sec at V3 shape (T=16384); % of MFMA peak",
+        "workload_note": None if args.workload == "v3-prefill-bf16-zipf" else
+        "not the headline workload: the metric line above is quoted on the T=16384 bf16 prefill",
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -191,7 +212,8 @@ def main():
         "tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
         "mfma_peak_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / peak, 4),
         "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(args.workload),
                      "avg_ms": round(g1_ms, 4), "flops_per_launch": flops_gemm1},
         "stages_ms": stage_ms,
         "gemm_down": {"achieved_tflops": round(flops_gemm2 / (float(st[:, 4].mean()) * 1e-3) / 1e12, 2),
