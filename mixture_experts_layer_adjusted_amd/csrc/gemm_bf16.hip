@@ -44,7 +44,16 @@ constexpr int kStageElems = (kTileM + kWRows) * kBK;  // bf16 elements per LDS s
 #define MOE_STREAM_BK 64
 #endif
 #ifndef MOE_GROUP_M
-#define MOE_GROUP_M 4
+#define MOE_GROUP_M 8
+#endif
+#ifndef MOE_STREAM_WAVES
+#define MOE_STREAM_WAVES 8
+#endif
+#ifndef MOE_STREAM_WROWS
+#define MOE_STREAM_WROWS 512
+#endif
+#ifndef MOE_STREAM_WGS
+#define MOE_STREAM_WGS 1
 #endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -212,30 +221,32 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_bf16_kernel(GemmOperand
 
 // ---------------------------------------------------------------------------- streaming variant
 //
-// 512 threads (8 wavefronts, two per SIMD) own 128 rows x 512 weight rows (gate/up: 256 gate +
-// the matching 256 up features; down: 512 output features); wavefront (wm, wn) of the 2 x 4
-// grid computes 64 rows x 128 weight rows as above.  The K-step BK sets the LDS stage size,
-// (128 + 512) * BK * 2 bytes, and the 160 KB of LDS holds 163840 / that many stages; direct
-// global->LDS loads run (stages - 1) K-steps ahead of the MFMAs.
+// WAVES wavefronts own 128 rows x WROWS weight rows (gate/up: WROWS/2 gate + the matching
+// WROWS/2 up features; down: WROWS output features); wavefront (wm, wn) of the 2 x (WAVES/2)
+// grid computes 64 rows x 128 weight rows as in the register-staged kernel.  WGS workgroups
+// share a CU, each with 160 KB / WGS of LDS holding as many stages of (128 + WROWS) x BK bf16
+// as fit; direct global->LDS loads run (stages - 1) K-steps ahead of the MFMAs.
 
-constexpr int kThreadsS = 512;
-constexpr int kWRowsS = 512;
 constexpr int kLdsBytes = 163840;
 constexpr int kXcds = 8;          // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
-constexpr int kXcdChunk = 32;     // consecutive logical tiles one XCD receives
+constexpr int kCusPerXcd = 32;
 constexpr int kGroupM = MOE_GROUP_M;  // M-tiles per block of the within-expert order
 
-template <int BK>
+template <int BK, int WAVES, int WROWS, int WGS>
 struct StreamCfg {
+  static constexpr int kThreads = WAVES * 64;
   static constexpr int kRowBytes = BK * 2;
   static constexpr int kChunks = BK / 8;                       // 16-byte chunks per LDS row
   static constexpr int kRowsPer256 = 256 / kRowBytes;          // rows sharing one pass of the 64 banks
-  static constexpr int kStageElems = (kTileM + kWRowsS) * BK;
-  static constexpr int kStages = kLdsBytes / (kStageElems * 2);
+  static constexpr int kStageElems = (kTileM + WROWS) * BK;
+  static constexpr int kStages = (kLdsBytes / WGS) / (kStageElems * 2);
   static constexpr int kRowsPerDma = 1024 / kRowBytes;          // rows one wave-wide 1 KB load fills
-  static constexpr int kADma = kTileM / kRowsPerDma / 8;        // activation loads per wave per stage
-  static constexpr int kWDma = kWRowsS / kRowsPerDma / 8;       // weight loads per wave per stage
+  static constexpr int kADma = kTileM / kRowsPerDma / WAVES;    // activation loads per wave per stage
+  static constexpr int kWDma = WROWS / kRowsPerDma / WAVES;     // weight loads per wave per stage
   static constexpr int kDmaPerStage = kADma + kWDma;
+  static constexpr int kXcdChunk = kCusPerXcd * WGS;            // workgroups an XCD holds at once
+  static_assert(kStages >= 2, "at least two LDS stages");
+  static_assert(kADma * kRowsPerDma * WAVES == kTileM && kWDma * kRowsPerDma * WAVES == WROWS, "load split");
   // chunk c of row r sits at slot c ^ swz(r): the 16 rows of a 16-lane read pass then cover all
   // 64 banks once (rows in one 256-byte bank span differ in their bank offset, rows in different
   // spans in their slot)
@@ -266,18 +277,20 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   if constexpr (MAXAHEAD >= 2) {
     if (ahead == 2) { wait_vmcnt<2 * PER>(); return; }
   }
-  if (ahead == 1) { wait_vmcnt<PER>(); return; }
+  if constexpr (MAXAHEAD >= 1) {
+    if (ahead == 1) { wait_vmcnt<PER>(); return; }
+  }
   wait_vmcnt<0>();
 }
 
-template <bool SWIGLU, int BK>
-__global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(GemmOperands g, int NT) {
-  using C = StreamCfg<BK>;
+template <bool SWIGLU, int BK, int WAVES, int WROWS, int WGS>
+__global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kernel(GemmOperands g, int NT) {
+  using C = StreamCfg<BK, WAVES, WROWS, WGS>;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   // ---- logical tile of this workgroup (see the file comment)
   const int b = blockIdx.x;
-  const int64_t L = (int64_t)(b / (kXcds * kXcdChunk)) * (kXcds * kXcdChunk) + (b % kXcds) * kXcdChunk +
-                    (b / kXcds) % kXcdChunk;
+  constexpr int kSpan = kXcds * C::kXcdChunk;
+  const int64_t L = (int64_t)(b / kSpan) * kSpan + (b % kXcds) * C::kXcdChunk + (b / kXcds) % C::kXcdChunk;
   const int64_t mt_glob = L / NT;
   if (mt_glob >= g.max_tiles) return;
   const int seg = g.tile_seg[mt_glob];
@@ -293,11 +306,12 @@ __global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(Gem
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS offsets stay scalar
+  constexpr int WN = WAVES / 2;
+  const int wm = wave / WN, wn = wave % WN;
   const int K = g.K, N = g.N;
   const int64_t m0 = (int64_t)mt * kTileM;
-  const int n0 = nt * (SWIGLU ? kWRowsS / 2 : kWRowsS);
+  const int n0 = nt * (SWIGLU ? WROWS / 2 : WROWS);
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
   const size_t wstride = (size_t)N * K;
@@ -306,15 +320,15 @@ __global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(Gem
                               : nullptr;
   const uint16_t* act = static_cast<const uint16_t*>(g.act);
 
-  // ---- per-lane sources: wave w fills activation rows [w * 128/8, +128/8) and weight-tile rows
-  // [w * 64, +64), kRowsPerDma rows per load; lane l covers row l / kChunks of its load and slot
-  // l % kChunks, which holds logical chunk slot ^ swz(row)
+  // ---- per-lane sources: wave w fills activation rows [w * 128/WAVES, +128/WAVES) and weight-tile
+  // rows [w * WROWS/WAVES, +WROWS/WAVES), kRowsPerDma rows per load; lane l covers row l / kChunks
+  // of its load and slot l % kChunks, which holds logical chunk slot ^ swz(row)
   const int lrow = lane / C::kChunks;
   const int lslot = lane % C::kChunks;
   const uint16_t* asrc[C::kADma];
 #pragma unroll
   for (int i = 0; i < C::kADma; ++i) {
-    const int row = wave * (kTileM / 8) + i * C::kRowsPerDma + lrow;
+    const int row = wave * (kTileM / WAVES) + i * C::kRowsPerDma + lrow;
     int64_t tok = g.row_token ? (int64_t)g.row_token[m0 + row] : m0 + row;
     if (tok < 0) tok = 0;  // padding row: any valid row (its outputs are never read)
     asrc[i] = act + tok * K + ((lslot ^ C::swz(row)) << 3);
@@ -322,12 +336,12 @@ __global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(Gem
   const uint16_t* wsrc[C::kWDma];
 #pragma unroll
   for (int i = 0; i < C::kWDma; ++i) {
-    const int r = wave * (kWRowsS / 8) + i * C::kRowsPerDma + lrow;  // 0..511 within the weight tile
+    const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;  // row within the weight tile
     const uint16_t* base;
     int n;
     if (SWIGLU) {
-      base = r < kWRowsS / 2 ? W0 : W1;
-      n = n0 + (r & (kWRowsS / 2 - 1));
+      base = r < WROWS / 2 ? W0 : W1;
+      n = n0 + (r % (WROWS / 2));
     } else {
       base = W0;
       n = n0 + r;
@@ -340,10 +354,10 @@ __global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(Gem
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < C::kADma; ++i)
-      lds_dma16(asrc[i] + k0, st + (wave * (kTileM / 8) + i * C::kRowsPerDma) * BK);
+      lds_dma16(asrc[i] + k0, st + (wave * (kTileM / WAVES) + i * C::kRowsPerDma) * BK);
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i)
-      lds_dma16(wsrc[i] + k0, st + (kTileM + wave * (kWRowsS / 8) + i * C::kRowsPerDma) * BK);
+      lds_dma16(wsrc[i] + k0, st + (kTileM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
   };
 
   f32x16 acc[2][4];
@@ -356,7 +370,7 @@ __global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(Gem
   int wrow[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
-    wrow[nb] = SWIGLU ? ((nb >> 1) * (kWRowsS / 2) + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
+    wrow[nb] = SWIGLU ? ((nb >> 1) * (WROWS / 2) + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
   const int l32 = lane & 31, khalf = lane >> 5;
 
   const int nk = K / BK;
@@ -371,23 +385,30 @@ __global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(Gem
     // kt-1, whose buffer the next loads overwrite (__syncthreads() would add a memory fence
     // that also drains the loads still in flight)
     __builtin_amdgcn_s_barrier();
-    if (kt + kAhead < nk) issue_stage(kt + kAhead);
     const uint16_t* st = lds + (kt % C::kStages) * C::kStageElems;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    // fragments of sub-step kk+1 are read while the MFMAs of sub-step kk run
+    bf16x8 xf[2][2], wf[2][4];
+    auto load_frags = [&](int buf, int kk) {
       const int c = kk * 2 + khalf;
-      bf16x8 xf[2], wf[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-        xf[mb] = *reinterpret_cast<const bf16x8*>(st + C::off(wm * 64 + mb * 32 + l32, c));
+        xf[buf][mb] = *reinterpret_cast<const bf16x8*>(st + C::off(wm * 64 + mb * 32 + l32, c));
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        wf[nb] = *reinterpret_cast<const bf16x8*>(st + C::off(kTileM + wrow[nb] + l32, c));
+        wf[buf][nb] = *reinterpret_cast<const bf16x8*>(st + C::off(kTileM + wrow[nb] + l32, c));
+    };
+    load_frags(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) load_frags(cur ^ 1, kk + 1);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][nb], xf[cur][mb], acc[mb][nb], 0, 0, 0);
+      // the next stage's loads go out once this sub-step's MFMAs are queued
+      if (kk == 0 && kt + kAhead < nk) issue_stage(kt + kAhead);
     }
   }
   store_tile<SWIGLU>(acc, static_cast<uint16_t*>(g.out), m0 + wm * 64, n0 + (SWIGLU ? wn * 64 : wn * 128), N, l32,
@@ -396,21 +417,23 @@ __global__ void __launch_bounds__(kThreadsS) grouped_gemm_bf16_stream_kernel(Gem
 
 template <bool SWIGLU>
 hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
-  constexpr int SBK = MOE_STREAM_BK;
+  constexpr int SBK = MOE_STREAM_BK, SW = MOE_STREAM_WAVES, SR = MOE_STREAM_WROWS, SG = MOE_STREAM_WGS;
+  using SC = StreamCfg<SBK, SW, SR, SG>;
   if (g.K % SBK == 0) {
-    const int NT = (int)ceil_div(g.N, SWIGLU ? kWRowsS / 2 : kWRowsS);
-    const size_t lds_bytes = StreamCfg<SBK>::kStages * StreamCfg<SBK>::kStageElems * sizeof(uint16_t);
+    const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
+    const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
+    auto kern = &grouped_gemm_bf16_stream_kernel<SWIGLU, SBK, SW, SR, SG>;
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_stream_kernel<SWIGLU, SBK>),
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
       if (err != hipSuccess) return err;
       attr_set = true;
     }
     const int64_t tiles = g.max_tiles * NT;
-    const int64_t grid = ceil_div(tiles, kXcds * kXcdChunk) * (kXcds * kXcdChunk);
-    hipLaunchKernelGGL((grouped_gemm_bf16_stream_kernel<SWIGLU, SBK>), dim3((unsigned)grid), dim3(kThreadsS), lds_bytes,
-                       st, g, NT);
+    const int64_t span = kXcds * SC::kXcdChunk;
+    const int64_t grid = ceil_div(tiles, span) * span;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SC::kThreads), lds_bytes, st, g, NT);
     return hipGetLastError();
   }
   const size_t lds_bytes = 2 * kStageElems * sizeof(uint16_t);
