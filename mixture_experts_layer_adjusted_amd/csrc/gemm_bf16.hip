@@ -50,10 +50,16 @@ constexpr int kStageElems = (kTileM + kWRows) * kBK;  // bf16 elements per LDS s
 #define MOE_STREAM_WAVES 8
 #endif
 #ifndef MOE_STREAM_WROWS
-#define MOE_STREAM_WROWS 512
+#define MOE_STREAM_WROWS 256
 #endif
 #ifndef MOE_STREAM_WGS
 #define MOE_STREAM_WGS 1
+#endif
+#ifndef MOE_STREAM_WM
+#define MOE_STREAM_WM 2
+#endif
+#ifndef MOE_STREAM_TM
+#define MOE_STREAM_TM 256
 #endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -76,22 +82,23 @@ __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x));
 
 
 // Epilogue: the lane holds, for row r0 + 32 mb + l32, features 8 q + 4 khalf + (0..3) of each
-// 32-feature block; SwiGLU pairs gate block nb with up block nb + 2.
-template <bool SWIGLU>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[2][4], uint16_t* out, int64_t r0, int fbase,
+// 32-feature block; SwiGLU pairs gate block nb with up block nb + NBW/2, the gate blocks covering
+// features fbase + 32 nb.
+template <bool SWIGLU, int MB = 2, int NBW = 4>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MB][NBW], uint16_t* out, int64_t r0, int fbase,
                                            int N, int l32, int khalf) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     uint16_t* orow = out + (r0 + mb * 32 + l32) * N;
 #pragma unroll
-    for (int nb = 0; nb < (SWIGLU ? 2 : 4); ++nb) {
+    for (int nb = 0; nb < (SWIGLU ? NBW / 2 : NBW); ++nb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int f = fbase + nb * 32 + q * 8 + khalf * 4;
         uint16_t h[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          h[v] = SWIGLU ? f32_to_bf16(silu(acc[mb][nb][q * 4 + v]) * acc[mb][nb + 2][q * 4 + v])
+          h[v] = SWIGLU ? f32_to_bf16(silu(acc[mb][nb][q * 4 + v]) * acc[mb][nb + NBW / 2][q * 4 + v])
                         : f32_to_bf16(acc[mb][nb][q * 4 + v]);
         if (f + 3 < N) {
           *reinterpret_cast<uint2*>(orow + f) =
@@ -221,32 +228,37 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_bf16_kernel(GemmOperand
 
 // ---------------------------------------------------------------------------- streaming variant
 //
-// WAVES wavefronts own 128 rows x WROWS weight rows (gate/up: WROWS/2 gate + the matching
-// WROWS/2 up features; down: WROWS output features); wavefront (wm, wn) of the 2 x (WAVES/2)
-// grid computes 64 rows x 128 weight rows as in the register-staged kernel.  WGS workgroups
-// share a CU, each with 160 KB / WGS of LDS holding as many stages of (128 + WROWS) x BK bf16
-// as fit; direct global->LDS loads run (stages - 1) K-steps ahead of the MFMAs.
+// WAVES wavefronts own TM rows (128, one M-tile; or 256, two M-tiles of the same segment) x
+// WROWS weight rows (gate/up: WROWS/2 gate + the matching WROWS/2 up features; down: WROWS
+// output features); wavefront (wm, wn) of the WM x (WAVES/WM) grid computes TM/WM rows x
+// WROWS/(WAVES/WM) weight rows.  WGS workgroups share a CU, each with 160 KB / WGS of LDS
+// holding as many stages of (TM + WROWS) x BK bf16 as fit; direct global->LDS loads run
+// (stages - 1) K-steps ahead of the MFMAs.  With TM = 256 a segment with an odd number of
+// M-tiles ends in a half tile: its second 128 rows belong to the next segment, so they load
+// a valid row and the wavefronts owning them skip their MFMAs and stores.
 
 constexpr int kLdsBytes = 163840;
 constexpr int kXcds = 8;          // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
 constexpr int kCusPerXcd = 32;
 constexpr int kGroupM = MOE_GROUP_M;  // M-tiles per block of the within-expert order
 
-template <int BK, int WAVES, int WROWS, int WGS>
+template <int BK, int WAVES, int WROWS, int WGS, int TM>
 struct StreamCfg {
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kRowBytes = BK * 2;
   static constexpr int kChunks = BK / 8;                       // 16-byte chunks per LDS row
   static constexpr int kRowsPer256 = 256 / kRowBytes;          // rows sharing one pass of the 64 banks
-  static constexpr int kStageElems = (kTileM + WROWS) * BK;
+  static constexpr int kStageElems = (TM + WROWS) * BK;
   static constexpr int kStages = (kLdsBytes / WGS) / (kStageElems * 2);
   static constexpr int kRowsPerDma = 1024 / kRowBytes;          // rows one wave-wide 1 KB load fills
-  static constexpr int kADma = kTileM / kRowsPerDma / WAVES;    // activation loads per wave per stage
+  static constexpr int kADma = TM / kRowsPerDma / WAVES;        // activation loads per wave per stage
   static constexpr int kWDma = WROWS / kRowsPerDma / WAVES;     // weight loads per wave per stage
   static constexpr int kDmaPerStage = kADma + kWDma;
   static constexpr int kXcdChunk = kCusPerXcd * WGS;            // workgroups an XCD holds at once
   static_assert(kStages >= 2, "at least two LDS stages");
-  static_assert(kADma * kRowsPerDma * WAVES == kTileM && kWDma * kRowsPerDma * WAVES == WROWS, "load split");
+  static_assert(kADma * kRowsPerDma * WAVES == TM && kWDma * kRowsPerDma * WAVES == WROWS, "load split");
+  static_assert((WROWS / WAVES) % kRowsPerDma == 0 && (WROWS / 2) % (WROWS / WAVES) == 0,
+                "gate/up split on a wave boundary");
   // chunk c of row r sits at slot c ^ swz(r): the 16 rows of a 16-lane read pass then cover all
   // 64 banks once (rows in one 256-byte bank span differ in their bank offset, rows in different
   // spans in their slot)
@@ -283,95 +295,107 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   wait_vmcnt<0>();
 }
 
-template <bool SWIGLU, int BK, int WAVES, int WROWS, int WGS>
+template <bool SWIGLU, int BK, int WAVES, int WROWS, int WGS, int WM, int TM>
 __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kernel(GemmOperands g, int NT) {
-  using C = StreamCfg<BK, WAVES, WROWS, WGS>;
+  using C = StreamCfg<BK, WAVES, WROWS, WGS, TM>;
+  constexpr int WN = WAVES / WM;           // wavefront grid WM x WN
+  constexpr int RW = TM / WM;              // rows per wavefront
+  constexpr int MB = RW / 32;              // 32-row blocks per wavefront
+  constexpr int WRW = WROWS / WN;          // weight rows per wavefront
+  constexpr int NBW = WRW / 32;            // 32-row weight blocks per wavefront
+  static_assert(TM == kTileM || TM == 2 * kTileM, "tile of one or two M-tiles");
+  static_assert(!SWIGLU || NBW % 2 == 0, "SwiGLU pairs gate and up blocks");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   // ---- logical tile of this workgroup (see the file comment)
   const int b = blockIdx.x;
   constexpr int kSpan = kXcds * C::kXcdChunk;
   const int64_t L = (int64_t)(b / kSpan) * kSpan + (b % kXcds) * C::kXcdChunk + (b / kXcds) % C::kXcdChunk;
-  const int64_t mt_glob = L / NT;
-  if (mt_glob >= g.max_tiles) return;
-  const int seg = g.tile_seg[mt_glob];
+  const int64_t slot = L / NT;             // M-tile (TM = 128) or pair of M-tiles (TM = 256)
+  if (slot >= g.max_tiles) return;
+  const int seg = TM == kTileM ? g.tile_seg[slot] : g.pair_seg[slot];
   if (seg < 0) return;
-  const int seg_m0 = g.seg_off[seg] / kTileM;
-  const int seg_mt = g.seg_off[seg + 1] / kTileM - seg_m0;
-  const int64_t lam = L - (int64_t)seg_m0 * NT;
+  const int seg_first = TM == kTileM ? g.seg_off[seg] / kTileM : g.pair_off[seg];
+  const int seg_count = TM == kTileM ? g.seg_off[seg + 1] / kTileM - seg_first : g.pair_off[seg + 1] - seg_first;
+  const int64_t lam = L - (int64_t)seg_first * NT;
   const int grp = (int)(lam / (kGroupM * NT));
-  const int gm = min(kGroupM, seg_mt - grp * kGroupM);
+  const int gm = min(kGroupM, seg_count - grp * kGroupM);
   const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
-  const int mt = seg_m0 + grp * kGroupM + rem % gm;
+  const int local = grp * kGroupM + rem % gm;
   const int nt = rem / gm;
+  const int64_t m0 = (int64_t)g.seg_off[seg] + (int64_t)local * TM;
+  // rows of this tile that belong to the segment (a half tile has 128)
+  const int tile_rows = TM == kTileM ? TM : min(TM, g.seg_off[seg + 1] - (int)(m0));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS offsets stay scalar
-  constexpr int WN = WAVES / 2;
   const int wm = wave / WN, wn = wave % WN;
   const int K = g.K, N = g.N;
-  const int64_t m0 = (int64_t)mt * kTileM;
   const int n0 = nt * (SWIGLU ? WROWS / 2 : WROWS);
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
   const size_t wstride = (size_t)N * K;
-  const uint16_t* W0 = static_cast<const uint16_t*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride;
-  const uint16_t* W1 = SWIGLU ? static_cast<const uint16_t*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride
-                              : nullptr;
-  const uint16_t* act = static_cast<const uint16_t*>(g.act);
+  const char* W0 = static_cast<const char*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride * 2;
+  const char* W1 = SWIGLU ? static_cast<const char*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride * 2
+                          : nullptr;
+  const char* act = static_cast<const char*>(g.act);
 
-  // ---- per-lane sources: wave w fills activation rows [w * 128/WAVES, +128/WAVES) and weight-tile
-  // rows [w * WROWS/WAVES, +WROWS/WAVES), kRowsPerDma rows per load; lane l covers row l / kChunks
-  // of its load and slot l % kChunks, which holds logical chunk slot ^ swz(row)
+  // ---- per-lane sources, as 32-bit byte offsets from a wave-uniform base (the launcher checks that
+  // the activation matrix and one expert's weight matrix stay below 4 GiB): wave w fills activation
+  // rows [w * TM/WAVES, +TM/WAVES) and weight-tile rows [w * WROWS/WAVES, +WROWS/WAVES),
+  // kRowsPerDma rows per load; lane l covers row l / kChunks of its load and slot l % kChunks,
+  // which holds logical chunk slot ^ swz(row)
   const int lrow = lane / C::kChunks;
   const int lslot = lane % C::kChunks;
-  const uint16_t* asrc[C::kADma];
+  uint32_t aoff[C::kADma];
 #pragma unroll
   for (int i = 0; i < C::kADma; ++i) {
-    const int row = wave * (kTileM / WAVES) + i * C::kRowsPerDma + lrow;
-    int64_t tok = g.row_token ? (int64_t)g.row_token[m0 + row] : m0 + row;
+    const int row = wave * (TM / WAVES) + i * C::kRowsPerDma + lrow;
+    const int64_t r = m0 + (row < tile_rows ? row : 0);  // rows past a half tile: a valid row
+    int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;  // padding row: any valid row (its outputs are never read)
-    asrc[i] = act + tok * K + ((lslot ^ C::swz(row)) << 3);
+    aoff[i] = (uint32_t)(tok * K * 2) + ((lslot ^ C::swz(row)) << 4);
   }
-  const uint16_t* wsrc[C::kWDma];
+  uint32_t woff[C::kWDma];
 #pragma unroll
   for (int i = 0; i < C::kWDma; ++i) {
     const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;  // row within the weight tile
-    const uint16_t* base;
-    int n;
-    if (SWIGLU) {
-      base = r < WROWS / 2 ? W0 : W1;
-      n = n0 + (r % (WROWS / 2));
-    } else {
-      base = W0;
-      n = n0 + r;
-    }
+    int n = n0 + (SWIGLU ? r % (WROWS / 2) : r);
     if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-    wsrc[i] = base + (size_t)n * K + ((lslot ^ C::swz(kTileM + r)) << 3);
+    woff[i] = (uint32_t)n * (uint32_t)(K * 2) + ((lslot ^ C::swz(TM + r)) << 4);
   }
+  // gate rows come from W0, up rows from W1; the split falls on a wave boundary
+  const char* wbase = (SWIGLU && wave * (WROWS / WAVES) >= WROWS / 2) ? W1 : W0;
   auto issue_stage = [&](int kt) {
     uint16_t* st = lds + (kt % C::kStages) * C::kStageElems;
-    const int k0 = kt * BK;
+    const int k0 = kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < C::kADma; ++i)
-      lds_dma16(asrc[i] + k0, st + (wave * (kTileM / WAVES) + i * C::kRowsPerDma) * BK);
+      lds_dma16(act + k0 + aoff[i], st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i)
-      lds_dma16(wsrc[i] + k0, st + (kTileM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
+      lds_dma16(wbase + k0 + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[MB][NBW];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < NBW; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
-  int wrow[4];
+  int wrow[NBW];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    wrow[nb] = SWIGLU ? ((nb >> 1) * (WROWS / 2) + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
+  for (int nb = 0; nb < NBW; ++nb) {
+    if (SWIGLU)
+      wrow[nb] = nb < NBW / 2 ? wn * (WRW / 2) + nb * 32 : WROWS / 2 + wn * (WRW / 2) + (nb - NBW / 2) * 32;
+    else
+      wrow[nb] = wn * WRW + nb * 32;
+  }
   const int l32 = lane & 31, khalf = lane >> 5;
+  const int mrow0 = wm * RW;
+  const bool active = mrow0 < tile_rows;   // false only for the upper half of a half tile
+  constexpr bool kAccInAgprs = MB * NBW * 16 > 128;
 
   const int nk = K / BK;
   constexpr int kAhead = C::kStages - 1;
@@ -387,42 +411,58 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
     __builtin_amdgcn_s_barrier();
     const uint16_t* st = lds + (kt % C::kStages) * C::kStageElems;
     // fragments of sub-step kk+1 are read while the MFMAs of sub-step kk run
-    bf16x8 xf[2][2], wf[2][4];
-    auto load_frags = [&](int buf, int kk) {
-      const int c = kk * 2 + khalf;
+    auto mma_stage = [&]() {
+      bf16x8 xf[2][MB], wf[2][NBW];
+      auto load_frags = [&](int buf, int kk) {
+        const int c = kk * 2 + khalf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        xf[buf][mb] = *reinterpret_cast<const bf16x8*>(st + C::off(wm * 64 + mb * 32 + l32, c));
+        for (int mb = 0; mb < MB; ++mb)
+          xf[buf][mb] = *reinterpret_cast<const bf16x8*>(st + C::off(mrow0 + mb * 32 + l32, c));
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        wf[buf][nb] = *reinterpret_cast<const bf16x8*>(st + C::off(kTileM + wrow[nb] + l32, c));
+        for (int nb = 0; nb < NBW; ++nb)
+          wf[buf][nb] = *reinterpret_cast<const bf16x8*>(st + C::off(TM + wrow[nb] + l32, c));
+      };
+      load_frags(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < BK / 16) load_frags(cur ^ 1, kk + 1);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][nb], xf[cur][mb], acc[mb][nb], 0, 0, 0);
+        // the next stage's loads go out once this sub-step's MFMAs are queued
+        if (kk == 0 && kt + kAhead < nk) issue_stage(kt + kAhead);
+      }
     };
-    load_frags(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) load_frags(cur ^ 1, kk + 1);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][nb], xf[cur][mb], acc[mb][nb], 0, 0, 0);
-      // the next stage's loads go out once this sub-step's MFMAs are queued
-      if (kk == 0 && kt + kAhead < nk) issue_stage(kt + kAhead);
+    if constexpr (kAccInAgprs) {
+      // accumulators beyond 256 VGPRs live in AGPRs; a branch around the MFMAs would make the
+      // compiler copy them to VGPRs and back every K-step, so the upper half of a half tile
+      // computes on its copied valid row and only skips its stores
+      mma_stage();
+    } else if (active) {
+      mma_stage();
+    } else if (kt + kAhead < nk) {
+      issue_stage(kt + kAhead);
     }
   }
-  store_tile<SWIGLU>(acc, static_cast<uint16_t*>(g.out), m0 + wm * 64, n0 + (SWIGLU ? wn * 64 : wn * 128), N, l32,
-                     khalf);
+  if (active)
+    store_tile<SWIGLU, MB, NBW>(acc, static_cast<uint16_t*>(g.out), m0 + mrow0,
+                                n0 + wn * (SWIGLU ? WRW / 2 : WRW), N, l32, khalf);
 }
 
 template <bool SWIGLU>
 hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
   constexpr int SBK = MOE_STREAM_BK, SW = MOE_STREAM_WAVES, SR = MOE_STREAM_WROWS, SG = MOE_STREAM_WGS;
-  using SC = StreamCfg<SBK, SW, SR, SG>;
-  if (g.K % SBK == 0) {
+  constexpr int SM = MOE_STREAM_WM, STM = MOE_STREAM_TM;
+  using SC = StreamCfg<SBK, SW, SR, SG, STM>;
+  // the streaming kernel addresses its sources with 32-bit byte offsets
+  const bool offsets_fit = g.act_rows * g.K * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.K * 2 < (int64_t(1) << 32);
+  if (g.K % SBK == 0 && offsets_fit) {
     const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
     const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
-    auto kern = &grouped_gemm_bf16_stream_kernel<SWIGLU, SBK, SW, SR, SG>;
+    auto kern = &grouped_gemm_bf16_stream_kernel<SWIGLU, SBK, SW, SR, SG, SM, STM>;
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -430,7 +470,7 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
       if (err != hipSuccess) return err;
       attr_set = true;
     }
-    const int64_t tiles = g.max_tiles * NT;
+    const int64_t tiles = (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
     const int64_t span = kXcds * SC::kXcdChunk;
     const int64_t grid = ceil_div(tiles, span) * span;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SC::kThreads), lds_bytes, st, g, NT);

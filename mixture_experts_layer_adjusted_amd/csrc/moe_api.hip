@@ -57,6 +57,8 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.seg_off = take((size_t)(N + Ns + 1) * 4);
   p.seg_rows = take((size_t)(N + Ns) * 4);
   p.tile_seg = take((size_t)p.max_tiles * 4);
+  p.pair_seg = take((size_t)p.max_tiles * 4);
+  p.pair_off = take((size_t)(N + Ns + 1) * 4);
   p.row_token = take((size_t)p.max_rows * 4);
   p.perm_row = take((size_t)T * K * 4);
   p.h = take((size_t)p.max_rows * I * (fp8 ? 1 : elem_bytes(s.dtype)));
@@ -141,10 +143,14 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.s_shared[1] = w->sh_up_scale;
   g1.tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
   g1.seg_off = reinterpret_cast<const int32_t*>(wsb + p.seg_off);
+  g1.pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
+  g1.pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
   g1.n_routed = s.n_routed;
   g1.K = s.hidden;
   g1.N = s.inter;
+  g1.act_rows = s.tokens;
   g1.max_tiles = p.max_tiles;
+  g1.max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + s.n_routed + s.n_shared) / 2);
   g1.out = wsb + p.h;
   g1.out_scale = fp8 ? reinterpret_cast<float*>(wsb + p.h_scale) : nullptr;
   if ((rc = hip_status(launch_gemm_swiglu(s.dtype, g1, st))) != MOE_OK) return rc;
@@ -160,10 +166,14 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g2.s_shared[0] = w->sh_down_scale;
   g2.tile_seg = g1.tile_seg;
   g2.seg_off = g1.seg_off;
+  g2.pair_seg = g1.pair_seg;
+  g2.pair_off = g1.pair_off;
   g2.n_routed = s.n_routed;
   g2.K = s.inter;
   g2.N = s.hidden;
+  g2.act_rows = p.max_rows;
   g2.max_tiles = p.max_tiles;
+  g2.max_pairs = g1.max_pairs;
   g2.out = wsb + p.y;
   if ((rc = hip_status(launch_gemm_down(s.dtype, g2, st))) != MOE_OK) return rc;
   if (mark(4) != hipSuccess) return MOE_ERR_HIP;

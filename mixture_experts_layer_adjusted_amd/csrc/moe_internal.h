@@ -34,6 +34,8 @@ struct WorkspacePlan {
   size_t seg_off;           // int32 [N_r + N_s + 1]   first padded row of each segment
   size_t seg_rows;          // int32 [N_r + N_s]       real rows of each segment
   size_t tile_seg;          // int32 [max_tiles]       segment of each M-tile, -1 past the end
+  size_t pair_seg;          // int32 [max_tiles]       segment of each pair of M-tiles (256-row tiles), -1 past the end
+  size_t pair_off;          // int32 [N_r + N_s + 1]   first pair of each segment
   size_t row_token;         // int32 [max_rows]        token of each permuted row, -1 for padding
   size_t perm_row;          // int32 [T, K_r]          permuted row of each (token, slot), -1 if skipped
   size_t h;                 // [max_rows, I]  bf16 / fp32 / e4m3
@@ -72,9 +74,14 @@ struct GemmOperands {
   const float* s_shared[2];
   const int32_t* tile_seg;
   const int32_t* seg_off;    // [N_r + N_s + 1] first padded row of each segment
+  const int32_t* pair_seg;   // [max_tiles] segment of each 256-row tile (pairs of M-tiles; a segment
+                             // with an odd M-tile count ends in a half tile)
+  const int32_t* pair_off;   // [N_r + N_s + 1] first 256-row tile of each segment
   int n_routed;
   int K, N;                  // contraction length, output features per expert
+  int64_t act_rows;          // rows of act
   int64_t max_tiles;
+  int64_t max_pairs;         // upper bound on the 256-row tiles: min(max_tiles, (max_tiles + N_r + N_s) / 2)
   void* out;                 // [max_rows, N]
   float* out_scale;          // fp8 SwiGLU output: [max_rows, N/128]
 };

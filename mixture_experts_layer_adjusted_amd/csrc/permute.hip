@@ -13,7 +13,8 @@
 //            by scanning the chunk's topk_idx from LDS;
 //  segments: one workgroup turns the per-chunk counts into segment sizes, padded
 //            segment offsets (block-wide exclusive scan), the row base of every
-//            (chunk, expert) pair, and the segment id of every M-tile;
+//            (chunk, expert) pair, the segment id of every M-tile, and the same for
+//            256-row tiles (pairs of M-tiles, a second scan);
 //  scatter:  per chunk, thread e walks the chunk's picks in (token, slot) order and
 //            hands out consecutive rows of segment e; extra workgroups write the
 //            identity rows of the shared segments and mark padding rows -1.
@@ -46,9 +47,11 @@ __global__ void __launch_bounds__(kSegThreads) perm_segments_kernel(const int32_
                                                                     int64_t max_tiles, int32_t* __restrict__ base,
                                                                     int32_t* __restrict__ seg_off,
                                                                     int32_t* __restrict__ seg_rows,
-                                                                    int32_t* __restrict__ tile_seg) {
+                                                                    int32_t* __restrict__ tile_seg,
+                                                                    int32_t* __restrict__ pair_seg,
+                                                                    int32_t* __restrict__ pair_off) {
   __shared__ int32_t scan[kSegThreads];
-  __shared__ int32_t total_rows;
+  __shared__ int32_t total_rows, total_pairs;
   const int tid = threadIdx.x;
   const int nseg = N + Ns;
   int rows = 0;
@@ -81,9 +84,30 @@ __global__ void __launch_bounds__(kSegThreads) perm_segments_kernel(const int32_
       run += counts[c * N + tid];
     }
   }
+  // second scan: 256-row tiles (pairs of M-tiles) per segment
+  const int pairs = (padded / kTileM + 1) / 2;
   __syncthreads();
-  if (tid == 0) seg_off[nseg] = total_rows;
+  scan[tid] = pairs;
+  __syncthreads();
+  for (int off = 1; off < kSegThreads; off <<= 1) {
+    int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int pstart = scan[tid] - pairs;
+  if (tid == kSegThreads - 1) total_pairs = scan[tid];
+  if (tid < nseg) {
+    pair_off[tid] = pstart;
+    for (int j = 0; j < pairs; ++j) pair_seg[pstart + j] = tid;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    seg_off[nseg] = total_rows;
+    pair_off[nseg] = total_pairs;
+  }
   for (int64_t j = total_rows / kTileM + tid; j < max_tiles; j += kSegThreads) tile_seg[j] = -1;
+  for (int64_t j = total_pairs + tid; j < max_tiles; j += kSegThreads) pair_seg[j] = -1;
 }
 
 __global__ void __launch_bounds__(kThreads) perm_scatter_kernel(const int32_t* __restrict__ idx, int T, int K, int N,
@@ -139,6 +163,8 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const Workspac
   int32_t* seg_off = reinterpret_cast<int32_t*>(ws + p.seg_off);
   int32_t* seg_rows = reinterpret_cast<int32_t*>(ws + p.seg_rows);
   int32_t* tile_seg = reinterpret_cast<int32_t*>(ws + p.tile_seg);
+  int32_t* pair_seg = reinterpret_cast<int32_t*>(ws + p.pair_seg);
+  int32_t* pair_off = reinterpret_cast<int32_t*>(ws + p.pair_off);
   int32_t* row_token = reinterpret_cast<int32_t*>(ws + p.row_token);
   int32_t* perm_row = reinterpret_cast<int32_t*>(ws + p.perm_row);
   if (p.chunks > 0) {
@@ -147,7 +173,7 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const Workspac
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(perm_segments_kernel, dim3(1), dim3(kSegThreads), 0, st, counts, p.chunks, T, N, Ns,
-                     p.max_tiles, base, seg_off, seg_rows, tile_seg);
+                     p.max_tiles, base, seg_off, seg_rows, tile_seg, pair_seg, pair_off);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)(p.chunks + N + Ns)), dim3(kThreads), 0, st, idx, T, K,
