@@ -5,11 +5,11 @@
 // list: E4M3 operands, one fp32 scale per 1x128 activation tile and per 128x128 weight
 // block, accumulation in fp32.  The page's design for its hardware moves the partial
 // sums of every 128-element K block out of the tensor cores into fp32 registers and
-// scales them there; gfx950's MFMA accumulates in full fp32 already, so the same
-// arithmetic is laid out as: per 128-wide K-step (one scale block) a fresh MFMA
-// accumulator collects the raw E4M3 products (v_mfma_scale_f32_32x32x64_f8f6f4 with
-// unit E8M0 scales), which is then added to the fp32 result with the factor
-// act_scale[row][kb] * weight_scale[feature block][kb].
+// scales them there.  On gfx950 one v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales)
+// contracts a whole 128-element scale block of a 16x16 output block, so every MFMA result
+// is that block's raw partial sum: it is folded into the fp32 result at once with the
+// factor act_scale[row][kb] * weight_scale[feature block][kb], and no partial accumulator
+// outlives its MFMA.
 //
 //   gate/up:  H[r, n] = SiLU(x_r . Wg[e][n]) * (x_r . Wu[e][n]), then H is quantised per
 //             1x128 tile along I (scale = amax / 448, round to nearest even, saturate);
@@ -17,12 +17,13 @@
 //             amax is a reduction across the four wavefronts that share the row
 //   down:     Y[r, n] = H[r] . Wd[e][n] in bf16
 //
-// Tiling: 512 threads (8 wavefronts, two per SIMD), 128 rows x 256 weight rows (gate/up: 128
-// gate + the matching 128 up features; down: 256 output features), wavefront (wm, wn) of the
-// 2 x 4 grid owning 64 rows x 64 weight rows.  One K-step is 128 bytes of every row, the LDS
-// row pitch of the bf16 kernels, with the same XOR swizzle (conflict-free 16-lane reads), three
-// 48 KB stages filled by direct global->LDS loads two K-steps ahead, and the same XCD-aware
-// tile order (blocks of 4 M-tiles x 8 N-tiles of one expert per XCD).
+// Tiling: 512 threads (8 wavefronts, two per SIMD), 256 rows (two M-tiles of one segment;
+// a segment with an odd M-tile count ends in a half tile whose upper wavefronts idle) x
+// 256 weight rows (gate/up: 128 gate + the matching 128 up features; down: 256 output
+// features).  Wavefront (wm, wn) of the 2 x 4 grid owns 128 rows x 64 weight rows as 8 x 4
+// blocks of 16 x 16.  One K-step is one 128-byte scale block of every row, staged in LDS
+// with a 16-byte-chunk XOR swizzle (conflict-free 16-lane reads) by direct global->LDS loads
+// one K-step ahead, in the XCD-aware tile order of the bf16 kernels.
 #include "fp8_codec.h"
 #include "moe_internal.h"
 
@@ -30,20 +31,26 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kTM = 2 * kTileM;     // activation rows per workgroup
 constexpr int kBK = 128;            // K elements (bytes) per step = one scale block
 constexpr int kWRows = 256;
-constexpr int kStages = 3;
-constexpr int kDataBytes = (kTileM + kWRows) * kBK;   // 48 KB of operands per stage
-constexpr int kScaleBytes = 1024;                      // 128 row scales + 2 weight-block scales, padded
+constexpr int kStages = 2;
+constexpr int kDataBytes = (kTM + kWRows) * kBK;      // 64 KB of operands per stage
+constexpr int kScaleBytes = 2048;                      // 256 row scales + 2 weight-block scales, padded
 constexpr int kStageBytes = kDataBytes + kScaleBytes;
+constexpr int kRowsPerDma = 8;                         // 128-byte rows one wave-wide 1 KB load fills
+constexpr int kADma = kTM / kRowsPerDma / kWaves;      // 4
+constexpr int kWDma = kWRows / kRowsPerDma / kWaves;   // 4
 constexpr int kXcds = 8;
 constexpr int kXcdChunk = 32;
-constexpr int kGroupM = 4;
-constexpr int kDmaPerStage = 7;     // loads per wavefront per stage: 2 activation + 4 weight (1 KB) + 1 scale
+constexpr int kGroupM = 4;          // 256-row tiles per block of the within-expert order
 constexpr int kE8M0One = 127;       // E8M0 encoding of 2^0
+constexpr int kMB = 8;              // 16-row token blocks per wavefront
+constexpr int kNB = 4;              // 16-row weight blocks per wavefront
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -72,28 +79,30 @@ __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x));
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands g, int NT) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ float row_amax[kTileM][4];
-  // ---- logical tile (same XCD-aware order as the bf16 streaming kernel)
+  __shared__ float row_amax[kTM][4];
+  // ---- logical tile (same XCD-aware order as the bf16 streaming kernels, over 256-row tiles)
   const int b = blockIdx.x;
   const int64_t L = (int64_t)(b / (kXcds * kXcdChunk)) * (kXcds * kXcdChunk) + (b % kXcds) * kXcdChunk +
                     (b / kXcds) % kXcdChunk;
-  const int64_t mt_glob = L / NT;
-  if (mt_glob >= g.max_tiles) return;
-  const int seg = g.tile_seg[mt_glob];
+  const int64_t slot = L / NT;
+  if (slot >= g.max_tiles) return;
+  const int seg = g.pair_seg[slot];
   if (seg < 0) return;
-  const int seg_m0 = g.seg_off[seg] / kTileM;
-  const int seg_mt = g.seg_off[seg + 1] / kTileM - seg_m0;
-  const int64_t lam = L - (int64_t)seg_m0 * NT;
+  const int seg_first = g.pair_off[seg];
+  const int seg_count = g.pair_off[seg + 1] - seg_first;
+  const int64_t lam = L - (int64_t)seg_first * NT;
   const int grp = (int)(lam / (kGroupM * NT));
-  const int gm = min(kGroupM, seg_mt - grp * kGroupM);
+  const int gm = min(kGroupM, seg_count - grp * kGroupM);
   const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
-  const int mt = seg_m0 + grp * kGroupM + rem % gm;
+  const int local = grp * kGroupM + rem % gm;
   const int nt = rem / gm;
+  const int64_t m0 = (int64_t)g.seg_off[seg] + (int64_t)local * kTM;
+  const int tile_rows = min(kTM, g.seg_off[seg + 1] - (int)m0);  // 256, or 128 for a half tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int K = g.K, N = g.N, KB = K / kBK;
-  const int64_t m0 = (int64_t)mt * kTileM;
   const int n0 = nt * (SWIGLU ? kWRows / 2 : kWRows);
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
@@ -106,45 +115,41 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   const float* S1 = SWIGLU ? (shared ? g.s_shared[1] : g.s_routed[1]) + e * sstride : nullptr;
   const uint8_t* act = static_cast<const uint8_t*>(g.act);
 
-  // ---- direct-load sources: wave w fills activation rows [16w, 16w+16) and weight-tile rows
-  // [32w, 32w+32), 8 rows of 128 bytes per load; lane l covers row l >> 3, slot l & 7
+  // ---- direct-load sources as 32-bit byte offsets (the launcher checks the sizes): wave w fills
+  // activation rows [32w, 32w+32) and weight-tile rows [32w, 32w+32), 8 rows of 128 bytes per
+  // load; lane l covers row l >> 3 of its load and slot l & 7 (logical chunk slot ^ swz(row))
   const int lrow = lane >> 3, lslot = lane & 7;
-  const uint8_t* asrc[2];
+  uint32_t aoff[kADma];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = wave * 16 + i * 8 + lrow;
-    int64_t tok = g.row_token ? (int64_t)g.row_token[m0 + row] : m0 + row;
+  for (int i = 0; i < kADma; ++i) {
+    const int row = wave * (kTM / kWaves) + i * kRowsPerDma + lrow;
+    const int64_t r = m0 + (row < tile_rows ? row : 0);  // rows past a half tile: a valid row
+    int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;  // padding row: any valid row (outputs never read)
-    asrc[i] = act + tok * K + ((lslot ^ swz(row)) << 4);
+    aoff[i] = (uint32_t)(tok * K) + ((lslot ^ swz(row)) << 4);
   }
-  const uint8_t* wsrc[4];
+  uint32_t woff[kWDma];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 32 + i * 8 + lrow;  // 0..255 within the weight tile
-    const uint8_t* base;
-    int n;
-    if (SWIGLU) {
-      base = r < kWRows / 2 ? W0 : W1;
-      n = n0 + (r & (kWRows / 2 - 1));
-    } else {
-      base = W0;
-      n = n0 + r;
-    }
+  for (int i = 0; i < kWDma; ++i) {
+    const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;  // 0..255 within the weight tile
+    int n = n0 + (SWIGLU ? (r & (kWRows / 2 - 1)) : r);
     if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-    wsrc[i] = base + (size_t)n * K + ((lslot ^ swz(kTileM + r)) << 4);
+    woff[i] = (uint32_t)n * (uint32_t)K + ((lslot ^ swz(kTM + r)) << 4);
   }
-  // ---- scale sources: every wave loads the activation scales of rows [16w, 16w+16) (lanes 0..15,
-  // 4 bytes each) into the stage's scale area; wave 7's lanes 16 and 17 load the scales of the
-  // two 128-row weight blocks of the tile, landing right after the 128 row scales
-  const int l32 = lane & 31, khalf = lane >> 5;
+  // gate rows (waves 0-3) come from W0, up rows (waves 4-7) from W1
+  const uint8_t* wbase = (SWIGLU && wave >= kWaves / 2) ? W1 : W0;
+  // ---- scale sources: lanes 0..31 of wave w load the activation scales of rows [32w, 32w+32)
+  // into the stage's scale area; wave 7's lanes 32 and 33 load the scales of the tile's two
+  // 128-row weight blocks, landing right after the 256 row scales
   const float* ssrc = nullptr;
-  if (lane < 16) {
-    const int row = wave * 16 + lane;
-    int64_t tok = g.row_token ? (int64_t)g.row_token[m0 + row] : m0 + row;
+  if (lane < 32) {
+    const int row = wave * 32 + lane;
+    const int64_t r = m0 + (row < tile_rows ? row : 0);
+    int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;
     ssrc = g.act_scale + tok * KB;
-  } else if (wave == 7 && lane < 18) {
-    const int nb = lane - 16;
+  } else if (wave == kWaves - 1 && lane < 34) {
+    const int nb = lane - 32;
     if (SWIGLU) {
       ssrc = (nb == 0 ? S0 : S1) + (size_t)(n0 / kBK) * KB;  // gate block, then the matching up block
     } else {
@@ -156,144 +161,127 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     uint8_t* st = lds + (kt % kStages) * kStageBytes;
     const int k0 = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(asrc[i] + k0, (lds_void_t*)(st + (wave * 16 + i * 8) * kBK), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(wsrc[i] + k0, (lds_void_t*)(st + (kTileM + wave * 32 + i * 8) * kBK), 16, 0,
+    for (int i = 0; i < kADma; ++i)
+      __builtin_amdgcn_global_load_lds(act + k0 + aoff[i],
+                                       (lds_void_t*)(st + (wave * (kTM / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
                                        0);
-    // lanes without a scale to load stay inactive for this one load (it still counts once)
-    if (ssrc) __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 64), 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kWDma; ++i)
+      __builtin_amdgcn_global_load_lds(
+          wbase + k0 + woff[i], (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
+          0);
+    // every wave has active lanes here, so every wave issues this load
+    if (ssrc) __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
   };
 
-  // weight rows of the wave's two 32-row blocks, and the 128-row scale block each falls in
-  int wrow[2], wblk[2];
+  // weight rows of the wave's four 16-row blocks, and the 128-row scale block each falls in
+  int wrow[kNB], wblk[kNB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     if (SWIGLU) {
-      wrow[nb] = nb * (kWRows / 2) + wn * 32;      // gate block, then the matching up block
-      wblk[nb] = nb;
+      wrow[nb] = (nb < 2 ? 0 : kWRows / 2) + wn * 32 + (nb & 1) * 16;  // gate blocks, then the matching up blocks
+      wblk[nb] = nb < 2 ? 0 : 1;
     } else {
-      wrow[nb] = wn * 64 + nb * 32;
+      wrow[nb] = wn * 64 + nb * 16;
       wblk[nb] = wrow[nb] / kBK;
     }
   }
+  const int l16 = lane & 15, kq = lane >> 4;  // token of the 16x16 block; K quarter and feature group
+  const int mrow0 = wm * (kTM / 2);
+  const bool active = mrow0 < tile_rows;      // false only for the upper half of a half tile
 
-  float acc[2][2][16];
+  f32x4 acc[kMB][kNB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kMB; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+    for (int c = 0; c < kNB; ++c) acc[a][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nk = KB;
   issue_stage(0);
-  if (nk > 1) issue_stage(1);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) wait_vmcnt<kDmaPerStage>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // stage kt landed for every wave; stage kt-1 is no longer read
-    if (kt + 2 < nk) issue_stage(kt + 2);
-    const uint8_t* st = lds + (kt % kStages) * kStageBytes;
-    const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
-    f32x16 part[2][2];
+    wait_vmcnt<0>();
+    // a bare barrier: every wave's loads of stage kt have landed and stage kt-1 is no longer read
+    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < nk) issue_stage(kt + 1);
+    if (active) {
+      const uint8_t* st = lds + (kt % kStages) * kStageBytes;
+      const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
+      i32x8 wf[kNB];
+      float sw[kNB];
 #pragma unroll
-    for (int kk = 0; kk < kBK / 64; ++kk) {
-      const int c = kk * 4 + khalf * 2;  // this lane's 32 bytes of the 64-byte slice
-      i32x8 xf[2], wf[2];
+      for (int nb = 0; nb < kNB; ++nb) {
+        wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
+        sw[nb] = sc[kTM + wblk[nb]];
+      }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) xf[mb] = frag32(st, wm * 64 + mb * 32 + l32, c);
+      for (int mb = 0; mb < kMB; ++mb) {
+        const int r = mrow0 + mb * 16 + l16;
+        const i32x8 xf = frag32(st, r, kq * 2);
+        const float sa = sc[r];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) wf[nb] = frag32(st, kTileM + wrow[nb] + l32, c);
+        for (int nb = 0; nb < kNB; ++nb) {
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb], xf, zero, 0, 0, 0, kE8M0One, 0,
+                                                                              kE8M0One);
+          const float f = sa * sw[nb];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          if (kk == 0) {
-            f32x16 z;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-            part[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[nb], xf[mb], z, 0, 0, 0, kE8M0One, 0,
-                                                                           kE8M0One);
-          } else {
-            part[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[nb], xf[mb], part[mb][nb], 0, 0, 0,
-                                                                           kE8M0One, 0, kE8M0One);
-          }
+          for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], f, acc[mb][nb][v]);
         }
-    }
-    // fold the block's products into the fp32 result with act_scale * weight_scale
-    const float sw0 = sc[kTileM + wblk[0]], sw1 = sc[kTileM + wblk[1]];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const float sa = sc[wm * 64 + mb * 32 + l32];
-      const float f0 = sa * sw0, f1 = sa * sw1;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        acc[mb][0][v] = fmaf(part[mb][0][v], f0, acc[mb][0][v]);
-        acc[mb][1][v] = fmaf(part[mb][1][v], f1, acc[mb][1][v]);
       }
     }
   }
 
-  // ---- epilogue.  Lane holds row 64 wm + 32 mb + l32 and, per 32-row weight block, features
-  // 8 q + 4 khalf + (0..3) of that block
+  // ---- epilogue.  Lane holds, for token row mrow0 + 16 mb + l16, features 4 kq + (0..3) of
+  // each 16-row weight block
   if (SWIGLU) {
     uint8_t* out = static_cast<uint8_t*>(g.out);
     const int IB = N / kBK;
-    float h[2][16];
-    float amax[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        h[mb][v] = silu(acc[mb][0][v]) * acc[mb][1][v];
-        amax[mb] = fmaxf(amax[mb], fabsf(h[mb][v]));
-      }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      amax[mb] = fmaxf(amax[mb], __shfl_xor(amax[mb], 32, 64));
-      if (khalf == 0) row_amax[wm * 64 + mb * 32 + l32][wn] = amax[mb];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int r = wm * 64 + mb * 32 + l32;
-      const float a = fmaxf(fmaxf(row_amax[r][0], row_amax[r][1]), fmaxf(row_amax[r][2], row_amax[r][3]));
-      const float scale = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
-      uint8_t* orow = out + (m0 + r) * N;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = n0 + wn * 32 + q * 8 + khalf * 4;
-        uint32_t w = 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) w |= e4m3_from_f32(__fdiv_rn(h[mb][q * 4 + v], scale)) << (8 * v);
-        *reinterpret_cast<uint32_t*>(orow + f) = w;
-      }
-      if (wn == 0 && khalf == 0) g.out_scale[(m0 + r) * IB + n0 / kBK] = scale;
-    }
-  } else {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      uint16_t* orow = out + (m0 + wm * 64 + mb * 32 + l32) * N;
+    for (int mb = 0; mb < kMB; ++mb) {
+      float amax = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = n0 + wrow[nb] + q * 8 + khalf * 4;
-          if (f + 3 < N) {
-            *reinterpret_cast<uint2*>(orow + f) =
-                make_uint2((uint32_t)f32_to_bf16(acc[mb][nb][q * 4 + 0]) |
-                               ((uint32_t)f32_to_bf16(acc[mb][nb][q * 4 + 1]) << 16),
-                           (uint32_t)f32_to_bf16(acc[mb][nb][q * 4 + 2]) |
-                               ((uint32_t)f32_to_bf16(acc[mb][nb][q * 4 + 3]) << 16));
-          } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (f + v < N) orow[f + v] = f32_to_bf16(acc[mb][nb][q * 4 + v]);
-          }
+        for (int v = 0; v < 4; ++v) {
+          acc[mb][nb][v] = silu(acc[mb][nb][v]) * acc[mb][nb + 2][v];  // h, in place of the gate value
+          amax = fmaxf(amax, fabsf(acc[mb][nb][v]));
         }
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      if (kq == 0) row_amax[mrow0 + mb * 16 + l16][wn] = amax;
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        const int r = mrow0 + mb * 16 + l16;
+        const float a = fmaxf(fmaxf(row_amax[r][0], row_amax[r][1]), fmaxf(row_amax[r][2], row_amax[r][3]));
+        const float scale = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+        uint8_t* orow = out + (m0 + r) * N;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int f = n0 + wn * 32 + nb * 16 + kq * 4;
+          uint32_t w = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) w |= e4m3_from_f32(__fdiv_rn(acc[mb][nb][v], scale)) << (8 * v);
+          *reinterpret_cast<uint32_t*>(orow + f) = w;
+        }
+        if (wn == 0 && kq == 0) g.out_scale[(m0 + r) * IB + n0 / kBK] = scale;
+      }
+    }
+  } else if (active) {
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      uint16_t* orow = out + (m0 + mrow0 + mb * 16 + l16) * N;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int f = n0 + wrow[nb] + kq * 4;  // N is a multiple of 128, so f < N covers f + 3
+        if (f < N)
+          *reinterpret_cast<uint2*>(orow + f) =
+              make_uint2((uint32_t)f32_to_bf16(acc[mb][nb][0]) | ((uint32_t)f32_to_bf16(acc[mb][nb][1]) << 16),
+                         (uint32_t)f32_to_bf16(acc[mb][nb][2]) | ((uint32_t)f32_to_bf16(acc[mb][nb][3]) << 16));
+      }
     }
   }
 }
@@ -301,6 +289,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
 template <bool SWIGLU>
 hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
   if (g.K % kBK != 0 || g.N % kBK != 0) return hipErrorInvalidValue;
+  // 32-bit byte offsets address the activation matrix and one expert's weight matrix
+  if (g.act_rows * g.K >= (int64_t(1) << 32) || (int64_t)g.N * g.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const size_t lds_bytes = kStages * kStageBytes;
   static bool attr_set = false;
   if (!attr_set) {
@@ -310,7 +300,7 @@ hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
     attr_set = true;
   }
   const int NT = (int)ceil_div(g.N, SWIGLU ? kWRows / 2 : kWRows);
-  const int64_t tiles = g.max_tiles * NT;
+  const int64_t tiles = g.max_pairs * NT;
   const int64_t grid = ceil_div(tiles, kXcds * kXcdChunk) * (kXcds * kXcdChunk);
   hipLaunchKernelGGL(grouped_gemm_fp8_kernel<SWIGLU>, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT);
   return hipGetLastError();
