@@ -28,24 +28,42 @@ __global__ void update_bias_kernel(int32_t n, int64_t total, const int32_t* __re
   bias[i] = b;
 }
 
-// one wavefront per 1x128 tile: each lane handles 2 consecutive elements
+// 16 lanes per 1x128 tile (8 consecutive elements each, one 16-byte load), 16 tiles per
+// 256-thread workgroup, grid-stride over the tiles
 __global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restrict__ x, int64_t rows, int32_t cols,
                                                         uint8_t* __restrict__ codes, float* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
+  const int sub = threadIdx.x & 15;
   const int64_t tiles_per_row = cols / 128;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tile >= rows * tiles_per_row) return;
-  const int64_t r = tile / tiles_per_row, c0 = (tile % tiles_per_row) * 128;
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(x + r * cols + c0 + 2 * lane);
-  const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xFFFF0000u);
-  float amax = fmaxf(fabsf(v0), fabsf(v1));
+  const int64_t tiles = rows * tiles_per_row;
+  for (int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); tile - (threadIdx.x >> 4) < tiles;
+       tile += (int64_t)gridDim.x * 16) {
+    // every lane of a wave stays in the loop (the shuffles below need all 64): lanes past the
+    // last tile work on a copy of tile 0 and store nothing
+    const bool live = tile < tiles;
+    const int64_t t = live ? tile : 0;
+    const int64_t r = t / tiles_per_row, c0 = (t % tiles_per_row) * 128 + 8 * sub;
+    const uint4 q = *reinterpret_cast<const uint4*>(x + r * cols + c0);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float v[8];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  const float scale = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  const uint32_t q0 = e4m3_from_f32(__fdiv_rn(v0, scale));
-  const uint32_t q1 = e4m3_from_f32(__fdiv_rn(v1, scale));
-  *reinterpret_cast<uint16_t*>(codes + r * cols + c0 + 2 * lane) = (uint16_t)(q0 | (q1 << 8));
-  if (lane == 0) scales[r * tiles_per_row + c0 / 128] = scale;
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    const float scale = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j >> 2] |= e4m3_from_f32(__fdiv_rn(v[j], scale)) << (8 * (j & 3));
+    if (live) {
+      *reinterpret_cast<uint2*>(codes + r * cols + c0) = make_uint2(o[0], o[1]);
+      if (sub == 0) scales[t] = scale;
+    }
+  }
 }
 
 // one workgroup (256 threads) per 128x128 block: each thread handles 64 elements
@@ -109,7 +127,8 @@ hipError_t launch_quantize_act(int64_t rows, int32_t cols, const void* x, uint8_
                                hipStream_t st) {
   const int64_t tiles = rows * (cols / 128);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)ceil_div(tiles, 4)), dim3(256), 0, st,
+  const int64_t blocks = std::min<int64_t>(ceil_div(tiles, 16), 8192);
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                      static_cast<const uint16_t*>(x), rows, cols, codes, scales);
   return hipGetLastError();
 }

@@ -3,17 +3,25 @@
 // The outer sums of the h'_t equation (方法 §2, "DeepSeek-V3 技術報告",
 // xyznot.com/zh-tw/paper/2412.19437): the residual, the always-on shared experts
 // (gate 1) and the gate-weighted routed experts, gathered back from the permuted
-// layout.  One workgroup per token; each thread owns 8 consecutive features and
-// issues all K_r + N_s + 1 row loads before summing them in fp32 in a fixed order
-// (residual, shared experts in order, routed slots in order), so the result is
-// bit-reproducible.  HBM-bound: (K_r + N_s + 2) * d * elem bytes per token.
+// layout.  One workgroup of up to 128 threads per token, each thread owning 8
+// consecutive features per pass; a thread issues all K_r + N_s + 1 row loads before
+// summing them in fp32 in a fixed order (residual, shared experts in order, routed slots
+// in order), so the result is bit-reproducible.  HBM-bound: (K_r + N_s + 2) * d * elem
+// bytes per token.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kMaxThreads = 128;
 constexpr int kVec = 8;
+
+// threads per token: one per 8 features up to two wavefronts (short workgroups keep many
+// tokens in flight per CU, which measured faster than one thread per chunk)
+inline int combine_threads(int d) {
+  const int chunks = (d + kVec - 1) / kVec;
+  return chunks > 64 ? 128 : 64;
+}
 
 struct Vec8 {
   float v[kVec];
@@ -53,7 +61,7 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 }
 
 template <typename T, int KMAX, int SMAX>
-__global__ void __launch_bounds__(kThreads) combine_kernel(const T* __restrict__ u, const T* __restrict__ y,
+__global__ void __launch_bounds__(kMaxThreads) combine_kernel(const T* __restrict__ u, const T* __restrict__ y,
                                                            const float* __restrict__ gate,
                                                            const int32_t* __restrict__ perm_row,
                                                            const int32_t* __restrict__ seg_off, int d, int K, int N,
@@ -74,7 +82,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const T* __restrict__
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) rows[KMAX + s] = s < Ns ? (int64_t)seg_off[N + s] + t : -1;
 
-  for (int j = threadIdx.x * kVec; j < d; j += kThreads * kVec) {
+  for (int j = threadIdx.x * kVec; j < d; j += blockDim.x * kVec) {
     Vec8 acc = load8(u + t * d + j);
     Vec8 parts[KMAX + SMAX];
 #pragma unroll
@@ -100,7 +108,7 @@ hipError_t launch_t(const moe_shape& s, const void* u, const float* gate, const 
   const T* y = reinterpret_cast<const T*>(ws + p.y);
   const int32_t* perm_row = reinterpret_cast<const int32_t*>(ws + p.perm_row);
   const int32_t* seg_off = reinterpret_cast<const int32_t*>(ws + p.seg_off);
-  hipLaunchKernelGGL((combine_kernel<T, KMAX, SMAX>), dim3((unsigned)s.tokens), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((combine_kernel<T, KMAX, SMAX>), dim3((unsigned)s.tokens), dim3(combine_threads(s.hidden)), 0, st,
                      static_cast<const T*>(u), y, gate, perm_row, seg_off, s.hidden, s.top_k, s.n_routed,
                      s.n_shared, static_cast<T*>(out));
   return hipGetLastError();
@@ -117,13 +125,13 @@ hipError_t launch_k(const moe_shape& s, const void* u, const float* gate, const 
 
 // general shapes: loop over the slots instead of holding them in registers
 template <typename T>
-__global__ void __launch_bounds__(kThreads) combine_loop_kernel(const T* __restrict__ u, const T* __restrict__ y,
+__global__ void __launch_bounds__(kMaxThreads) combine_loop_kernel(const T* __restrict__ u, const T* __restrict__ y,
                                                                 const float* __restrict__ gate,
                                                                 const int32_t* __restrict__ perm_row,
                                                                 const int32_t* __restrict__ seg_off, int d, int K,
                                                                 int N, int Ns, T* __restrict__ out) {
   const int64_t t = blockIdx.x;
-  for (int j = threadIdx.x * kVec; j < d; j += kThreads * kVec) {
+  for (int j = threadIdx.x * kVec; j < d; j += blockDim.x * kVec) {
     Vec8 acc = load8(u + t * d + j);
     for (int s = 0; s < Ns; ++s) {
       Vec8 p = load8(y + ((int64_t)seg_off[N + s] + t) * d + j);
@@ -146,7 +154,7 @@ template <typename T>
 hipError_t launch_any(const moe_shape& s, const void* u, const float* gate, const WorkspacePlan& p, const char* ws,
                       void* out, hipStream_t st) {
   if (s.top_k <= 16 && s.n_shared <= 4) return launch_k<T>(s, u, gate, p, ws, out, st);
-  hipLaunchKernelGGL(combine_loop_kernel<T>, dim3((unsigned)s.tokens), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(combine_loop_kernel<T>, dim3((unsigned)s.tokens), dim3(combine_threads(s.hidden)), 0, st,
                      static_cast<const T*>(u), reinterpret_cast<const T*>(ws + p.y), gate,
                      reinterpret_cast<const int32_t*>(ws + p.perm_row), reinterpret_cast<const int32_t*>(ws + p.seg_off),
                      s.hidden, s.top_k, s.n_routed, s.n_shared, static_cast<T*>(out));

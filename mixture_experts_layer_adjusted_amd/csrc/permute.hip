@@ -8,16 +8,16 @@
 // every token, in order, for shared expert s.  Each segment starts on a multiple
 // of kTileM rows, so every M-tile of the grouped GEMM belongs to one expert.
 //
-// Three atomic-free passes:
-//  count:    per chunk of kChunkTokens tokens, thread e counts the picks of expert e
-//            by scanning the chunk's topk_idx from LDS;
+// Three passes, with no global atomics (the result is the same on every run):
+//  count:    per chunk of kChunkTokens tokens, the picks of every expert (LDS counters);
 //  segments: one workgroup turns the per-chunk counts into segment sizes, padded
 //            segment offsets (block-wide exclusive scan), the row base of every
 //            (chunk, expert) pair, the segment id of every M-tile, and the same for
 //            256-row tiles (pairs of M-tiles, a second scan);
-//  scatter:  per chunk, thread e walks the chunk's picks in (token, slot) order and
-//            hands out consecutive rows of segment e; extra workgroups write the
-//            identity rows of the shared segments and mark padding rows -1.
+//  scatter:  per chunk, every pick gets row base[chunk][e] + (picks of e before it in
+//            (token, slot) order), ranked 64 picks at a time with ballots; extra
+//            workgroups write the identity rows of the shared segments and mark padding
+//            rows -1.
 #include "moe_internal.h"
 
 namespace moe {
@@ -26,20 +26,34 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSegThreads = 1024;
 
+// per chunk and expert: the number of picks, from LDS atomic increments (exact integers, so
+// the result does not depend on their order)
 __global__ void __launch_bounds__(kThreads) perm_count_kernel(const int32_t* __restrict__ idx, int T, int K, int N,
                                                               int32_t* __restrict__ counts) {
-  __shared__ int32_t picks[kChunkTokens * kMaxTopK];
+  __shared__ int32_t cnt[kMaxRouted];
   const int c = blockIdx.x;
   const int t0 = c * kChunkTokens;
-  const int nt = min(kChunkTokens, T - t0);
-  const int n = nt * K;
-  for (int q = threadIdx.x; q < n; q += kThreads) picks[q] = idx[(int64_t)t0 * K + q];
+  const int n = min(kChunkTokens, T - t0) * K;
+  for (int e = threadIdx.x; e < N; e += kThreads) cnt[e] = 0;
   __syncthreads();
-  for (int e = threadIdx.x; e < N; e += kThreads) {
-    int cnt = 0;
-    for (int q = 0; q < n; ++q) cnt += (picks[q] == e);
-    counts[(int64_t)c * N + e] = cnt;
+  for (int q = threadIdx.x; q < n; q += kThreads) {
+    const int e = idx[(int64_t)t0 * K + q];
+    if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += kThreads) counts[(int64_t)c * N + e] = cnt[e];
+}
+
+// lanes holding the same expert as this lane (among the lanes with ok set), from one ballot per
+// bit of the expert index
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool ok, int nbits) {
+  uint64_t m = __ballot(ok);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = (e >> bit) & 1;
+    const uint64_t bal = __ballot(ok && set);
+    m &= set ? bal : ~bal;
+  }
+  return m;
 }
 
 __global__ void __launch_bounds__(kSegThreads) perm_segments_kernel(const int32_t* __restrict__ counts,
@@ -117,28 +131,59 @@ __global__ void __launch_bounds__(kThreads) perm_scatter_kernel(const int32_t* _
                                                                 const int32_t* __restrict__ seg_rows,
                                                                 int32_t* __restrict__ row_token,
                                                                 int32_t* __restrict__ perm_row) {
-  __shared__ int32_t picks[kChunkTokens * kMaxTopK];
+  constexpr int kWaves = kThreads / 64;
+  __shared__ int32_t before[kWaves][kMaxRouted];   // picks of each expert ahead of the wave's position
   const int tid = threadIdx.x;
   if (blockIdx.x < chunks) {
+    // The chunk's picks, in (token, slot) order, are split into kWaves contiguous runs, one per
+    // wavefront.  A pick's row is base[chunk][e] + (picks of e in earlier runs) + (picks of e
+    // earlier in its own run); the latter is counted 64 picks at a time: the lanes holding the
+    // same expert are found by ballots, and the highest of them adds the group to the count.
     const int c = blockIdx.x;
     const int t0 = c * kChunkTokens;
-    const int nt = min(kChunkTokens, T - t0);
-    const int n = nt * K;
-    for (int q = tid; q < n; q += kThreads) {
-      int e = idx[(int64_t)t0 * K + q];
-      picks[q] = e;
-      if (e < 0 || e >= N) perm_row[(int64_t)t0 * K + q] = -1;   // ignored pick
+    const int n = min(kChunkTokens, T - t0) * K;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int per = (n + kWaves - 1) / kWaves;
+    const int q0 = wave * per, q1 = min(n, q0 + per);
+    const int nbits = N > 1 ? 32 - __clz(N - 1) : 1;
+    const uint64_t below = (1ull << lane) - 1;
+    const int32_t* cidx = idx + (int64_t)t0 * K;
+    for (int i = tid; i < kWaves * N; i += kThreads) before[i / N][i % N] = 0;
+    __syncthreads();
+    // pass 1: picks of each expert in each run
+    for (int q = q0 + lane; q - lane < q1; q += 64) {
+      const bool valid = q < q1;
+      const int e = valid ? cidx[q] : -1;
+      const bool ok = valid && e >= 0 && e < N;
+      const uint64_t m = same_expert_lanes(e, ok, nbits);
+      if (ok && (m >> lane) == 1ull) before[wave][e] += __popcll(m);   // highest lane of its group
     }
     __syncthreads();
+    // exclusive prefix over the runs, per expert
     for (int e = tid; e < N; e += kThreads) {
-      int row = base[(int64_t)c * N + e];
-      for (int q = 0; q < n; ++q) {
-        if (picks[q] == e) {
-          row_token[row] = t0 + q / K;
-          perm_row[(int64_t)t0 * K + q] = row;
-          ++row;
-        }
+      int acc = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int v = before[w][e];
+        before[w][e] = acc;
+        acc += v;
       }
+    }
+    __syncthreads();
+    // pass 2: rows
+    for (int q = q0 + lane; q - lane < q1; q += 64) {
+      const bool valid = q < q1;
+      const int e = valid ? cidx[q] : -1;
+      const bool ok = valid && e >= 0 && e < N;
+      const uint64_t m = same_expert_lanes(e, ok, nbits);
+      if (valid && !ok) perm_row[(int64_t)t0 * K + q] = -1;   // ignored pick
+      if (ok) {
+        const int row = base[(int64_t)c * N + e] + before[wave][e] + __popcll(m & below);
+        row_token[row] = t0 + q / K;
+        perm_row[(int64_t)t0 * K + q] = row;
+      }
+      // every lane has read its count above (same wavefront, LDS in program order)
+      if (ok && (m >> lane) == 1ull) before[wave][e] += __popcll(m);
     }
     return;
   }
