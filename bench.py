@@ -173,6 +173,27 @@ def main():
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
 
+    # group-limited routing (8 equal expert groups, 4 eligible per token) on the same batch and
+    # bias, timed outside the step: the cost of the limit next to the plain route
+    route_grouped = None
+    if N % 8 == 0 and 4 * (N // 8) >= K:
+        gidx, ggate, gload = torch.empty_like(idx), torch.empty_like(gate), torch.empty_like(load)
+        ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        reps = 10
+        for _ in range(2):
+            moe.moe_route_grouped(shape, 8, 4, dev["u"], dev["centroids"], bias, gidx, ggate, gload, ws, stream)
+        ev_r[0].record(stream)
+        for _ in range(reps):
+            moe.moe_route(shape, dev["u"], dev["centroids"], bias, idx, gate, load, ws, stream)
+        ev_r[1].record(stream)
+        for _ in range(reps):
+            moe.moe_route_grouped(shape, 8, 4, dev["u"], dev["centroids"], bias, gidx, ggate, gload, ws, stream)
+        ev_r[2].record(stream)
+        torch.cuda.synchronize()
+        route_grouped = {"n_groups": 8, "topk_groups": 4,
+                         "route_ms": round(ev_r[0].elapsed_time(ev_r[1]) / reps, 4),
+                         "route_grouped_ms": round(ev_r[1].elapsed_time(ev_r[2]) / reps, 4)}
+
     st = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(7)] for i in range(args.steps)])
     stage_names = ["route", "permute", "quantize_act", "gemm_gate_up_swiglu", "gemm_down", "combine",
                    "update_bias"]
@@ -221,6 +242,7 @@ def main():
         "combine_hbm": {"achieved_GBs": round(combine_bytes / (float(st[:, 5].mean()) * 1e-3) / 1e9, 1),
                         "frac": round(combine_bytes / (float(st[:, 5].mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "load_max_over_mean": ratios,
+        "route_grouped": route_grouped,
         "wall_s_timed": round(t_wall, 3),
         "cpu_baseline": None,
     }

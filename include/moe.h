@@ -109,6 +109,21 @@ moe_status moe_route(const moe_shape* shape, const void* u, const float* centroi
                      int32_t* expert_load, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* moe_route with a per-token group limit.  The page's cross-node all-to-all section limits
+ * every token to experts on at most 4 nodes and prints no rule for choosing them; the reading
+ * here: the N_r experts form n_groups equal contiguous groups (expert i is in group
+ * i / (N_r / n_groups)), a group's score is the highest s+b among its experts, the
+ * topk_groups groups with the highest scores (ties to the lower group index; NaN below every
+ * number) stay eligible, and the K_r experts are then picked among the eligible ones exactly as
+ * in moe_route.  Gates and expert_load as in moe_route.  n_groups == 1 or
+ * topk_groups == n_groups is moe_route.
+ * Errors: MOE_ERR_INVALID_ARG unless 1 <= topk_groups <= n_groups <= 64, N_r % n_groups == 0 and
+ * topk_groups * N_r / n_groups >= K_r (plus moe_route's checks); nothing is launched then. */
+moe_status moe_route_grouped(const moe_shape* shape, int32_t n_groups, int32_t topk_groups,
+                             const void* u, const float* centroids, const float* bias,
+                             int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Expert half of the layer (方法 §2, the h'_t equation): permutes tokens into per-expert
  * segments, runs every routed expert on its tokens and every shared expert on all tokens
  * (grouped SwiGLU GEMMs), and combines out_t = u_t + sum_s FFN_s(u_t) + sum_k gate FFN(u_t).

@@ -51,6 +51,8 @@ _P = ctypes.c_void_p
 _SIG = {
     "moe_workspace_size": [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)],
     "moe_route": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_route_grouped": [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                          ctypes.c_size_t, _P],
     "moe_forward": [ctypes.POINTER(Shape), _P, ctypes.POINTER(Weights), _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_forward_profiled": [ctypes.POINTER(Shape), _P, ctypes.POINTER(Weights), _P, _P, _P, _P, ctypes.c_size_t,
                              _P, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32],
@@ -103,11 +105,21 @@ def moe_workspace_size(shape: Shape) -> int:
     return n.value
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
 def moe_route(shape, u, centroids, bias, topk_idx, topk_gate, expert_load, workspace, stream=None):
     _check("moe_route", _lib.moe_route(ctypes.byref(shape), _ptr(u), _ptr(centroids), _ptr(bias), _ptr(topk_idx),
-                                       _ptr(topk_gate), _ptr(expert_load), _ptr(workspace),
-                                       workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                       _ptr(topk_gate), _ptr(expert_load), _ptr(workspace), _nbytes(workspace),
                                        _stream(stream)))
+
+
+def moe_route_grouped(shape, n_groups, topk_groups, u, centroids, bias, topk_idx, topk_gate, expert_load, workspace,
+                      stream=None):
+    _check("moe_route_grouped", _lib.moe_route_grouped(
+        ctypes.byref(shape), n_groups, topk_groups, _ptr(u), _ptr(centroids), _ptr(bias), _ptr(topk_idx),
+        _ptr(topk_gate), _ptr(expert_load), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def moe_forward(shape, u, weights: Weights, topk_idx, topk_gate, out, workspace, stream=None):

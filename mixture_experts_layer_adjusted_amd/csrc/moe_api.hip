@@ -197,9 +197,9 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
   return MOE_OK;
 }
 
-moe_status moe_route(const moe_shape* shape, const void* u, const float* centroids, const float* bias,
-                     int32_t* topk_idx, float* topk_gate, int32_t* expert_load, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+static moe_status route_impl(const moe_shape* shape, GroupLimit gl, const void* u, const float* centroids,
+                             const float* bias, int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!expert_load) return MOE_ERR_INVALID_ARG;
@@ -211,7 +211,26 @@ moe_status moe_route(const moe_shape* shape, const void* u, const float* centroi
   RouteWorkspace rw{reinterpret_cast<int32_t*>(wsb + p.route_partial), reinterpret_cast<uint16_t*>(wsb + p.route_e_hi),
                     reinterpret_cast<uint16_t*>(wsb + p.route_e_mid), reinterpret_cast<uint16_t*>(wsb + p.route_e_lo),
                     reinterpret_cast<float*>(wsb + p.route_scores)};
-  return hip_status(launch_route(*shape, u, centroids, bias, topk_idx, topk_gate, expert_load, rw, stream));
+  return hip_status(launch_route(*shape, u, centroids, bias, gl, topk_idx, topk_gate, expert_load, rw, stream));
+}
+
+moe_status moe_route(const moe_shape* shape, const void* u, const float* centroids, const float* bias,
+                     int32_t* topk_idx, float* topk_gate, int32_t* expert_load, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  return route_impl(shape, GroupLimit{1, 1}, u, centroids, bias, topk_idx, topk_gate, expert_load, workspace,
+                    workspace_bytes, stream);
+}
+
+moe_status moe_route_grouped(const moe_shape* shape, int32_t n_groups, int32_t topk_groups, const void* u,
+                             const float* centroids, const float* bias, int32_t* topk_idx, float* topk_gate,
+                             int32_t* expert_load, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (n_groups < 1 || n_groups > 64 || topk_groups < 1 || topk_groups > n_groups) return MOE_ERR_INVALID_ARG;
+  if (shape->n_routed % n_groups != 0) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)topk_groups * (shape->n_routed / n_groups) < shape->top_k) return MOE_ERR_INVALID_ARG;
+  return route_impl(shape, GroupLimit{n_groups, topk_groups}, u, centroids, bias, topk_idx, topk_gate, expert_load,
+                    workspace, workspace_bytes, stream);
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* u, const moe_weights* weights, const int32_t* topk_idx,

@@ -58,8 +58,16 @@ struct RouteWorkspace {
 // ---- launchers (return hipSuccess or the launch error) ----
 bool route_uses_mfma(const moe_shape& s);
 int64_t route_mfma_blocks(const moe_shape& s);
+// group-limited selection: n_groups equal contiguous expert groups, picks only from the
+// topk_groups best groups (topk_groups >= n_groups: no limit)
+struct GroupLimit {
+  int n_groups;
+  int topk_groups;
+};
+
 hipError_t launch_route(const moe_shape& s, const void* u, const float* centroids, const float* bias,
-                        int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w, hipStream_t st);
+                        GroupLimit gl, int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w,
+                        hipStream_t st);
 
 hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const WorkspacePlan& p, char* ws,
                           hipStream_t st);

@@ -72,12 +72,46 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Group limit (the per-token node limit of the page's cross-node all-to-all section, with the
+// group score it leaves open read as the group's best biased score): the N_r experts form
+// n_groups equal contiguous groups, only the topk_groups groups with the highest best s+b
+// (ties to the lower group index) stay eligible, and the K_r picks are made among their
+// experts.  Returns the lanes' "taken" bits of the ineligible candidates; gm is this
+// wavefront's 64-entry LDS scratch.  topk_groups >= n_groups disables the limit.
+template <int CPL>
+__device__ __forceinline__ uint32_t group_limit_taken(const uint64_t (&key)[CPL], int N, int n_groups,
+                                                      int topk_groups, int lane, uint32_t* gm) {
+  if (topk_groups >= n_groups) return 0u;
+  const int gs = N / n_groups;
+  if (lane < n_groups) gm[lane] = 0u;
+  // LDS operations of one wavefront take effect in program order
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int e = lane + 64 * j;
+    if (e < N) atomicMax(&gm[e / gs], (uint32_t)(key[j] >> 32));
+  }
+  const uint64_t gk = lane < n_groups ? (((uint64_t)gm[lane] << 32) | (uint32_t)(~(uint32_t)lane)) : 0ull;
+  uint64_t sel = 0ull;
+  for (int r = 0; r < topk_groups; ++r) {
+    const uint64_t w = wave_max_u64(((sel >> lane) & 1ull) ? 0ull : gk);
+    sel |= 1ull << (int)(~(uint32_t)w);
+  }
+  uint32_t taken = 0u;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int e = lane + 64 * j;
+    if (e < N && !((sel >> (e / gs)) & 1ull)) taken |= 1u << j;
+  }
+  return taken;
+}
+
 template <int CPL, typename TIn>
 __global__ void __launch_bounds__(kThreads) route_kernel(const TIn* __restrict__ u, const float* __restrict__ E,
                                                          const float* __restrict__ bias, int T, int d, int N, int K,
-                                                         int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
-                                                         int32_t* __restrict__ partial) {
+                                                         GroupLimit gl, int32_t* __restrict__ idx_out,
+                                                         float* __restrict__ gate_out, int32_t* __restrict__ partial) {
   __shared__ float Us[kSlice][kRouteTokens + 1];
+  __shared__ uint32_t gmax[kThreads / 64][64];
   __shared__ float Es[kSlice][kEsPitch];
   __shared__ float S[kRouteTokens][CPL * 64];
   __shared__ int32_t picks[kRouteTokens * kMaxTopK];
@@ -163,7 +197,7 @@ __global__ void __launch_bounds__(kThreads) route_kernel(const TIn* __restrict__
       int e = lane + 64 * j;
       key[j] = e < N ? score_key(S[tt][e] + bl[j], e) : 0ull;
     }
-    uint32_t taken = 0;
+    uint32_t taken = group_limit_taken<CPL>(key, N, gl.n_groups, gl.topk_groups, lane, gmax[wave]);
     float mys = 0.0f, sum = 0.0f;
     int myidx = -1;
     for (int k = 0; k < K; ++k) {
@@ -378,9 +412,11 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
 // top-K over precomputed affinities: one wavefront per token, kTopkTokens tokens per workgroup
 template <int CPL>
 __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict__ s_in, const float* __restrict__ bias,
-                                                        int T, int N, int K, int32_t* __restrict__ idx_out,
-                                                        float* __restrict__ gate_out, int32_t* __restrict__ partial) {
+                                                        int T, int N, int K, GroupLimit gl,
+                                                        int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+                                                        int32_t* __restrict__ partial) {
   __shared__ int32_t picks[kTopkTokens * kMaxTopK];
+  __shared__ uint32_t gmax[kThreads / 64][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kTopkTokens;
   for (int q = tid; q < kTopkTokens * kMaxTopK; q += kThreads) picks[q] = -1;
@@ -403,7 +439,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
       sv[j] = e < N ? srow[e] : 0.0f;
       key[j] = e < N ? score_key(sv[j] + bl[j], e) : 0ull;
     }
-    uint32_t taken = 0;
+    uint32_t taken = group_limit_taken<CPL>(key, N, gl.n_groups, gl.topk_groups, lane, gmax[wave]);
     float mys = 0.0f, sum = 0.0f;
     int myidx = -1;
     for (int k = 0; k < K; ++k) {
@@ -452,13 +488,13 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
 
 template <typename TIn>
 hipError_t launch_route_t(const moe_shape& s, const TIn* u, const float* centroids, const float* bias,
-                          int32_t* idx, float* gate, int32_t* load, int32_t* partial, int64_t blocks,
+                          GroupLimit gl, int32_t* idx, float* gate, int32_t* load, int32_t* partial, int64_t blocks,
                           hipStream_t st) {
   const int N = s.n_routed;
   dim3 grid((unsigned)blocks), block(kThreads);
 #define MOE_ROUTE_CASE(C)                                                                                  \
   hipLaunchKernelGGL((route_kernel<C, TIn>), grid, block, 0, st, u, centroids, bias, s.tokens, s.hidden, N, \
-                     s.top_k, idx, gate, partial)
+                     s.top_k, gl, idx, gate, partial)
   if (N <= 64) MOE_ROUTE_CASE(1);
   else if (N <= 128) MOE_ROUTE_CASE(2);
   else if (N <= 256) MOE_ROUTE_CASE(4);
@@ -471,7 +507,8 @@ hipError_t launch_route_t(const moe_shape& s, const TIn* u, const float* centroi
 }
 
 hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float* centroids, const float* bias,
-                             int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w, hipStream_t st) {
+                             GroupLimit gl, int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w,
+                             hipStream_t st) {
   const int T = s.tokens, d = s.hidden, N = s.n_routed;
   const int64_t npad = ceil_div(N, kLE) * kLE;
   hipLaunchKernelGGL(split_centroids_kernel, dim3(1024), dim3(256), 0, st, centroids, (int64_t)N * d, npad * d,
@@ -492,7 +529,7 @@ hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float*
   const int64_t blocks = ceil_div(T, kTopkTokens);
   dim3 grid((unsigned)blocks), block(kThreads);
 #define MOE_TOPK_CASE(C) \
-  hipLaunchKernelGGL((topk_kernel<C>), grid, block, 0, st, w.scores, bias, T, N, s.top_k, idx, gate, w.partial)
+  hipLaunchKernelGGL((topk_kernel<C>), grid, block, 0, st, w.scores, bias, T, N, s.top_k, gl, idx, gate, w.partial)
   if (N <= 64) MOE_TOPK_CASE(1);
   else if (N <= 128) MOE_TOPK_CASE(2);
   else if (N <= 256) MOE_TOPK_CASE(4);
@@ -512,9 +549,10 @@ bool route_uses_mfma(const moe_shape& s) {
 int64_t route_mfma_blocks(const moe_shape& s) { return ceil_div(s.tokens, kTopkTokens); }
 
 hipError_t launch_route(const moe_shape& s, const void* u, const float* centroids, const float* bias,
-                        int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w, hipStream_t st) {
+                        GroupLimit gl, int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w,
+                        hipStream_t st) {
   if (s.tokens > 0 && route_uses_mfma(s))
-    return launch_route_mfma(s, static_cast<const uint16_t*>(u), centroids, bias, idx, gate, load, w, st);
+    return launch_route_mfma(s, static_cast<const uint16_t*>(u), centroids, bias, gl, idx, gate, load, w, st);
   int32_t* partial = w.partial;
   const int64_t blocks = ceil_div(s.tokens, kRouteTokens);
   if (s.tokens == 0) {
@@ -522,8 +560,10 @@ hipError_t launch_route(const moe_shape& s, const void* u, const float* centroid
     return hipGetLastError();
   }
   if (s.dtype == MOE_DTYPE_F32)
-    return launch_route_t(s, static_cast<const float*>(u), centroids, bias, idx, gate, load, partial, blocks, st);
-  return launch_route_t(s, static_cast<const uint16_t*>(u), centroids, bias, idx, gate, load, partial, blocks, st);
+    return launch_route_t(s, static_cast<const float*>(u), centroids, bias, gl, idx, gate, load, partial, blocks,
+                          st);
+  return launch_route_t(s, static_cast<const uint16_t*>(u), centroids, bias, gl, idx, gate, load, partial, blocks,
+                        st);
 }
 
 }  // namespace moe

@@ -39,6 +39,12 @@ R8  FP8: scale = fp32(amax / 448) (E4M3FN maximum), amax = 0 -> scale 1,
     128x128 block of the stored [out, in] matrix; both GEMM inputs quantised
     (u before the gate/up projections, H before the down projection); the
     residual and gates stay unquantised.
+R13 group limit (the page's cross-node all-to-all section caps every token at 4 nodes
+    and prints no rule): the N_r experts form n_groups equal contiguous groups; a
+    group's score is the highest c = s+b among its experts (NaN below every number);
+    the topk_groups best groups (ties to the lower group index) stay eligible and
+    the K_r picks follow R2 among their experts.  Parity of this rule is pinned by
+    a hand-worked example and by invariants only.
 """
 from __future__ import annotations
 
@@ -96,6 +102,58 @@ def route(u, centroids, bias, k: int):
     c = selection_scores(s, bias)
     idx, gap = select_topk(c, k)
     return idx, gates(s, idx), expert_load(idx, np.asarray(centroids).shape[0]), s, c, gap
+
+
+_NAN_RANK = -1e300   # below every score a sigmoid plus a bias can produce, above "not eligible"
+
+
+def group_scores(c: np.ndarray, n_groups: int) -> np.ndarray:
+    """Score of each of the n_groups contiguous expert groups: its highest c (R13)."""
+    c = np.asarray(c, dtype=np.float64)
+    v = np.where(np.isnan(c), _NAN_RANK, c)
+    t, n = v.shape
+    return v.reshape(t, n_groups, n // n_groups).max(axis=2)
+
+
+def select_topk_grouped(c: np.ndarray, k: int, n_groups: int, topk_groups: int):
+    """R13: the K_r picks among the experts of the topk_groups best groups.
+
+    Returns (idx [T, K] int64, gap [T], group_gap [T]): gap is c_(K) - c_(K+1) among the
+    eligible experts (+inf when all of them are picked), group_gap is the margin of the last
+    eligible group's score over the best ineligible one (+inf when every group is eligible).
+    """
+    c = np.asarray(c)
+    t, n = c.shape
+    gs = n // n_groups
+    gsc = group_scores(c, n_groups)
+    gorder = np.argsort(-gsc, axis=1, kind="stable")
+    keep = gorder[:, :topk_groups]
+    eligible = ((np.arange(n) // gs)[None, :, None] == keep[:, None, :]).any(axis=2)
+    v = np.where(np.isnan(c), _NAN_RANK, c.astype(np.float64))
+    v = np.where(eligible, v, -np.inf)
+    order = np.argsort(-v, axis=1, kind="stable")
+    idx = order[:, :k]
+    if k < eligible.sum(axis=1).min():
+        vk = np.take_along_axis(v, order[:, k - 1:k], axis=1)[:, 0]
+        vk1 = np.take_along_axis(v, order[:, k:k + 1], axis=1)[:, 0]
+        gap = np.where(np.isfinite(vk1), vk - vk1, np.inf)
+    else:
+        gap = np.full(t, np.inf)
+    if topk_groups < n_groups:
+        g1 = np.take_along_axis(gsc, gorder[:, topk_groups - 1:topk_groups], axis=1)[:, 0]
+        g2 = np.take_along_axis(gsc, gorder[:, topk_groups:topk_groups + 1], axis=1)[:, 0]
+        group_gap = g1 - g2
+    else:
+        group_gap = np.full(t, np.inf)
+    return idx, gap, group_gap
+
+
+def route_grouped(u, centroids, bias, k: int, n_groups: int, topk_groups: int):
+    """Group-limited routing (R13): (idx, gate, load, s, c, gap, group_gap)."""
+    s = affinity(u, centroids)
+    c = selection_scores(s, bias)
+    idx, gap, group_gap = select_topk_grouped(c, k, n_groups, topk_groups)
+    return idx, gates(s, idx), expert_load(idx, np.asarray(centroids).shape[0]), s, c, gap, group_gap
 
 
 def update_bias(bias: np.ndarray, load: np.ndarray, total_assignments: int, gamma: float = 0.001) -> np.ndarray:

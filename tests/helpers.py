@@ -125,6 +125,41 @@ def check_routing(idx_gpu, gate_gpu, load_gpu, s_or, c_or, idx_or, gap_or, n_rou
     return exempt
 
 
+def check_grouped_routing(idx_gpu, gate_gpu, load_gpu, s_or, c_or, n_groups, topk_groups, n_routed):
+    """Group-limited routing (R13) against the oracle; returns the mask of exempt tokens.
+
+    Tokens whose oracle expert margin or group margin is below GAP_EXEMPT are exempt from the
+    exact-set check; their picks must still come from at most topk_groups groups whose scores
+    are within GAP_EXEMPT of the last eligible group's, be legal among those groups' experts,
+    and be ordered by score.
+    """
+    T, K = idx_gpu.shape
+    idx_or, gap, ggap = O.select_topk_grouped(c_or, K, n_groups, topk_groups)
+    assert np.array_equal(load_gpu, np.bincount(idx_gpu.ravel(), minlength=n_routed))
+    assert np.all((idx_gpu >= 0) & (idx_gpu < n_routed))
+    assert all(len(set(r)) == K for r in idx_gpu.tolist())
+    gs = n_routed // n_groups
+    assert all(len(set((r // gs).tolist())) <= topk_groups for r in idx_gpu)
+    exempt = (gap < GAP_EXEMPT) | (ggap < GAP_EXEMPT)
+    same = np.sort(idx_gpu, 1) == np.sort(idx_or, 1)
+    bad = ~same.all(1) & ~exempt
+    assert not bad.any(), f"{bad.sum()} non-exempt tokens differ, e.g. {np.nonzero(bad)[0][:5]}"
+    c64 = c_or.astype(np.float64)
+    gsc = O.group_scores(c_or, n_groups)
+    g_last = np.sort(gsc, 1)[:, ::-1][:, topk_groups - 1]
+    for t in np.nonzero(exempt)[0]:
+        groups = sorted(set((idx_gpu[t] // gs).tolist()))
+        assert all(gsc[t, q] >= g_last[t] - GAP_EXEMPT for q in groups)
+        allowed = [q for q in range(n_groups) if gsc[t, q] >= g_last[t] - GAP_EXEMPT]
+        elig = np.concatenate([c64[t, q * gs:(q + 1) * gs] for q in allowed])
+        ck = np.sort(elig)[::-1][K - 1]
+        assert np.all(c64[t, idx_gpu[t]] >= ck - GAP_EXEMPT), "an exempt token picked an illegal expert"
+    cg = np.take_along_axis(c64, idx_gpu, 1)
+    assert np.all(cg[:, :-1] >= cg[:, 1:] - GAP_EXEMPT), "picks not ordered by score"
+    np.testing.assert_allclose(gate_gpu, O.gates(s_or, idx_gpu.astype(np.int64)), rtol=0, atol=1e-5)
+    return exempt
+
+
 def rel_err(y_gpu, y_ref, u=None):
     """max_t ||y_gpu - y_ref||_inf / ||y_ref||_inf (and the same on y - u when u is given)."""
     y_gpu = np.asarray(y_gpu, np.float64)

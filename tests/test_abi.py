@@ -83,6 +83,11 @@ def test_null_and_workspace_errors_before_launch():
     rc = lib.moe_forward(ctypes.byref(s), fake, ctypes.byref(w2), fake, fake, ctypes.c_void_p(0x2000), fake,
                          1 << 40, None)
     assert rc == 1
+    # group limits that cannot be met -> invalid argument, nothing launched
+    big = ctypes.c_size_t(1 << 40)
+    for ng, mg in ((0, 1), (4, 5), (4, 0), (3, 1), (65, 1), (16, 1)):
+        rc = lib.moe_route_grouped(ctypes.byref(s), ng, mg, fake, fake, fake, fake, fake, fake, fake, big, None)
+        assert rc == 1, (ng, mg)
     assert lib.moe_update_bias(0, 10, fake, fake, ctypes.c_float(0.001), None) == 1
     assert lib.moe_quantize_weights(1, 100, 128, fake, fake, fake, None) == 2
     assert lib.moe_quantize_act(4, 130, fake, fake, fake, None) == 2

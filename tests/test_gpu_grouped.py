@@ -1,0 +1,86 @@
+"""GPU parity of the group-limited router (moe_route_grouped) against the oracle's reading R13.
+
+The page ("DeepSeek-V3 技術報告", xyznot.com/zh-tw/paper/2412.19437, cross-node all-to-all
+section) limits each token to experts on 4 nodes without printing the rule; the oracle's rule
+is pinned by the CPU tests of test_oracle_grouped.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_adjusted_amd as moe
+from oracle import moe_oracle as O
+from synth import bf16_bits_to_f32, host
+from synth.configs import CONFIGS
+from synth.device import host_to_device
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from helpers import Runner, TOL, check_grouped_routing, rel_err, shape_of, to_host_f32
+
+
+def _f(a):
+    return bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, np.float32)
+
+
+def _route_grouped(cfg, ng, mg):
+    h = host.make_host_inputs(cfg, with_weights=False)
+    dev = host_to_device(h)
+    shape = shape_of(cfg)
+    ws = torch.empty(max(moe.moe_workspace_size(shape), 1), dtype=torch.uint8, device="cuda")
+    T, K, N = cfg.tokens, cfg.top_k, cfg.n_routed
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    load = torch.empty((N,), dtype=torch.int32, device="cuda")
+    moe.moe_route_grouped(shape, ng, mg, dev["u"], dev["centroids"], dev["bias"], idx, gate, load, ws)
+    torch.cuda.synchronize()
+    hf = {k: _f(v) for k, v in h.items()}
+    s = O.affinity(hf["u"], hf["centroids"])
+    c = O.selection_scores(s, hf["bias"])
+    return idx.cpu().numpy(), gate.cpu().numpy(), load.cpu().numpy(), s, c, dev, shape, ws
+
+
+@pytest.mark.parametrize("cid,ng,mg", [(0, 4, 2), (1, 8, 3), (1, 4, 1), (2, 8, 4)])
+def test_grouped_routing_parity(cid, ng, mg):
+    cfg = CONFIGS[cid]
+    print(f"grouped routing: config {cid}, {ng} groups, {mg} eligible", flush=True)
+    idx, gate, load, s, c, *_ = _route_grouped(cfg, ng, mg)
+    exempt = check_grouped_routing(idx, gate, load, s, c, ng, mg, cfg.n_routed)
+    ungrouped, _ = O.select_topk(c, cfg.top_k)
+    changed = (np.sort(ungrouped, 1) != np.sort(idx, 1)).any(1).mean()
+    print(f"exempt {exempt.sum()}, tokens whose picks the limit changed: {changed:.3f}")
+    assert changed > 0   # the limit binds at these settings
+
+
+def test_grouped_with_every_group_eligible_is_moe_route():
+    cfg = CONFIGS[1]
+    idx, gate, load, s, c, dev, shape, ws = _route_grouped(cfg, 8, 8)
+    T, K, N = cfg.tokens, cfg.top_k, cfg.n_routed
+    idx2 = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate2 = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    load2 = torch.empty((N,), dtype=torch.int32, device="cuda")
+    moe.moe_route(shape, dev["u"], dev["centroids"], dev["bias"], idx2, gate2, load2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx, idx2.cpu().numpy())
+    assert np.array_equal(gate.view(np.uint32), gate2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(load, load2.cpu().numpy())
+
+
+def test_grouped_routing_feeds_the_forward():
+    cfg = CONFIGS[1]
+    h = host.make_host_inputs(cfg)
+    hf = {k: _f(v) for k, v in h.items()}
+    dev = host_to_device(h)
+    r = Runner(cfg, dev)
+    moe.moe_route_grouped(r.shape, 8, 3, dev["u"], dev["centroids"], dev["bias"], r.idx, r.gate, r.load, r.ws)
+    r.forward()
+    torch.cuda.synchronize()
+    idx = r.idx.cpu().numpy().astype(np.int64)
+    s = O.affinity(hf["u"], hf["centroids"])
+    shared = list(zip(hf["sh_gate"], hf["sh_up"], hf["sh_down"]))
+    y_ref = O.layer_forward(hf["u"], idx, O.gates(s, idx), O.stacked(hf["w_gate"], hf["w_up"], hf["w_down"]), shared)
+    e_all, e_exp = rel_err(to_host_f32(r.out), y_ref, hf["u"])
+    assert e_all <= TOL["bf16"] and e_exp <= TOL["bf16"], (e_all, e_exp)
