@@ -45,6 +45,10 @@ R13 group limit (the page's cross-node all-to-all section caps every token at 4 
     the topk_groups best groups (ties to the lower group index) stay eligible and
     the K_r picks follow R2 among their experts.  Parity of this rule is pinned by
     a hand-worked example and by invariants only.
+R14 backward: gradients of L = <dout, h'> with the selection (idx) held fixed, as the Topk
+    is piecewise constant; the bias gets no gradient (it never enters a gate); the
+    gate path is differentiated through the unbiased s of the gate equation with s
+    evaluated in float64 (no fp32 rounding, so that finite differences can pin it).
 """
 from __future__ import annotations
 
@@ -205,6 +209,77 @@ def layer_forward(u, idx, gate, routed, shared, ffn=swiglu_ffn, x=None) -> np.nd
         wg, wu, wd = routed(int(e))
         out[rows] += gate[rows, slots][:, None] * ffn(x[rows], wg, wu, wd)
     return out
+
+
+def affinity64(u, centroids) -> np.ndarray:
+    """s = Sigmoid(u^T e) in float64 throughout (the smooth form the backward differentiates)."""
+    z = np.asarray(u, dtype=np.float64) @ np.asarray(centroids, dtype=np.float64).T
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy):
+    """Gradients of y = (SiLU(x Wg^T) * (x Wu^T)) Wd^T given dL/dy: (dx, dWg, dWu, dWd), float64.
+
+    With a = x Wg^T, b = x Wu^T, h = SiLU(a) * b and SiLU'(a) = sigma(a) (1 + a (1 - sigma(a))):
+    dh = dy Wd, dWd = dy^T h, da = dh * b * SiLU'(a), db = dh * SiLU(a),
+    dx = da Wg + db Wu, dWg = da^T x, dWu = db^T x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    wg, wu, wd = (np.asarray(w, dtype=np.float64) for w in (w_gate, w_up, w_down))
+    dy = np.asarray(dy, dtype=np.float64)
+    a = x @ wg.T
+    b = x @ wu.T
+    sg = 1.0 / (1.0 + np.exp(-a))
+    h = a * sg * b
+    dh = dy @ wd
+    da = dh * b * sg * (1.0 + a * (1.0 - sg))
+    db = dh * a * sg
+    return da @ wg + db @ wu, da.T @ x, db.T @ x, dy.T @ h
+
+
+def layer_backward(u, centroids, idx, routed, shared, dout):
+    """Backward of the layer (R14): gradients of <dout, h'> for a fixed selection idx.
+
+    routed: e -> (w_gate, w_up, w_down); shared: sequence of (w_gate, w_up, w_down).
+    Returns (du [T, d], d_centroids [N_r, d], d_routed {e: (dWg, dWu, dWd)} for the experts
+    that appear in idx, d_shared [(dWg, dWu, dWd)] per shared expert), all float64.
+
+    With g_k = s_k / S (S = sum of the selected s) and dg_k = <dout_t, FFN_k(u_t)>:
+    ds_j = dg_j / S - (sum_k dg_k s_k) / S^2 for selected j (0 elsewhere),
+    dz = ds * s (1 - s), du_t += sum_k dz_k e_k, de_k += dz_k u_t.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    e = np.asarray(centroids, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    idx = np.asarray(idx)
+    t_n, k_n = idx.shape
+    s = affinity64(u, e)
+    ssel = np.take_along_axis(s, idx, axis=1)
+    ssum = ssel.sum(axis=1, keepdims=True)
+    gate = ssel / ssum
+    du = dout.copy()
+    d_shared = []
+    for wg, wu, wd in shared:
+        dx, dwg, dwu, dwd = swiglu_ffn_backward(u, wg, wu, wd, dout)
+        du += dx
+        d_shared.append((dwg, dwu, dwd))
+    dg = np.zeros((t_n, k_n))
+    d_routed = {}
+    for ex in np.unique(idx):
+        rows, slots = np.nonzero(idx == ex)
+        wg, wu, wd = routed(int(ex))
+        y = swiglu_ffn(u[rows], wg, wu, wd)
+        dg[rows, slots] = np.sum(dout[rows] * y, axis=1)
+        dx, dwg, dwu, dwd = swiglu_ffn_backward(u[rows], wg, wu, wd, gate[rows, slots][:, None] * dout[rows])
+        du[rows] += dx
+        d_routed[int(ex)] = (dwg, dwu, dwd)
+    ds = dg / ssum - np.sum(dg * ssel, axis=1, keepdims=True) / ssum ** 2
+    dz = ds * ssel * (1.0 - ssel)
+    de = np.zeros_like(e)
+    for k in range(k_n):
+        du += dz[:, k:k + 1] * e[idx[:, k]]
+        np.add.at(de, idx[:, k], dz[:, k:k + 1] * u)
+    return du, de, d_routed, d_shared
 
 
 def stacked(w_gate, w_up, w_down):
