@@ -146,6 +146,39 @@ moe_status moe_forward_profiled(const moe_shape* shape, const void* u, const moe
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* events, int32_t n_events);
 
+/* Weight gradients written by moe_backward: bf16, same layouts as the weights
+ * (gate/up [N, I, d], down [N, d, I], N = N_r or N_s).  Owned by the caller. */
+typedef struct {
+  void* w_gate;
+  void* w_up;
+  void* w_down;
+  void* sh_gate;
+  void* sh_up;
+  void* sh_down;
+} moe_weight_grads;
+
+/* Bytes of device workspace moe_backward needs for `shape` (BF16 only; d and I multiples of
+ * 128).  MOE_ERR_UNSUPPORTED for other shapes. */
+moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Layer backward (方法 §2, the h'_t, s_{i,t} and g'_{i,t} equations): gradients of
+ * L = <dout, h'> with the routing (topk_idx) held fixed — the Topk is piecewise constant — and
+ * none for the bias, which never enters a gate.  With g_k = s_k / S (S = sum of the selected
+ * s) the gate gradient flows through the unbiased s into u and the centroids.
+ *   u, centroids, weights, topk_idx, topk_gate   as given to moe_route / moe_forward (BF16)
+ *   dout        [T, d]   bf16 dL/dh'
+ *   du          [T, d]   bf16 out: dL/du (residual + every expert's input gradient + router term)
+ *   d_centroids [N_r, d] fp32 out (rows of experts no token picked are zero)
+ *   dw          bf16 out, every routed and shared expert's gate/up/down gradient (zero for
+ *               experts no token picked)
+ * Errors: MOE_ERR_UNSUPPORTED unless dtype == BF16, d % 128 == 0, I % 128 == 0;
+ * MOE_ERR_INVALID_ARG for a null pointer or du aliasing u or dout; MOE_ERR_WORKSPACE if
+ * workspace_bytes < moe_backward_workspace_size.  Nothing is launched on an error. */
+moe_status moe_backward(const moe_shape* shape, const void* u, const float* centroids,
+                        const moe_weights* weights, const int32_t* topk_idx, const float* topk_gate,
+                        const void* dout, void* du, float* d_centroids, const moe_weight_grads* dw,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Auxiliary-loss-free bias update (方法 §2, last paragraph), in place on bias[N_r] (fp32):
  * expert i is overloaded when load_i * N_r > total_assignments (= T * K_r, i.e. above the
  * step mean), underloaded when below; b_i <- b_i - gamma resp. b_i + gamma as one fp32 add;

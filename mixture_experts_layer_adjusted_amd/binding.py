@@ -43,6 +43,10 @@ class Weights(ctypes.Structure):
         "w_gate_scale", "w_up_scale", "w_down_scale", "sh_gate_scale", "sh_up_scale", "sh_down_scale")]
 
 
+class WeightGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
 _lib = ctypes.CDLL(LIB_PATH)
@@ -59,6 +63,9 @@ _SIG = {
     "moe_update_bias": [ctypes.c_int32, ctypes.c_int64, _P, _P, ctypes.c_float, _P],
     "moe_quantize_weights": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
     "moe_quantize_act": [ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
+    "moe_backward_workspace_size": [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)],
+    "moe_backward": [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(Weights), _P, _P, _P, _P, _P,
+                     ctypes.POINTER(WeightGrads), _P, ctypes.c_size_t, _P],
     "moe_status_string": [ctypes.c_int32],
 }
 for _name, _args in _SIG.items():
@@ -97,6 +104,25 @@ def make_weights(w_gate, w_up, w_down, sh_gate=None, sh_up=None, sh_down=None, s
     for k, t in (scales or {}).items():
         setattr(w, k, t.data_ptr() if t is not None else None)
     return w
+
+
+def make_weight_grads(w_gate, w_up, w_down, sh_gate=None, sh_up=None, sh_down=None) -> WeightGrads:
+    return WeightGrads(*(_ptr(t).value if t is not None else None
+                         for t in (w_gate, w_up, w_down, sh_gate, sh_up, sh_down)))
+
+
+def moe_backward_workspace_size(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size", _lib.moe_backward_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def moe_backward(shape, u, centroids, weights, topk_idx, topk_gate, dout, du, d_centroids, weight_grads, workspace,
+                 stream=None):
+    _check("moe_backward", _lib.moe_backward(
+        ctypes.byref(shape), _ptr(u), _ptr(centroids), ctypes.byref(weights), _ptr(topk_idx), _ptr(topk_gate),
+        _ptr(dout), _ptr(du), _ptr(d_centroids), ctypes.byref(weight_grads), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
 
 
 def moe_workspace_size(shape: Shape) -> int:

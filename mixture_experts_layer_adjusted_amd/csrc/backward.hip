@@ -1,0 +1,224 @@
+// Layer backward: the non-GEMM kernels.
+//
+// Gradients of L = <dout, h'> for the h'_t equation of 方法 §2 ("DeepSeek-V3 技術報告",
+// xyznot.com/zh-tw/paper/2412.19437) with the selection held fixed (the Topk is piecewise
+// constant; the bias never enters a gate, so it gets no gradient).  With g_k = s_k / S over the
+// selected experts (S = their sum of s) and dg_k = <dout_t, FFN_k(u_t)>:
+//   ds_k = dg_k / S - (sum_j dg_j s_j) / S^2,   dz_k = ds_k s_k (1 - s_k),
+//   du_t = dout_t + sum over the token's rows of dX + sum_k dz_k e_{idx_k},
+//   de_i = sum over the (token, slot) pairs that picked i of dz u_t.
+//
+//  row_gate:   the gate of every permuted row (its (token, slot) gate; 1 for shared-expert rows;
+//              0 for padding rows), which scales dY = g dout in the backward GEMMs;
+//  router_bwd: one workgroup per token: the K_r logits z = u_t . e_k are recomputed in fp32
+//              (blocked partial sums in a fixed order), dg_k is the fixed-order sum of the
+//              per-tile partials the gate/up backward GEMM wrote, then dz, and du_t summed in a
+//              fixed order (residual, routed rows, shared rows, centroid terms);
+//  dcentroid:  de_i by a fixed-order loop over the rows of segment i.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRouterThreads = 128;
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  uint32_t b = __float_as_uint(v);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+// one thread per (token, slot) pair, then per (token, shared expert)
+__global__ void row_gate_kernel(const int32_t* __restrict__ perm_row, const float* __restrict__ gate,
+                                const int32_t* __restrict__ seg_off, int T, int K, int N, int Ns,
+                                float* __restrict__ row_gate) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t routed = (int64_t)T * K;
+  if (i < routed) {
+    const int r = perm_row[i];
+    if (r >= 0) row_gate[r] = gate[i];
+  } else if (i < routed + (int64_t)T * Ns) {
+    const int64_t j = i - routed;
+    const int s = (int)(j / T), t = (int)(j % T);
+    row_gate[seg_off[N + s] + t] = 1.0f;
+  }
+}
+
+__global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(
+    const uint16_t* __restrict__ u, const float* __restrict__ E, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm_row, const float* __restrict__ dg_part, int NT,
+    const int32_t* __restrict__ seg_off, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ dX, int d,
+    int N, int K, int Ns, uint16_t* __restrict__ du, float* __restrict__ row_dz) {
+  __shared__ float red[kMaxTopK][kRouterThreads];
+  __shared__ float s_k[kMaxTopK], dg_k[kMaxTopK], dz_k[kMaxTopK];
+  __shared__ int32_t e_k[kMaxTopK], row_k[kMaxTopK];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < K) {
+    const int e = idx[t * K + tid];
+    const int r = perm_row[t * K + tid];
+    const bool ok = e >= 0 && e < N && r >= 0;
+    e_k[tid] = ok ? e : -1;
+    row_k[tid] = ok ? r : -1;
+  }
+  __syncthreads();
+  // logits of the selected experts: per-thread partial sums over 8-element slices, then a
+  // fixed-order sum over the threads
+  const uint16_t* urow = u + t * d;
+  for (int k = 0; k < K; ++k) {
+    float acc = 0.0f;
+    const int e = e_k[k];
+    if (e >= 0) {
+      const float* erow = E + (int64_t)e * d;
+      for (int j = tid * 8; j < d; j += kRouterThreads * 8) {
+        float uv[8];
+        load8(urow + j, uv);
+        const float4 e0 = *reinterpret_cast<const float4*>(erow + j);
+        const float4 e1 = *reinterpret_cast<const float4*>(erow + j + 4);
+        float part = 0.0f;
+        part = fmaf(uv[0], e0.x, part);
+        part = fmaf(uv[1], e0.y, part);
+        part = fmaf(uv[2], e0.z, part);
+        part = fmaf(uv[3], e0.w, part);
+        part = fmaf(uv[4], e1.x, part);
+        part = fmaf(uv[5], e1.y, part);
+        part = fmaf(uv[6], e1.z, part);
+        part = fmaf(uv[7], e1.w, part);
+        acc += part;
+      }
+    }
+    red[k][tid] = acc;
+  }
+  __syncthreads();
+  if (tid < K) {
+    float z = 0.0f;
+    for (int i = 0; i < kRouterThreads; ++i) z += red[tid][i];
+    float dg = 0.0f;
+    const int r = row_k[tid];
+    if (r >= 0)
+      for (int q = 0; q < NT; ++q) dg += dg_part[(int64_t)r * NT + q];
+    s_k[tid] = r >= 0 ? 1.0f / (1.0f + expf(-z)) : 0.0f;
+    dg_k[tid] = dg;
+  }
+  __syncthreads();
+  if (tid < K) {
+    float S = 0.0f, D = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      S += s_k[k];
+      D += dg_k[k] * s_k[k];
+    }
+    const float s = s_k[tid];
+    const float ds = dg_k[tid] / S - D / (S * S);
+    const float dz = row_k[tid] >= 0 ? ds * s * (1.0f - s) : 0.0f;
+    dz_k[tid] = dz;
+    if (row_k[tid] >= 0) row_dz[row_k[tid]] = dz;
+  }
+  __syncthreads();
+  for (int j = tid * 8; j < d; j += kRouterThreads * 8) {
+    float acc[8], v[8];
+    load8(dout + t * d + j, acc);
+    for (int k = 0; k < K; ++k) {
+      if (row_k[k] < 0) continue;
+      load8(dX + (int64_t)row_k[k] * d + j, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    for (int s = 0; s < Ns; ++s) {
+      load8(dX + ((int64_t)seg_off[N + s] + t) * d + j, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    for (int k = 0; k < K; ++k) {
+      if (e_k[k] < 0) continue;
+      const float* erow = E + (int64_t)e_k[k] * d + j;
+      const float4 e0 = *reinterpret_cast<const float4*>(erow);
+      const float4 e1 = *reinterpret_cast<const float4*>(erow + 4);
+      const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(dz_k[k], ev[i], acc[i]);
+    }
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(du + t * d + j) = o;
+  }
+}
+
+// de[i, j] = sum over the real rows r of segment i of row_dz[r] * u[row_token[r], j]
+__global__ void __launch_bounds__(256) dcentroid_kernel(const uint16_t* __restrict__ u,
+                                                        const int32_t* __restrict__ row_token,
+                                                        const float* __restrict__ row_dz,
+                                                        const int32_t* __restrict__ seg_off,
+                                                        const int32_t* __restrict__ seg_rows, int d,
+                                                        float* __restrict__ de) {
+  const int i = blockIdx.x;
+  const int j = blockIdx.y * 256 + threadIdx.x;
+  if (j >= d) return;
+  const int r0 = seg_off[i], r1 = r0 + seg_rows[i];
+  float acc = 0.0f;
+  int r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    float v[4], w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = __uint_as_float((uint32_t)u[(int64_t)row_token[r + q] * d + j] << 16);
+      w[q] = row_dz[r + q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = fmaf(w[q], v[q], acc);
+  }
+  for (; r < r1; ++r) acc = fmaf(row_dz[r], __uint_as_float((uint32_t)u[(int64_t)row_token[r] * d + j] << 16), acc);
+  de[(int64_t)i * d + j] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const float* gate, const int32_t* seg_off,
+                           int64_t max_rows, float* row_gate, float* row_dz, hipStream_t st) {
+  const int64_t fill_blocks = std::min<int64_t>(ceil_div(max_rows, 256), 4096);
+  if (fill_blocks > 0) {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, st, row_gate, max_rows);
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)fill_blocks), dim3(256), 0, st, row_dz, max_rows);
+  }
+  const int64_t n = (int64_t)s.tokens * (s.top_k + s.n_shared);
+  if (n > 0)
+    hipLaunchKernelGGL(row_gate_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, perm_row, gate, seg_off,
+                       s.tokens, s.top_k, s.n_routed, s.n_shared, row_gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* centroids, const int32_t* idx,
+                             const int32_t* perm_row, const float* dg_part, const int32_t* seg_off, const void* dout,
+                             const void* dX, void* du, float* row_dz, hipStream_t st) {
+  if (s.tokens == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)s.tokens), dim3(kRouterThreads), 0, st,
+                     static_cast<const uint16_t*>(u), centroids, idx, perm_row, dg_part, s.inter / 128, seg_off,
+                     static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(dX), s.hidden, s.n_routed,
+                     s.top_k, s.n_shared, static_cast<uint16_t*>(du), row_dz);
+  return hipGetLastError();
+}
+
+hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* row_token, const float* row_dz,
+                            const int32_t* seg_off, const int32_t* seg_rows, float* de, hipStream_t st) {
+  hipLaunchKernelGGL(dcentroid_kernel, dim3((unsigned)s.n_routed, (unsigned)ceil_div(s.hidden, 256)), dim3(256), 0,
+                     st, static_cast<const uint16_t*>(u), row_token, row_dz, seg_off, seg_rows, s.hidden, de);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -295,8 +295,65 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   wait_vmcnt<0>();
 }
 
-template <bool SWIGLU, int BK, int WAVES, int WROWS, int WGS, int WM, int TM>
+// SwiGLU backward epilogue: acc[mb][0] holds the gate pre-activations a and acc[mb][1] the up
+// values b of rows r0 + 32 mb + l32, features fbase + 8 q + 4 khalf + (0..3).  With
+// sg = sigmoid(a), h = a sg b and dh = row_gate * dh_in (the gate of the row's (token, slot)):
+// dA = dh b sg (1 + a (1 - sg)) and dB = dh a sg go to out = [dA dB], h to out2, and the
+// row's sum of dh_in * h over the workgroup's 128 features (its share of <dY, FFN(x)>, the
+// gate gradient) to dg_part[row, nt], reduced across the wavefronts sharing the row.
+template <int MB>
+__device__ __forceinline__ void store_swiglu_bwd(const f32x16 (&acc)[MB][2], const GemmOperands& g, int64_t m0,
+                                                 int mrow0, int fbase, int nt, int wn, int tile_rows, bool active,
+                                                 int l32, int khalf, float (*red)[4]) {
+  const int N = g.N;
+  const uint16_t* dhp = static_cast<const uint16_t*>(g.dh);
+  uint16_t* dab = static_cast<uint16_t*>(g.out);
+  uint16_t* hout = static_cast<uint16_t*>(g.out2);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rl = mrow0 + mb * 32 + l32;
+    const int64_t r = m0 + rl;
+    float part = 0.0f;
+    if (active) {
+      const float rg = g.row_gate[r];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = fbase + q * 8 + khalf * 4;
+        const uint2 dq = *reinterpret_cast<const uint2*>(dhp + r * N + f);
+        const float dhu[4] = {__uint_as_float(dq.x << 16), __uint_as_float(dq.x & 0xFFFF0000u),
+                              __uint_as_float(dq.y << 16), __uint_as_float(dq.y & 0xFFFF0000u)};
+        uint16_t da[4], db[4], hh[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = acc[mb][0][q * 4 + v], b = acc[mb][1][q * 4 + v];
+          const float sg = 1.0f / (1.0f + __expf(-a));
+          const float h = a * sg * b;
+          const float dh = rg * dhu[v];
+          da[v] = f32_to_bf16(dh * b * sg * (1.0f + a * (1.0f - sg)));
+          db[v] = f32_to_bf16(dh * a * sg);
+          hh[v] = f32_to_bf16(h);
+          part += dhu[v] * h;
+        }
+        *reinterpret_cast<uint2*>(dab + r * 2 * N + f) =
+            make_uint2((uint32_t)da[0] | ((uint32_t)da[1] << 16), (uint32_t)da[2] | ((uint32_t)da[3] << 16));
+        *reinterpret_cast<uint2*>(dab + r * 2 * N + N + f) =
+            make_uint2((uint32_t)db[0] | ((uint32_t)db[1] << 16), (uint32_t)db[2] | ((uint32_t)db[3] << 16));
+        *reinterpret_cast<uint2*>(hout + r * N + f) =
+            make_uint2((uint32_t)hh[0] | ((uint32_t)hh[1] << 16), (uint32_t)hh[2] | ((uint32_t)hh[3] << 16));
+      }
+    }
+    part += __shfl_xor(part, 32, 64);
+    if (khalf == 0) red[rl][wn] = part;
+  }
+  __syncthreads();
+  for (int row = threadIdx.x; row < tile_rows; row += blockDim.x)
+    g.dg_part[(m0 + row) * (N / 128) + nt] = red[row][0] + red[row][1] + red[row][2] + red[row][3];
+}
+
+// EPI: 0 plain store (down GEMM), 1 SwiGLU (gate/up GEMM), 2 SwiGLU backward (gate/up recomputed)
+template <int EPI, int BK, int WAVES, int WROWS, int WGS, int WM, int TM>
 __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kernel(GemmOperands g, int NT) {
+  constexpr bool SWIGLU = EPI != 0;
   using C = StreamCfg<BK, WAVES, WROWS, WGS, TM>;
   constexpr int WN = WAVES / WM;           // wavefront grid WM x WN
   constexpr int RW = TM / WM;              // rows per wavefront
@@ -447,13 +504,19 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
       issue_stage(kt + kAhead);
     }
   }
-  if (active)
+  if constexpr (EPI == 2) {
+    static_assert(NBW == 2 && WN == 4, "one gate and one up block per wavefront, four wavefronts per row");
+    __shared__ float red[TM][4];
+    store_swiglu_bwd<MB>(acc, g, m0, mrow0, n0 + wn * (WRW / 2), nt, wn, tile_rows, active, l32, khalf, red);
+  } else if (active) {
     store_tile<SWIGLU, MB, NBW>(acc, static_cast<uint16_t*>(g.out), m0 + mrow0,
                                 n0 + wn * (SWIGLU ? WRW / 2 : WRW), N, l32, khalf);
+  }
 }
 
-template <bool SWIGLU>
+template <int EPI>
 hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
+  constexpr bool SWIGLU = EPI != 0;
   constexpr int SBK = MOE_STREAM_BK, SW = MOE_STREAM_WAVES, SR = MOE_STREAM_WROWS, SG = MOE_STREAM_WGS;
   constexpr int SM = MOE_STREAM_WM, STM = MOE_STREAM_TM;
   using SC = StreamCfg<SBK, SW, SR, SG, STM>;
@@ -462,7 +525,7 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
   if (g.K % SBK == 0 && offsets_fit) {
     const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
     const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
-    auto kern = &grouped_gemm_bf16_stream_kernel<SWIGLU, SBK, SW, SR, SG, SM, STM>;
+    auto kern = &grouped_gemm_bf16_stream_kernel<EPI, SBK, SW, SR, SG, SM, STM>;
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -476,6 +539,7 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SC::kThreads), lds_bytes, st, g, NT);
     return hipGetLastError();
   }
+  if (EPI == 2) return hipErrorInvalidValue;   // the backward epilogue exists in the streaming kernel only
   const size_t lds_bytes = 2 * kStageElems * sizeof(uint16_t);
   static bool attr_set = false;
   if (!attr_set) {
@@ -491,7 +555,8 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st) { return launch_bf16<true>(g, st); }
-hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st) { return launch_bf16<false>(g, st); }
+hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st) { return launch_bf16<1>(g, st); }
+hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st) { return launch_bf16<0>(g, st); }
+hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_bf16<2>(g, st); }
 
 }  // namespace moe

@@ -12,6 +12,7 @@ hipError_t launch_gemm_f32_swiglu(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_f32_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st);
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st) {
   if (dtype == MOE_DTYPE_F32) return launch_gemm_f32_swiglu(g, st);
@@ -68,6 +69,12 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.u_scale = take(fp8 ? (size_t)T * (d / 128) * 4 : 0);
   p.forward_bytes = o;
   p.total = p.route_bytes > p.forward_bytes ? p.route_bytes : p.forward_bytes;
+  p.bwd_h = take((size_t)p.max_rows * I * 2);
+  p.bwd_dab = take((size_t)p.max_rows * 2 * I * 2);
+  p.bwd_row_gate = take((size_t)p.max_rows * 4);
+  p.bwd_row_dz = take((size_t)p.max_rows * 4);
+  p.bwd_dg_part = take((size_t)p.max_rows * (I / 128 > 0 ? I / 128 : 1) * 4);
+  p.backward_total = o;
   return p;
 }
 
@@ -245,6 +252,174 @@ moe_status moe_forward_profiled(const moe_shape* shape, const void* u, const moe
   if (!events) return MOE_ERR_INVALID_ARG;
   return forward_impl(shape, u, weights, topk_idx, topk_gate, out, workspace, workspace_bytes, stream, events,
                       n_events);
+}
+
+static moe_status check_backward_shape(const moe_shape* s) {
+  moe_status rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (s->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden % 128 != 0 || s->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  // the streaming and backward GEMMs address their operands with 32-bit byte offsets
+  const int64_t max_rows =
+      ((int64_t)s->tokens * s->top_k + (int64_t)s->n_routed * (kTileM - 1)) / kTileM * kTileM +
+      (int64_t)s->n_shared * ceil_div(s->tokens, kTileM) * kTileM;
+  if (max_rows * 2 * s->inter * 2 >= (int64_t(1) << 32) || (int64_t)s->tokens * s->hidden * 2 >= (int64_t(1) << 32))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes) {
+  moe_status rc = check_backward_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = plan_workspace(*shape).backward_total;
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_shape* shape, const void* u, const float* centroids, const moe_weights* w,
+                        const int32_t* topk_idx, const float* topk_gate, const void* dout, void* du,
+                        float* d_centroids, const moe_weight_grads* dw, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  moe_status rc = check_backward_shape(shape);
+  if (rc != MOE_OK) return rc;
+  const moe_shape& s = *shape;
+  if (!u || !centroids || !w || !dout || !du || !d_centroids || !dw || !workspace) return MOE_ERR_INVALID_ARG;
+  if (s.tokens > 0 && (!topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || !w->w_up || !w->w_down || !dw->w_gate || !dw->w_up || !dw->w_down) return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down || !dw->sh_gate || !dw->sh_up || !dw->sh_down))
+    return MOE_ERR_INVALID_ARG;
+  if (du == u || du == dout) return MOE_ERR_INVALID_ARG;
+  const WorkspacePlan p = plan_workspace(s);
+  if (workspace_bytes < p.backward_total) return MOE_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(workspace);
+  const int64_t T = s.tokens, d = s.hidden, I = s.inter;
+  const int32_t* row_token = reinterpret_cast<const int32_t*>(wsb + p.row_token);
+  const int32_t* perm_row = reinterpret_cast<const int32_t*>(wsb + p.perm_row);
+  const int32_t* seg_off = reinterpret_cast<const int32_t*>(wsb + p.seg_off);
+  const int32_t* seg_rows = reinterpret_cast<const int32_t*>(wsb + p.seg_rows);
+  float* row_gate = reinterpret_cast<float*>(wsb + p.bwd_row_gate);
+  float* row_dz = reinterpret_cast<float*>(wsb + p.bwd_row_dz);
+  float* dg_part = reinterpret_cast<float*>(wsb + p.bwd_dg_part);
+  uint16_t* dhu = reinterpret_cast<uint16_t*>(wsb + p.h);          // dL/dH before the gate
+  uint16_t* dx = reinterpret_cast<uint16_t*>(wsb + p.y);           // dL/dX of every permuted row
+  uint16_t* hb = reinterpret_cast<uint16_t*>(wsb + p.bwd_h);
+  uint16_t* dab = reinterpret_cast<uint16_t*>(wsb + p.bwd_dab);
+  auto bf = [](const void* q) { return static_cast<const uint16_t*>(q); };
+
+  if (T > 0) {
+    if ((rc = hip_status(launch_permute(s, topk_idx, p, wsb, stream))) != MOE_OK) return rc;
+  } else {
+    // no tokens: every segment is empty, so the weight and centroid gradients are zero
+    if ((rc = hip_status(launch_permute(s, nullptr, p, wsb, stream))) != MOE_OK) return rc;
+  }
+  if ((rc = hip_status(launch_row_gate(s, perm_row, topk_gate, seg_off, p.max_rows, row_gate, row_dz, stream))) !=
+      MOE_OK)
+    return rc;
+  if (T > 0) {
+    // dH (before the gate) = dout[token] W_down
+    BwdDgrad g1{};
+    g1.a = bf(dout);
+    g1.lda = d;
+    g1.a_gather = row_token;
+    g1.b_routed[0] = bf(w->w_down);
+    g1.b_shared[0] = bf(w->sh_down);
+    g1.b_estride = d * I;
+    g1.ldb = I;
+    g1.b_split = (int)d;
+    g1.out = dhu;
+    g1.ldo = I;
+    g1.tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
+    g1.n_routed = s.n_routed;
+    g1.max_tiles = p.max_tiles;
+    g1.K = (int)d;
+    g1.N = (int)I;
+    if ((rc = hip_status(launch_bwd_dgrad(g1, stream))) != MOE_OK) return rc;
+    // gate/up recomputed: [dA dB], H and the gate-gradient partials
+    GemmOperands g2{};
+    g2.act = u;
+    g2.row_token = row_token;
+    g2.w_routed[0] = w->w_gate;
+    g2.w_routed[1] = w->w_up;
+    g2.w_shared[0] = w->sh_gate;
+    g2.w_shared[1] = w->sh_up;
+    g2.tile_seg = g1.tile_seg;
+    g2.seg_off = seg_off;
+    g2.pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
+    g2.pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
+    g2.n_routed = s.n_routed;
+    g2.K = (int)d;
+    g2.N = (int)I;
+    g2.act_rows = T;
+    g2.max_tiles = p.max_tiles;
+    g2.max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + s.n_routed + s.n_shared) / 2);
+    g2.out = dab;
+    g2.dh = dhu;
+    g2.row_gate = row_gate;
+    g2.out2 = hb;
+    g2.dg_part = dg_part;
+    if ((rc = hip_status(launch_gemm_bf16_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
+    // dX = [dA dB] [W_gate; W_up]
+    BwdDgrad g3{};
+    g3.a = dab;
+    g3.lda = 2 * I;
+    g3.b_routed[0] = bf(w->w_gate);
+    g3.b_routed[1] = bf(w->w_up);
+    g3.b_shared[0] = bf(w->sh_gate);
+    g3.b_shared[1] = bf(w->sh_up);
+    g3.b_estride = I * d;
+    g3.ldb = d;
+    g3.b_split = (int)I;
+    g3.out = dx;
+    g3.ldo = d;
+    g3.tile_seg = g1.tile_seg;
+    g3.n_routed = s.n_routed;
+    g3.max_tiles = p.max_tiles;
+    g3.K = (int)(2 * I);
+    g3.N = (int)d;
+    if ((rc = hip_status(launch_bwd_dgrad(g3, stream))) != MOE_OK) return rc;
+    // router backward and du
+    if ((rc = hip_status(launch_router_bwd(s, u, centroids, topk_idx, perm_row, dg_part, seg_off, dout, dx, du,
+                                           row_dz, stream))) != MOE_OK)
+      return rc;
+  }
+  // dW_down = (g dout)^T H over each segment's rows
+  BwdWgrad g4{};
+  g4.a = bf(dout);
+  g4.lda = d;
+  g4.a_gather = row_token;
+  g4.a_scale = row_gate;
+  g4.b = hb;
+  g4.ldb = I;
+  g4.out_routed[0] = static_cast<uint16_t*>(dw->w_down);
+  g4.out_shared[0] = static_cast<uint16_t*>(dw->sh_down);
+  g4.out_estride = d * I;
+  g4.ldo = I;
+  g4.out_split = (int)d;
+  g4.seg_off = seg_off;
+  g4.n_routed = s.n_routed;
+  g4.M = (int)d;
+  g4.N = (int)I;
+  if ((rc = hip_status(launch_bwd_wgrad(g4, s.n_routed + s.n_shared, stream))) != MOE_OK) return rc;
+  // [dW_gate; dW_up] = [dA dB]^T X
+  BwdWgrad g5{};
+  g5.a = dab;
+  g5.lda = 2 * I;
+  g5.b = bf(u);
+  g5.ldb = d;
+  g5.b_gather = row_token;
+  g5.out_routed[0] = static_cast<uint16_t*>(dw->w_gate);
+  g5.out_routed[1] = static_cast<uint16_t*>(dw->w_up);
+  g5.out_shared[0] = static_cast<uint16_t*>(dw->sh_gate);
+  g5.out_shared[1] = static_cast<uint16_t*>(dw->sh_up);
+  g5.out_estride = I * d;
+  g5.ldo = d;
+  g5.out_split = (int)I;
+  g5.seg_off = seg_off;
+  g5.n_routed = s.n_routed;
+  g5.M = (int)(2 * I);
+  g5.N = (int)d;
+  if ((rc = hip_status(launch_bwd_wgrad(g5, s.n_routed + s.n_shared, stream))) != MOE_OK) return rc;
+  return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, seg_rows, d_centroids, stream));
 }
 
 moe_status moe_update_bias(int32_t n_routed, int64_t total_assignments, const int32_t* expert_load, float* bias,

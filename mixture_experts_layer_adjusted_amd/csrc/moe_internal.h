@@ -44,6 +44,13 @@ struct WorkspacePlan {
   size_t u_q;               // e4m3 [T, d]             (fp8)
   size_t u_scale;           // fp32 [T, d/128]         (fp8)
   size_t route_bytes, forward_bytes, total;
+  // backward only (after the forward section): H, [dA dB], row gates, row dz, gate-gradient partials
+  size_t bwd_h;             // bf16 [max_rows, I]
+  size_t bwd_dab;           // bf16 [max_rows, 2 I]
+  size_t bwd_row_gate;      // fp32 [max_rows]
+  size_t bwd_row_dz;        // fp32 [max_rows]
+  size_t bwd_dg_part;       // fp32 [max_rows, I / 128]
+  size_t backward_total;
   int64_t route_blocks, chunks, max_tiles, max_rows;
 };
 
@@ -92,7 +99,56 @@ struct GemmOperands {
   int64_t max_pairs;         // upper bound on the 256-row tiles: min(max_tiles, (max_tiles + N_r + N_s) / 2)
   void* out;                 // [max_rows, N]
   float* out_scale;          // fp8 SwiGLU output: [max_rows, N/128]
+  // SwiGLU backward epilogue (bf16): reads dh (dL/dH before the gate, [max_rows, N]) and
+  // row_gate, writes out = [dA dB] ([max_rows, 2N]), out2 = H ([max_rows, N]) and
+  // dg_part[row, N-tile] = sum over the tile's features of dh * H
+  const void* dh;
+  const float* row_gate;
+  void* out2;
+  float* dg_part;
 };
+
+// layer backward GEMMs whose operands are not K-contiguous (gemm_bwd.hip)
+struct BwdDgrad {           // out[r, n] = sum_k A[a_gather(r), k] * B_e[k, n]
+  const uint16_t* a;
+  int64_t lda;
+  const int32_t* a_gather;  // optional row map (-1: any valid row)
+  const uint16_t* b_routed[2];  // B_e rows k < b_split from [0], the rest from [1] (at k - b_split)
+  const uint16_t* b_shared[2];
+  int64_t b_estride, ldb;
+  int b_split;
+  uint16_t* out;
+  int64_t ldo;
+  const int32_t* tile_seg;
+  int n_routed;
+  int64_t max_tiles;
+  int K, N;                 // multiples of 64 and 128
+};
+struct BwdWgrad {           // out_e[m, n] = sum_{r in segment e} A[a_gather(r), m] a_scale(r) B[b_gather(r), n]
+  const uint16_t* a;
+  int64_t lda;
+  const int32_t* a_gather;
+  const float* a_scale;     // optional per-row factor
+  const uint16_t* b;
+  int64_t ldb;
+  const int32_t* b_gather;
+  uint16_t* out_routed[2];  // rows m < out_split to [0], the rest to [1] (at m - out_split)
+  uint16_t* out_shared[2];
+  int64_t out_estride, ldo;
+  int out_split;
+  const int32_t* seg_off;
+  int n_routed;
+  int M, N;                 // multiples of 128
+};
+hipError_t launch_bwd_dgrad(const BwdDgrad& g, hipStream_t st);
+hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const float* gate, const int32_t* seg_off,
+                           int64_t max_rows, float* row_gate, float* row_dz, hipStream_t st);
+hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* centroids, const int32_t* idx,
+                             const int32_t* perm_row, const float* dg_part, const int32_t* seg_off, const void* dout,
+                             const void* dX, void* du, float* row_dz, hipStream_t st);
+hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* row_token, const float* row_dz,
+                            const int32_t* seg_off, const int32_t* seg_rows, float* de, hipStream_t st);
+hipError_t launch_bwd_wgrad(const BwdWgrad& g, int n_segments, hipStream_t st);
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_down(int dtype, const GemmOperands& g, hipStream_t st);

@@ -44,6 +44,7 @@ TAG_U, TAG_CENTROID, TAG_BIAS = 1, 2, 3
 TAG_W_GATE, TAG_W_UP, TAG_W_DOWN = 4, 5, 6
 TAG_SH_GATE, TAG_SH_UP, TAG_SH_DOWN = 7, 8, 9
 TAG_PERM = 10
+TAG_DOUT = 11          # upstream gradient dL/dh' of the backward
 
 _MASK64 = (1 << 64) - 1
 

@@ -88,6 +88,19 @@ def test_null_and_workspace_errors_before_launch():
     for ng, mg in ((0, 1), (4, 5), (4, 0), (3, 1), (65, 1), (16, 1)):
         rc = lib.moe_route_grouped(ctypes.byref(s), ng, mg, fake, fake, fake, fake, fake, fake, fake, big, None)
         assert rc == 1, (ng, mg)
+    # backward: bf16 with d, I multiples of 128 only; null pointers, aliasing and a short workspace
+    wg = moe.WeightGrads(0x3000, 0x3000, 0x3000, 0x3000, 0x3000, 0x3000)
+    sb = moe.make_shape(64, 256, 16, 4, 1, 128, moe.MOE_DTYPE_BF16)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_backward_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 2          # fp32
+    assert lib.moe_backward_workspace_size(ctypes.byref(moe.make_shape(64, 136, 16, 4, 1, 128, moe.MOE_DTYPE_BF16)),
+                                           ctypes.byref(n)) == 2                            # d % 128
+    assert lib.moe_backward_workspace_size(ctypes.byref(sb), ctypes.byref(n)) == 0 and n.value > 0
+    args = [fake, fake, ctypes.byref(w), fake, fake, fake, ctypes.c_void_p(0x2000), fake, ctypes.byref(wg)]
+    assert lib.moe_backward(ctypes.byref(sb), *args, fake, 16, None) == 3                   # workspace
+    assert lib.moe_backward(ctypes.byref(sb), *args, None, big, None) == 1                  # null workspace
+    alias = [fake, fake, ctypes.byref(w), fake, fake, fake, fake, fake, ctypes.byref(wg)]  # du == u
+    assert lib.moe_backward(ctypes.byref(sb), *alias, fake, big, None) == 1
     assert lib.moe_update_bias(0, 10, fake, fake, ctypes.c_float(0.001), None) == 1
     assert lib.moe_quantize_weights(1, 100, 128, fake, fake, fake, None) == 2
     assert lib.moe_quantize_act(4, 130, fake, fake, fake, None) == 2
