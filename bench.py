@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--workload", default="v3-prefill-bf16-zipf", choices=sorted(WORKLOADS))
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-backward", action="store_true", help="skip the layer-backward timing (bf16 workloads)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return p.parse_args()
@@ -194,6 +195,40 @@ def main():
                          "route_ms": round(ev_r[0].elapsed_time(ev_r[1]) / reps, 4),
                          "route_grouped_ms": round(ev_r[1].elapsed_time(ev_r[2]) / reps, 4)}
 
+    # layer backward (bf16): gradients of <dout, h'> for the routing of the last step, timed on its own
+    backward = None
+    if cfg.dtype == "bf16" and not args.no_backward:
+        from synth import TAG_DOUT, stream_key
+        from synth.device import fill_normal_
+        dout = fill_normal_(torch.empty((T, d), dtype=torch.bfloat16, device="cuda"),
+                            stream_key(cfg.seed, cfg.cid, TAG_DOUT, 0), 1.0)
+        du = torch.empty_like(dout)
+        dcent = torch.empty((N, d), dtype=torch.float32, device="cuda")
+        grads = {k: torch.empty_like(dev[k]) for k in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")}
+        wgr = moe.make_weight_grads(grads["w_gate"], grads["w_up"], grads["w_down"], grads["sh_gate"] if Ns else None,
+                                    grads["sh_up"] if Ns else None, grads["sh_down"] if Ns else None)
+        ws_b = torch.empty(moe.moe_backward_workspace_size(shape), dtype=torch.uint8, device="cuda")
+        moe.moe_backward(shape, dev["u"], dev["centroids"], weights, idx, gate, dout, du, dcent, wgr, ws_b, stream)
+        ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 3
+        ev_b[0].record(stream)
+        for _ in range(reps):
+            moe.moe_backward(shape, dev["u"], dev["centroids"], weights, idx, gate, dout, du, dcent, wgr, ws_b,
+                             stream)
+        ev_b[1].record(stream)
+        torch.cuda.synchronize()
+        b_ms = ev_b[0].elapsed_time(ev_b[1]) / reps
+        rows_b = T * K + Ns * T
+        # algorithmic: dgrad 6 d I + wgrad 6 d I per row; executed adds the recomputed gate/up (4 d I)
+        fl_alg = 12.0 * rows_b * d * I + 4.0 * T * K * d
+        fl_exec = fl_alg + 4.0 * rows_b * d * I
+        backward = {"ms": round(b_ms, 3), "tokens_per_s": round(T / (b_ms * 1e-3), 1),
+                    "tflops_algorithmic": round(fl_alg / (b_ms * 1e-3) / 1e12, 1),
+                    "tflops_executed": round(fl_exec / (b_ms * 1e-3) / 1e12, 1),
+                    "mfma_peak_frac_executed": round(fl_exec / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+        del grads, ws_b, du, dout, dcent
+        torch.cuda.empty_cache()
+
     st = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(7)] for i in range(args.steps)])
     stage_names = ["route", "permute", "quantize_act", "gemm_gate_up_swiglu", "gemm_down", "combine",
                    "update_bias"]
@@ -243,6 +278,7 @@ def main():
                         "frac": round(combine_bytes / (float(st[:, 5].mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "load_max_over_mean": ratios,
         "route_grouped": route_grouped,
+        "backward": backward,
         "wall_s_timed": round(t_wall, 3),
         "cpu_baseline": None,
     }

@@ -12,7 +12,7 @@ BUILD = os.path.join(_HERE, "_build")
 LIB = os.path.join(_HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip", "gemm_fp8.hip",
-           "combine.hip", "bias_quant.hip", "gemm_bwd.hip", "backward.hip"]
+           "combine.hip", "bias_quant.hip", "backward.hip"]
 FLAGS = ["--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=fast",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]

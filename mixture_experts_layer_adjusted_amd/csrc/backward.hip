@@ -187,6 +187,56 @@ __global__ void __launch_bounds__(256) dcentroid_kernel(const uint16_t* __restri
   de[(int64_t)i * d + j] = acc;
 }
 
+// dst[b][c * ldd + off + r] = scale[r] * src[b][gather[r] * lds + c] for r < R, c < C (bf16):
+// 64 x 64 tiles through LDS, 16-byte loads along c and 16-byte stores along r.  A row with
+// gather < 0 (padding) or scale 0 is written as zeros.
+__global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
+  __shared__ uint16_t tile[64][64 + 8];
+  const int64_t b = blockIdx.z;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const uint16_t* src = a.src + b * a.src_bstride;
+  uint16_t* dst = a.dst + b * a.dst_bstride;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int v = tid + 256 * i;          // 512 vectors of 8 along c
+    const int rl = v >> 3, cl = (v & 7) * 8;
+    const int r = r0 + rl, c = c0 + cl;
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if (r < a.R && c < a.C) {
+      const int64_t srow = a.gather ? (int64_t)a.gather[r] : r;
+      if (srow >= 0) {
+        q = *reinterpret_cast<const uint4*>(src + srow * a.lds + c);
+        if (a.scale) {
+          const float s = a.scale[r];
+          uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = (uint32_t)f32_to_bf16(__uint_as_float(w[j] << 16) * s) |
+                   ((uint32_t)f32_to_bf16(__uint_as_float(w[j] & 0xFFFF0000u) * s) << 16);
+          q = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[rl][cl + j] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int v = tid + 256 * i;          // 512 vectors of 8 along r
+    const int cl = v >> 3, rl = (v & 7) * 8;
+    const int r = r0 + rl, c = c0 + cl;
+    if (c < a.C && r < a.R) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)tile[rl + 2 * j][cl] | ((uint32_t)tile[rl + 2 * j + 1][cl] << 16);
+      *reinterpret_cast<uint4*>(dst + (int64_t)c * a.ldd + a.off + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const float* gate, const int32_t* seg_off,
@@ -218,6 +268,17 @@ hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* ro
                             const int32_t* seg_off, const int32_t* seg_rows, float* de, hipStream_t st) {
   hipLaunchKernelGGL(dcentroid_kernel, dim3((unsigned)s.n_routed, (unsigned)ceil_div(s.hidden, 256)), dim3(256), 0,
                      st, static_cast<const uint16_t*>(u), row_token, row_dz, seg_off, seg_rows, s.hidden, de);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_transpose(const TransposeArgs& a, int batch, hipStream_t st) {
+  if (a.R == 0 || a.C == 0 || batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(a.R, 64), (unsigned)ceil_div(a.C, 64), (unsigned)batch),
+                     dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -353,7 +353,7 @@ __device__ __forceinline__ void store_swiglu_bwd(const f32x16 (&acc)[MB][2], con
 // EPI: 0 plain store (down GEMM), 1 SwiGLU (gate/up GEMM), 2 SwiGLU backward (gate/up recomputed)
 template <int EPI, int BK, int WAVES, int WROWS, int WGS, int WM, int TM>
 __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kernel(GemmOperands g, int NT) {
-  constexpr bool SWIGLU = EPI != 0;
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
   using C = StreamCfg<BK, WAVES, WROWS, WGS, TM>;
   constexpr int WN = WAVES / WM;           // wavefront grid WM x WN
   constexpr int RW = TM / WM;              // rows per wavefront
@@ -367,21 +367,39 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   const int b = blockIdx.x;
   constexpr int kSpan = kXcds * C::kXcdChunk;
   const int64_t L = (int64_t)(b / kSpan) * kSpan + (b % kXcds) * C::kXcdChunk + (b / kXcds) % C::kXcdChunk;
-  const int64_t slot = L / NT;             // M-tile (TM = 128) or pair of M-tiles (TM = 256)
-  if (slot >= g.max_tiles) return;
-  const int seg = TM == kTileM ? g.tile_seg[slot] : g.pair_seg[slot];
-  if (seg < 0) return;
-  const int seg_first = TM == kTileM ? g.seg_off[seg] / kTileM : g.pair_off[seg];
-  const int seg_count = TM == kTileM ? g.seg_off[seg + 1] / kTileM - seg_first : g.pair_off[seg + 1] - seg_first;
-  const int64_t lam = L - (int64_t)seg_first * NT;
-  const int grp = (int)(lam / (kGroupM * NT));
-  const int gm = min(kGroupM, seg_count - grp * kGroupM);
-  const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
-  const int local = grp * kGroupM + rem % gm;
-  const int nt = rem / gm;
-  const int64_t m0 = (int64_t)g.seg_off[seg] + (int64_t)local * TM;
-  // rows of this tile that belong to the segment (a half tile has 128)
-  const int tile_rows = TM == kTileM ? TM : min(TM, g.seg_off[seg + 1] - (int)(m0));
+  int seg, nt, tile_rows, nk;
+  int64_t m0, k_base;
+  if constexpr (EPI == 3) {
+    // weight gradient: segment seg's M x N matrix, K over the segment's columns
+    const int MT = (g.wg_m + TM - 1) / TM;
+    const int64_t per = (int64_t)MT * NT;
+    seg = (int)(L / per);
+    if (seg >= g.n_seg) return;
+    const int rem = (int)(L - (int64_t)seg * per);
+    nt = rem / MT;
+    m0 = (int64_t)(rem % MT) * TM;
+    tile_rows = min(TM, g.wg_m - (int)m0);
+    k_base = g.seg_off[seg];
+    nk = (g.seg_off[seg + 1] - g.seg_off[seg]) / BK;
+  } else {
+    const int64_t slot = L / NT;             // M-tile (TM = 128) or pair of M-tiles (TM = 256)
+    if (slot >= g.max_tiles) return;
+    seg = TM == kTileM ? g.tile_seg[slot] : g.pair_seg[slot];
+    if (seg < 0) return;
+    const int seg_first = TM == kTileM ? g.seg_off[seg] / kTileM : g.pair_off[seg];
+    const int seg_count = TM == kTileM ? g.seg_off[seg + 1] / kTileM - seg_first : g.pair_off[seg + 1] - seg_first;
+    const int64_t lam = L - (int64_t)seg_first * NT;
+    const int grp = (int)(lam / (kGroupM * NT));
+    const int gm = min(kGroupM, seg_count - grp * kGroupM);
+    const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
+    const int local = grp * kGroupM + rem % gm;
+    nt = rem / gm;
+    m0 = (int64_t)g.seg_off[seg] + (int64_t)local * TM;
+    // rows of this tile that belong to the segment (a half tile has 128)
+    tile_rows = TM == kTileM ? TM : min(TM, g.seg_off[seg + 1] - (int)(m0));
+    k_base = 0;
+    nk = g.K / BK;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -392,10 +410,14 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
   const size_t wstride = (size_t)N * K;
-  const char* W0 = static_cast<const char*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride * 2;
+  // row strides (elements): the forward reads rows of length K; the weight-gradient mode reads
+  // the transposed activations, rows of length lda / ldw, from column k_base on
+  const int64_t lda = EPI == 3 ? g.lda : K, ldw = EPI == 3 ? g.ldw : K;
+  const char* W0 = EPI == 3 ? static_cast<const char*>(g.w_routed[0]) + k_base * 2
+                            : static_cast<const char*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride * 2;
   const char* W1 = SWIGLU ? static_cast<const char*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride * 2
                           : nullptr;
-  const char* act = static_cast<const char*>(g.act);
+  const char* act = static_cast<const char*>(g.act) + k_base * 2;
 
   // ---- per-lane sources, as 32-bit byte offsets from a wave-uniform base (the launcher checks that
   // the activation matrix and one expert's weight matrix stay below 4 GiB): wave w fills activation
@@ -411,7 +433,7 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
     const int64_t r = m0 + (row < tile_rows ? row : 0);  // rows past a half tile: a valid row
     int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;  // padding row: any valid row (its outputs are never read)
-    aoff[i] = (uint32_t)(tok * K * 2) + ((lslot ^ C::swz(row)) << 4);
+    aoff[i] = (uint32_t)(tok * lda * 2) + ((lslot ^ C::swz(row)) << 4);
   }
   uint32_t woff[C::kWDma];
 #pragma unroll
@@ -419,7 +441,7 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
     const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;  // row within the weight tile
     int n = n0 + (SWIGLU ? r % (WROWS / 2) : r);
     if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-    woff[i] = (uint32_t)n * (uint32_t)(K * 2) + ((lslot ^ C::swz(TM + r)) << 4);
+    woff[i] = (uint32_t)(n * ldw * 2) + ((lslot ^ C::swz(TM + r)) << 4);
   }
   // gate rows come from W0, up rows from W1; the split falls on a wave boundary
   const char* wbase = (SWIGLU && wave * (WROWS / WAVES) >= WROWS / 2) ? W1 : W0;
@@ -454,7 +476,6 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   const bool active = mrow0 < tile_rows;   // false only for the upper half of a half tile
   constexpr bool kAccInAgprs = MB * NBW * 16 > 128;
 
-  const int nk = K / BK;
   constexpr int kAhead = C::kStages - 1;
 #pragma unroll
   for (int s = 0; s < kAhead; ++s)
@@ -508,6 +529,9 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
     static_assert(NBW == 2 && WN == 4, "one gate and one up block per wavefront, four wavefronts per row");
     __shared__ float red[TM][4];
     store_swiglu_bwd<MB>(acc, g, m0, mrow0, n0 + wn * (WRW / 2), nt, wn, tile_rows, active, l32, khalf, red);
+  } else if constexpr (EPI == 3) {
+    uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
+    if (active) store_tile<false, MB, NBW>(acc, out, m0 + mrow0, n0 + wn * WRW, N, l32, khalf);
   } else if (active) {
     store_tile<SWIGLU, MB, NBW>(acc, static_cast<uint16_t*>(g.out), m0 + mrow0,
                                 n0 + wn * (SWIGLU ? WRW / 2 : WRW), N, l32, khalf);
@@ -516,12 +540,14 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
 
 template <int EPI>
 hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
-  constexpr bool SWIGLU = EPI != 0;
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
   constexpr int SBK = MOE_STREAM_BK, SW = MOE_STREAM_WAVES, SR = MOE_STREAM_WROWS, SG = MOE_STREAM_WGS;
   constexpr int SM = MOE_STREAM_WM, STM = MOE_STREAM_TM;
   using SC = StreamCfg<SBK, SW, SR, SG, STM>;
   // the streaming kernel addresses its sources with 32-bit byte offsets
-  const bool offsets_fit = g.act_rows * g.K * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.K * 2 < (int64_t(1) << 32);
+  const bool offsets_fit =
+      EPI == 3 ? (int64_t)g.wg_m * g.lda * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.ldw * 2 < (int64_t(1) << 32)
+               : g.act_rows * g.K * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.K * 2 < (int64_t(1) << 32);
   if (g.K % SBK == 0 && offsets_fit) {
     const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
     const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
@@ -533,13 +559,14 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
       if (err != hipSuccess) return err;
       attr_set = true;
     }
-    const int64_t tiles = (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
+    const int64_t tiles = EPI == 3 ? (int64_t)g.n_seg * ceil_div(g.wg_m, STM) * NT
+                                   : (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
     const int64_t span = kXcds * SC::kXcdChunk;
     const int64_t grid = ceil_div(tiles, span) * span;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SC::kThreads), lds_bytes, st, g, NT);
     return hipGetLastError();
   }
-  if (EPI == 2) return hipErrorInvalidValue;   // the backward epilogue exists in the streaming kernel only
+  if (EPI >= 2) return hipErrorInvalidValue;   // the backward modes exist in the streaming kernel only
   const size_t lds_bytes = 2 * kStageElems * sizeof(uint16_t);
   static bool attr_set = false;
   if (!attr_set) {
@@ -558,5 +585,6 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
 hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st) { return launch_bf16<1>(g, st); }
 hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st) { return launch_bf16<0>(g, st); }
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_bf16<2>(g, st); }
+hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st) { return launch_bf16<3>(g, st); }
 
 }  // namespace moe

@@ -13,6 +13,7 @@ hipError_t launch_gemm_f32_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st);
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st) {
   if (dtype == MOE_DTYPE_F32) return launch_gemm_f32_swiglu(g, st);
@@ -74,6 +75,12 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.bwd_row_gate = take((size_t)p.max_rows * 4);
   p.bwd_row_dz = take((size_t)p.max_rows * 4);
   p.bwd_dg_part = take((size_t)p.max_rows * (I / 128 > 0 ? I / 128 : 1) * 4);
+  p.bwd_wd_t = take((size_t)(N + Ns) * I * d * 2);
+  p.bwd_wc_t = take((size_t)(N + Ns) * d * 2 * I * 2);
+  p.bwd_dy_t = take((size_t)d * p.max_rows * 2);
+  p.bwd_h_t = take((size_t)I * p.max_rows * 2);
+  p.bwd_dab_t = take((size_t)2 * I * p.max_rows * 2);
+  p.bwd_x_t = take((size_t)d * p.max_rows * 2);
   p.backward_total = o;
   return p;
 }
@@ -263,7 +270,8 @@ static moe_status check_backward_shape(const moe_shape* s) {
   const int64_t max_rows =
       ((int64_t)s->tokens * s->top_k + (int64_t)s->n_routed * (kTileM - 1)) / kTileM * kTileM +
       (int64_t)s->n_shared * ceil_div(s->tokens, kTileM) * kTileM;
-  if (max_rows * 2 * s->inter * 2 >= (int64_t(1) << 32) || (int64_t)s->tokens * s->hidden * 2 >= (int64_t(1) << 32))
+  const int64_t widest = std::max<int64_t>(s->hidden, 2 * (int64_t)s->inter);
+  if (max_rows * widest * 2 >= (int64_t(1) << 32) || (int64_t)s->tokens * s->hidden * 2 >= (int64_t(1) << 32))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -315,110 +323,107 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
   if ((rc = hip_status(launch_row_gate(s, perm_row, topk_gate, seg_off, p.max_rows, row_gate, row_dz, stream))) !=
       MOE_OK)
     return rc;
+  const int64_t Nr = s.n_routed, Ns = s.n_shared, P = p.max_rows;
+  uint16_t* wd_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_wd_t);   // [N_r + N_s][I][d]
+  uint16_t* wc_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_wc_t);   // [N_r + N_s][d][2I]
+  uint16_t* dy_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_dy_t);   // [d][P]
+  uint16_t* h_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_h_t);     // [I][P]
+  uint16_t* dab_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_dab_t); // [2I][P]
+  uint16_t* x_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_x_t);     // [d][P]
+  auto transpose = [&](const void* src, int64_t lds, int64_t src_b, const int32_t* gather, const float* scale,
+                       uint16_t* dst, int64_t ldd, int64_t off, int64_t dst_b, int64_t R, int64_t C, int64_t batch) {
+    TransposeArgs t{bf(src), lds, src_b, gather, scale, dst, ldd, off, dst_b, (int)R, (int)C};
+    return hip_status(launch_transpose(t, (int)batch, stream));
+  };
+  const int32_t* tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
+  const int32_t* pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
+  const int32_t* pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
+  const int64_t max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + Nr + Ns) / 2);
+  auto grouped = [&](const void* act, const int32_t* rt, int64_t act_rows, const uint16_t* w_r, const uint16_t* w_s,
+                     int K, int N, void* out) {
+    GemmOperands g{};
+    g.act = act;
+    g.row_token = rt;
+    g.w_routed[0] = w_r;
+    g.w_shared[0] = w_s;
+    g.tile_seg = tile_seg;
+    g.seg_off = seg_off;
+    g.pair_seg = pair_seg;
+    g.pair_off = pair_off;
+    g.n_routed = s.n_routed;
+    g.K = K;
+    g.N = N;
+    g.act_rows = act_rows;
+    g.max_tiles = p.max_tiles;
+    g.max_pairs = max_pairs;
+    g.out = out;
+    return g;
+  };
+  auto wgrad = [&](const uint16_t* a_t, int M, const uint16_t* b_t, int N, void* out_r, void* out_s) {
+    GemmOperands g{};
+    g.act = a_t;
+    g.w_routed[0] = b_t;
+    g.seg_off = seg_off;
+    g.n_routed = s.n_routed;
+    g.N = N;
+    g.lda = P;
+    g.ldw = P;
+    g.wg_m = M;
+    g.n_seg = (int)(Nr + Ns);
+    g.out = out_r;
+    g.out2 = out_s;
+    return hip_status(launch_gemm_bf16_wgrad(g, stream));
+  };
+
   if (T > 0) {
+    // K-contiguous copies of the weights for the input-gradient GEMMs:
+    // W_down^T [I][d] and [W_gate; W_up]^T [d][2I] per expert
+    if ((rc = transpose(w->w_down, I, d * I, nullptr, nullptr, wd_t, d, 0, I * d, d, I, Nr)) != MOE_OK) return rc;
+    if ((rc = transpose(w->w_gate, d, I * d, nullptr, nullptr, wc_t, 2 * I, 0, d * 2 * I, I, d, Nr)) != MOE_OK) return rc;
+    if ((rc = transpose(w->w_up, d, I * d, nullptr, nullptr, wc_t, 2 * I, I, d * 2 * I, I, d, Nr)) != MOE_OK) return rc;
+    if (Ns > 0) {
+      if ((rc = transpose(w->sh_down, I, d * I, nullptr, nullptr, wd_t + Nr * I * d, d, 0, I * d, d, I, Ns)) != MOE_OK)
+        return rc;
+      if ((rc = transpose(w->sh_gate, d, I * d, nullptr, nullptr, wc_t + Nr * d * 2 * I, 2 * I, 0, d * 2 * I, I, d,
+                          Ns)) != MOE_OK)
+        return rc;
+      if ((rc = transpose(w->sh_up, d, I * d, nullptr, nullptr, wc_t + Nr * d * 2 * I, 2 * I, I, d * 2 * I, I, d,
+                          Ns)) != MOE_OK)
+        return rc;
+    }
     // dH (before the gate) = dout[token] W_down
-    BwdDgrad g1{};
-    g1.a = bf(dout);
-    g1.lda = d;
-    g1.a_gather = row_token;
-    g1.b_routed[0] = bf(w->w_down);
-    g1.b_shared[0] = bf(w->sh_down);
-    g1.b_estride = d * I;
-    g1.ldb = I;
-    g1.b_split = (int)d;
-    g1.out = dhu;
-    g1.ldo = I;
-    g1.tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
-    g1.n_routed = s.n_routed;
-    g1.max_tiles = p.max_tiles;
-    g1.K = (int)d;
-    g1.N = (int)I;
-    if ((rc = hip_status(launch_bwd_dgrad(g1, stream))) != MOE_OK) return rc;
+    GemmOperands g1 = grouped(dout, row_token, T, wd_t, wd_t + Nr * I * d, (int)d, (int)I, dhu);
+    if ((rc = hip_status(launch_gemm_bf16_down(g1, stream))) != MOE_OK) return rc;
     // gate/up recomputed: [dA dB], H and the gate-gradient partials
-    GemmOperands g2{};
-    g2.act = u;
-    g2.row_token = row_token;
+    GemmOperands g2 = grouped(u, row_token, T, nullptr, nullptr, (int)d, (int)I, dab);
     g2.w_routed[0] = w->w_gate;
     g2.w_routed[1] = w->w_up;
     g2.w_shared[0] = w->sh_gate;
     g2.w_shared[1] = w->sh_up;
-    g2.tile_seg = g1.tile_seg;
-    g2.seg_off = seg_off;
-    g2.pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
-    g2.pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
-    g2.n_routed = s.n_routed;
-    g2.K = (int)d;
-    g2.N = (int)I;
-    g2.act_rows = T;
-    g2.max_tiles = p.max_tiles;
-    g2.max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + s.n_routed + s.n_shared) / 2);
-    g2.out = dab;
     g2.dh = dhu;
     g2.row_gate = row_gate;
     g2.out2 = hb;
     g2.dg_part = dg_part;
     if ((rc = hip_status(launch_gemm_bf16_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
     // dX = [dA dB] [W_gate; W_up]
-    BwdDgrad g3{};
-    g3.a = dab;
-    g3.lda = 2 * I;
-    g3.b_routed[0] = bf(w->w_gate);
-    g3.b_routed[1] = bf(w->w_up);
-    g3.b_shared[0] = bf(w->sh_gate);
-    g3.b_shared[1] = bf(w->sh_up);
-    g3.b_estride = I * d;
-    g3.ldb = d;
-    g3.b_split = (int)I;
-    g3.out = dx;
-    g3.ldo = d;
-    g3.tile_seg = g1.tile_seg;
-    g3.n_routed = s.n_routed;
-    g3.max_tiles = p.max_tiles;
-    g3.K = (int)(2 * I);
-    g3.N = (int)d;
-    if ((rc = hip_status(launch_bwd_dgrad(g3, stream))) != MOE_OK) return rc;
+    GemmOperands g3 = grouped(dab, nullptr, P, wc_t, wc_t + Nr * d * 2 * I, (int)(2 * I), (int)d, dx);
+    if ((rc = hip_status(launch_gemm_bf16_down(g3, stream))) != MOE_OK) return rc;
     // router backward and du
     if ((rc = hip_status(launch_router_bwd(s, u, centroids, topk_idx, perm_row, dg_part, seg_off, dout, dx, du,
                                            row_dz, stream))) != MOE_OK)
       return rc;
+    // K-contiguous (transposed) activations of every permuted row for the weight-gradient GEMMs:
+    // (g dout)^T [d][P], H^T [I][P], [dA dB]^T [2I][P], X^T [d][P]; padding rows are zero
+    if ((rc = transpose(dout, d, 0, row_token, row_gate, dy_t, P, 0, 0, P, d, 1)) != MOE_OK) return rc;
+    if ((rc = transpose(hb, I, 0, nullptr, nullptr, h_t, P, 0, 0, P, I, 1)) != MOE_OK) return rc;
+    if ((rc = transpose(dab, 2 * I, 0, nullptr, nullptr, dab_t, P, 0, 0, P, 2 * I, 1)) != MOE_OK) return rc;
+    if ((rc = transpose(u, d, 0, row_token, nullptr, x_t, P, 0, 0, P, d, 1)) != MOE_OK) return rc;
   }
-  // dW_down = (g dout)^T H over each segment's rows
-  BwdWgrad g4{};
-  g4.a = bf(dout);
-  g4.lda = d;
-  g4.a_gather = row_token;
-  g4.a_scale = row_gate;
-  g4.b = hb;
-  g4.ldb = I;
-  g4.out_routed[0] = static_cast<uint16_t*>(dw->w_down);
-  g4.out_shared[0] = static_cast<uint16_t*>(dw->sh_down);
-  g4.out_estride = d * I;
-  g4.ldo = I;
-  g4.out_split = (int)d;
-  g4.seg_off = seg_off;
-  g4.n_routed = s.n_routed;
-  g4.M = (int)d;
-  g4.N = (int)I;
-  if ((rc = hip_status(launch_bwd_wgrad(g4, s.n_routed + s.n_shared, stream))) != MOE_OK) return rc;
-  // [dW_gate; dW_up] = [dA dB]^T X
-  BwdWgrad g5{};
-  g5.a = dab;
-  g5.lda = 2 * I;
-  g5.b = bf(u);
-  g5.ldb = d;
-  g5.b_gather = row_token;
-  g5.out_routed[0] = static_cast<uint16_t*>(dw->w_gate);
-  g5.out_routed[1] = static_cast<uint16_t*>(dw->w_up);
-  g5.out_shared[0] = static_cast<uint16_t*>(dw->sh_gate);
-  g5.out_shared[1] = static_cast<uint16_t*>(dw->sh_up);
-  g5.out_estride = I * d;
-  g5.ldo = d;
-  g5.out_split = (int)I;
-  g5.seg_off = seg_off;
-  g5.n_routed = s.n_routed;
-  g5.M = (int)(2 * I);
-  g5.N = (int)d;
-  if ((rc = hip_status(launch_bwd_wgrad(g5, s.n_routed + s.n_shared, stream))) != MOE_OK) return rc;
+  // dW_down = (g dY)^T H, dW_gate = dA^T X, dW_up = dB^T X over each segment's rows (an empty
+  // segment writes zeros)
+  if ((rc = wgrad(dy_t, (int)d, h_t, (int)I, dw->w_down, dw->sh_down)) != MOE_OK) return rc;
+  if ((rc = wgrad(dab_t, (int)I, x_t, (int)d, dw->w_gate, dw->sh_gate)) != MOE_OK) return rc;
+  if ((rc = wgrad(dab_t + I * P, (int)I, x_t, (int)d, dw->w_up, dw->sh_up)) != MOE_OK) return rc;
   return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, seg_rows, d_centroids, stream));
 }
 

@@ -50,6 +50,12 @@ struct WorkspacePlan {
   size_t bwd_row_gate;      // fp32 [max_rows]
   size_t bwd_row_dz;        // fp32 [max_rows]
   size_t bwd_dg_part;       // fp32 [max_rows, I / 128]
+  size_t bwd_wd_t;          // bf16 [N_r + N_s, I, d]   W_down transposed
+  size_t bwd_wc_t;          // bf16 [N_r + N_s, d, 2 I] [W_gate; W_up] transposed
+  size_t bwd_dy_t;          // bf16 [d, max_rows]      (gate * dout of each row) transposed
+  size_t bwd_h_t;           // bf16 [I, max_rows]
+  size_t bwd_dab_t;         // bf16 [2 I, max_rows]
+  size_t bwd_x_t;           // bf16 [d, max_rows]
   size_t backward_total;
   int64_t route_blocks, chunks, max_tiles, max_rows;
 };
@@ -106,41 +112,26 @@ struct GemmOperands {
   const float* row_gate;
   void* out2;
   float* dg_part;
+  // weight-gradient mode (bf16): out_e[m, n] = sum over the columns k of segment e of
+  // act[m, k] * w_routed[0][n, k] (transposed activations, row strides lda and ldw), m < wg_m;
+  // routed segments write out + e M N, shared ones out2 + (e - N_r) M N
+  int64_t lda, ldw;
+  int wg_m, n_seg;
 };
 
-// layer backward GEMMs whose operands are not K-contiguous (gemm_bwd.hip)
-struct BwdDgrad {           // out[r, n] = sum_k A[a_gather(r), k] * B_e[k, n]
-  const uint16_t* a;
-  int64_t lda;
-  const int32_t* a_gather;  // optional row map (-1: any valid row)
-  const uint16_t* b_routed[2];  // B_e rows k < b_split from [0], the rest from [1] (at k - b_split)
-  const uint16_t* b_shared[2];
-  int64_t b_estride, ldb;
-  int b_split;
-  uint16_t* out;
-  int64_t ldo;
-  const int32_t* tile_seg;
-  int n_routed;
-  int64_t max_tiles;
-  int K, N;                 // multiples of 64 and 128
+// layer backward helpers (backward.hip)
+// dst[b][c * ldd + off + r] = scale[r] * src[b][gather[r] * lds + c], r < R, c < C (bf16); R and C
+// multiples of 8; a row whose gather entry is negative is written as zeros
+struct TransposeArgs {
+  const uint16_t* src;
+  int64_t lds, src_bstride;
+  const int32_t* gather;
+  const float* scale;
+  uint16_t* dst;
+  int64_t ldd, off, dst_bstride;
+  int R, C;
 };
-struct BwdWgrad {           // out_e[m, n] = sum_{r in segment e} A[a_gather(r), m] a_scale(r) B[b_gather(r), n]
-  const uint16_t* a;
-  int64_t lda;
-  const int32_t* a_gather;
-  const float* a_scale;     // optional per-row factor
-  const uint16_t* b;
-  int64_t ldb;
-  const int32_t* b_gather;
-  uint16_t* out_routed[2];  // rows m < out_split to [0], the rest to [1] (at m - out_split)
-  uint16_t* out_shared[2];
-  int64_t out_estride, ldo;
-  int out_split;
-  const int32_t* seg_off;
-  int n_routed;
-  int M, N;                 // multiples of 128
-};
-hipError_t launch_bwd_dgrad(const BwdDgrad& g, hipStream_t st);
+hipError_t launch_transpose(const TransposeArgs& a, int batch, hipStream_t st);
 hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const float* gate, const int32_t* seg_off,
                            int64_t max_rows, float* row_gate, float* row_dz, hipStream_t st);
 hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* centroids, const int32_t* idx,
@@ -148,7 +139,6 @@ hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* cen
                              const void* dX, void* du, float* row_dz, hipStream_t st);
 hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* row_token, const float* row_dz,
                             const int32_t* seg_off, const int32_t* seg_rows, float* de, hipStream_t st);
-hipError_t launch_bwd_wgrad(const BwdWgrad& g, int n_segments, hipStream_t st);
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_down(int dtype, const GemmOperands& g, hipStream_t st);

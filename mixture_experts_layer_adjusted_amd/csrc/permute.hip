@@ -13,7 +13,8 @@
 //  segments: one workgroup turns the per-chunk counts into segment sizes, padded
 //            segment offsets (block-wide exclusive scan), the row base of every
 //            (chunk, expert) pair, the segment id of every M-tile, and the same for
-//            256-row tiles (pairs of M-tiles, a second scan);
+//            256-row tiles (pairs of M-tiles, a second scan); rows past the last
+//            segment get row_token -1;
 //  scatter:  per chunk, every pick gets row base[chunk][e] + (picks of e before it in
 //            (token, slot) order), ranked 64 picks at a time with ballots; extra
 //            workgroups write the identity rows of the shared segments and mark padding
@@ -63,7 +64,8 @@ __global__ void __launch_bounds__(kSegThreads) perm_segments_kernel(const int32_
                                                                     int32_t* __restrict__ seg_rows,
                                                                     int32_t* __restrict__ tile_seg,
                                                                     int32_t* __restrict__ pair_seg,
-                                                                    int32_t* __restrict__ pair_off) {
+                                                                    int32_t* __restrict__ pair_off,
+                                                                    int32_t* __restrict__ row_token) {
   __shared__ int32_t scan[kSegThreads];
   __shared__ int32_t total_rows, total_pairs;
   const int tid = threadIdx.x;
@@ -122,6 +124,9 @@ __global__ void __launch_bounds__(kSegThreads) perm_segments_kernel(const int32_
   }
   for (int64_t j = total_rows / kTileM + tid; j < max_tiles; j += kSegThreads) tile_seg[j] = -1;
   for (int64_t j = total_pairs + tid; j < max_tiles; j += kSegThreads) pair_seg[j] = -1;
+  // rows past the last segment belong to no token (passes over all max_rows rows gather through
+  // row_token)
+  for (int64_t j = total_rows + tid; j < max_tiles * kTileM; j += kSegThreads) row_token[j] = -1;
 }
 
 __global__ void __launch_bounds__(kThreads) perm_scatter_kernel(const int32_t* __restrict__ idx, int T, int K, int N,
@@ -218,7 +223,7 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const Workspac
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(perm_segments_kernel, dim3(1), dim3(kSegThreads), 0, st, counts, p.chunks, T, N, Ns,
-                     p.max_tiles, base, seg_off, seg_rows, tile_seg, pair_seg, pair_off);
+                     p.max_tiles, base, seg_off, seg_rows, tile_seg, pair_seg, pair_off, row_token);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)(p.chunks + N + Ns)), dim3(kThreads), 0, st, idx, T, K,

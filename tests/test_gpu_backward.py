@@ -163,6 +163,32 @@ def test_backward_v3_decode_shape_sampled():
     assert e_du <= BWD_TOL and e_de <= BWD_TOL and e_w <= BWD_TOL
 
 
+def test_backward_ignores_stale_workspace():
+    """Every row of the permuted layout that the backward's passes touch is defined by the call
+    itself: a workspace holding arbitrary bytes from earlier use gives the same gradients."""
+    cfg = _small("bwd-stale", 77, 384, 8, 3, 0, 384, cid=65)
+    h = host.make_host_inputs(cfg)
+    dev = host_to_device(h)
+    r = Runner(cfg, dev)
+    r.route()
+    dout_d, _ = _dout(cfg, cfg.tokens)
+    ws = torch.empty(moe.moe_backward_workspace_size(r.shape), dtype=torch.uint8, device="cuda")
+    outs = []
+    for fill in (0x00, 0x55):
+        ws.fill_(fill)
+        du = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+        de = torch.empty((cfg.n_routed, cfg.hidden), dtype=torch.float32, device="cuda")
+        g = _grads_like(dev, 0)
+        wg = moe.make_weight_grads(g["w_gate"], g["w_up"], g["w_down"])
+        moe.moe_backward(r.shape, dev["u"], dev["centroids"], r.weights, r.idx, r.gate, dout_d, du, de, wg, ws)
+        torch.cuda.synchronize()
+        outs.append((du, de, g))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+    for k in ("w_gate", "w_up", "w_down"):
+        assert torch.equal(outs[0][2][k].view(torch.int16), outs[1][2][k].view(torch.int16)), k
+
+
 def test_backward_zero_tokens_writes_zero_gradients():
     cfg = _small("bwd-empty", 64, 256, 8, 2, 1, 128, cid=64)
     h = host.make_host_inputs(cfg)
