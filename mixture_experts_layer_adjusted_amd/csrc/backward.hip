@@ -188,52 +188,55 @@ __global__ void __launch_bounds__(256) dcentroid_kernel(const uint16_t* __restri
 }
 
 // dst[b][c * ldd + off + r] = scale[r] * src[b][gather[r] * lds + c] for r < R, c < C (bf16):
-// 64 x 64 tiles through LDS, 16-byte loads along c and 16-byte stores along r.  A row with
-// gather < 0 (padding) or scale 0 is written as zeros.
+// 64 x 64 tiles through LDS.  Each thread loads rows 2p and 2p + 1 at 8 consecutive columns
+// (two 16-byte loads) and stores the 8 column pairs as 32-bit words tile[c][p] (the pitch of 33
+// words keeps a wavefront's writes on distinct banks); the store phase reads 4 words = 8
+// consecutive rows of one column and writes them with one 16-byte store.  A row whose gather
+// entry is negative (padding) is written as zeros.
+__device__ __forceinline__ uint4 load_row8(const TransposeArgs& a, const uint16_t* src, int r, int c) {
+  if (r >= a.R || c >= a.C) return make_uint4(0u, 0u, 0u, 0u);
+  const int64_t srow = a.gather ? (int64_t)a.gather[r] : r;
+  if (srow < 0) return make_uint4(0u, 0u, 0u, 0u);
+  uint4 q = *reinterpret_cast<const uint4*>(src + srow * a.lds + c);
+  if (a.scale) {
+    const float s = a.scale[r];
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)f32_to_bf16(__uint_as_float(w[j] << 16) * s) |
+             ((uint32_t)f32_to_bf16(__uint_as_float(w[j] & 0xFFFF0000u) * s) << 16);
+    q = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return q;
+}
+
 __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
-  __shared__ uint16_t tile[64][64 + 8];
+  __shared__ uint32_t tile[64][33];
   const int64_t b = blockIdx.z;
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const uint16_t* src = a.src + b * a.src_bstride;
   uint16_t* dst = a.dst + b * a.dst_bstride;
   const int tid = threadIdx.x;
+  {
+    const int p = tid >> 3, cl = (tid & 7) * 8;
+    const uint4 q0 = load_row8(a, src, r0 + 2 * p, c0 + cl);
+    const uint4 q1 = load_row8(a, src, r0 + 2 * p + 1, c0 + cl);
+    const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w}, w1[4] = {q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int v = tid + 256 * i;          // 512 vectors of 8 along c
-    const int rl = v >> 3, cl = (v & 7) * 8;
-    const int r = r0 + rl, c = c0 + cl;
-    uint4 q = make_uint4(0u, 0u, 0u, 0u);
-    if (r < a.R && c < a.C) {
-      const int64_t srow = a.gather ? (int64_t)a.gather[r] : r;
-      if (srow >= 0) {
-        q = *reinterpret_cast<const uint4*>(src + srow * a.lds + c);
-        if (a.scale) {
-          const float s = a.scale[r];
-          uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            w[j] = (uint32_t)f32_to_bf16(__uint_as_float(w[j] << 16) * s) |
-                   ((uint32_t)f32_to_bf16(__uint_as_float(w[j] & 0xFFFF0000u) * s) << 16);
-          q = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      tile[cl + 2 * j][p] = (w0[j] & 0xFFFFu) | (w1[j] << 16);
+      tile[cl + 2 * j + 1][p] = (w0[j] >> 16) | (w1[j] & 0xFFFF0000u);
     }
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[rl][cl + j] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int v = tid + 256 * i;          // 512 vectors of 8 along r
-    const int cl = v >> 3, rl = (v & 7) * 8;
-    const int r = r0 + rl, c = c0 + cl;
-    if (c < a.C && r < a.R) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)tile[rl + 2 * j][cl] | ((uint32_t)tile[rl + 2 * j + 1][cl] << 16);
-      *reinterpret_cast<uint4*>(dst + (int64_t)c * a.ldd + a.off + r) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    const int v = tid + 256 * i;          // 512 stores of 8 rows
+    const int cl = v >> 3, rg = v & 7;
+    const int r = r0 + 8 * rg, c = c0 + cl;
+    if (c < a.C && r < a.R)
+      *reinterpret_cast<uint4*>(dst + (int64_t)c * a.ldd + a.off + r) =
+          make_uint4(tile[cl][4 * rg], tile[cl][4 * rg + 1], tile[cl][4 * rg + 2], tile[cl][4 * rg + 3]);
   }
 }
 
