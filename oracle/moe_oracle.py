@@ -45,6 +45,11 @@ R13 group limit (the page's cross-node all-to-all section caps every token at 4 
     the topk_groups best groups (ties to the lower group index) stay eligible and
     the K_r picks follow R2 among their experts.  Parity of this rule is pinned by
     a hand-worked example and by invariants only.
+R15 sequence-wise balance loss (the page adds "a tiny sequence-level balance loss,
+    alpha = 0.0001" to the bias rule and prints no formula; the reading here, parity
+    unpinned beyond alpha): for each sequence of L consecutive tokens,
+    f_i = N_r / (K_r L) * (number of the sequence's picks of expert i),
+    P_i = (1/L) sum_t s_{i,t} / sum_j s_{j,t},  loss = alpha * sum_i f_i P_i.
 R14 backward: gradients of L = <dout, h'> with the selection (idx) held fixed, as the Topk
     is piecewise constant; the bias gets no gradient (it never enters a gate); the
     gate path is differentiated through the unbiased s of the gate equation with s
@@ -209,6 +214,22 @@ def layer_forward(u, idx, gate, routed, shared, ffn=swiglu_ffn, x=None) -> np.nd
         wg, wu, wd = routed(int(e))
         out[rows] += gate[rows, slots][:, None] * ffn(x[rows], wg, wu, wd)
     return out
+
+
+def seq_balance_loss(s, idx, seq_len: int, alpha: float = 1e-4) -> np.ndarray:
+    """R15: one loss per sequence of seq_len consecutive tokens, float64."""
+    s = np.asarray(s, dtype=np.float64)
+    idx = np.asarray(idx)
+    t_n, n = s.shape
+    k = idx.shape[1]
+    out = []
+    for q in range(t_n // seq_len):
+        rows = slice(q * seq_len, (q + 1) * seq_len)
+        counts = np.bincount(idx[rows].ravel(), minlength=n).astype(np.float64)
+        f = counts * n / (k * seq_len)
+        p = (s[rows] / s[rows].sum(axis=1, keepdims=True)).mean(axis=0)
+        out.append(alpha * float(np.sum(f * p)))
+    return np.array(out)
 
 
 def affinity64(u, centroids) -> np.ndarray:

@@ -87,3 +87,32 @@ def test_route_grouped_gates_from_unbiased_s():
     np.testing.assert_allclose(gate, sel / sel.sum(1, keepdims=True), rtol=0, atol=1e-15)
     assert np.array_equal(load, np.bincount(idx.ravel(), minlength=16))
     assert all(len(set((r // 4).tolist())) <= 2 for r in idx)
+
+
+# ----------------------------------------------------------------------------- balance loss (R15)
+
+def test_seq_balance_hand_worked(golden_dir):
+    d = json.load(open(os.path.join(golden_dir, "seq_balance.json")))
+    s = np.array([[float(v) for v in r] for r in d["s"]])
+    loss = O.seq_balance_loss(s, np.array(d["idx"]), d["seq_len"], d["alpha"])
+    np.testing.assert_allclose(loss, [float(v) for v in d["loss"]], rtol=1e-14)
+
+
+def test_seq_balance_uniform_picks_give_alpha():
+    # every expert picked equally often in each sequence: f_i = 1, and sum_i P_i = 1 always
+    rng = np.random.default_rng(2)
+    n, k, L = 8, 2, 12
+    s = rng.random((3 * L, n)) + 0.01
+    idx = np.array([[(2 * t) % n, (2 * t + 1) % n] for t in range(3 * L)])
+    np.testing.assert_allclose(O.seq_balance_loss(s, idx, L, 0.5), 0.5, rtol=1e-13)
+
+
+def test_seq_balance_collapsed_routing():
+    # all tokens pick experts {0, 1}: f = N/K on them, so loss = alpha N/K (P_0 + P_1)
+    rng = np.random.default_rng(3)
+    n, k, L = 16, 2, 10
+    s = rng.random((L, n)) + 0.01
+    idx = np.tile([0, 1], (L, 1))
+    sn = s / s.sum(1, keepdims=True)
+    want = 1e-4 * n / k * (sn[:, 0].mean() + sn[:, 1].mean())
+    np.testing.assert_allclose(O.seq_balance_loss(s, idx, L), [want], rtol=1e-13)
