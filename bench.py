@@ -194,6 +194,22 @@ def main():
         route_grouped = {"n_groups": 8, "topk_groups": 4,
                          "route_ms": round(ev_r[0].elapsed_time(ev_r[1]) / reps, 4),
                          "route_grouped_ms": round(ev_r[1].elapsed_time(ev_r[2]) / reps, 4)}
+    # routing plus the sequence-wise balance statistic (sequences of up to 4096 tokens)
+    route_balance = None
+    seq = min(T, 4096)
+    if T % seq == 0:
+        bl = torch.empty((T // seq,), dtype=torch.float32, device="cuda")
+        bidx, bgate, bload = torch.empty_like(idx), torch.empty_like(gate), torch.empty_like(load)
+        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        moe.moe_route_balance(shape, seq, 1e-4, dev["u"], dev["centroids"], bias, bidx, bgate, bload, bl, ws, stream)
+        ev_s[0].record(stream)
+        for _ in range(10):
+            moe.moe_route_balance(shape, seq, 1e-4, dev["u"], dev["centroids"], bias, bidx, bgate, bload, bl, ws,
+                                  stream)
+        ev_s[1].record(stream)
+        torch.cuda.synchronize()
+        route_balance = {"seq_len": seq, "route_balance_ms": round(ev_s[0].elapsed_time(ev_s[1]) / 10, 4),
+                         "loss_first_sequences": [round(float(x), 8) for x in bl[:4].cpu()]}
 
     # layer backward (bf16): gradients of <dout, h'> for the routing of the last step, timed on its own
     backward = None
@@ -278,6 +294,7 @@ def main():
                         "frac": round(combine_bytes / (float(st[:, 5].mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "load_max_over_mean": ratios,
         "route_grouped": route_grouped,
+        "route_balance": route_balance,
         "backward": backward,
         "wall_s_timed": round(t_wall, 3),
         "cpu_baseline": None,

@@ -124,6 +124,19 @@ moe_status moe_route_grouped(const moe_shape* shape, int32_t n_groups, int32_t t
                              int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* moe_route plus the sequence-wise balance statistic.  The page (方法 §2, last paragraph) adds
+ * a tiny sequence-level balance loss (alpha = 0.0001) to the bias rule and prints no formula;
+ * the reading here: for each of the T / seq_len sequences of consecutive tokens,
+ *   f_i = N_r / (K_r seq_len) * (the sequence's picks of expert i),
+ *   P_i = mean over the sequence's tokens of s_{i,t} / sum_j s_{j,t},
+ *   seq_loss[q] = alpha * sum_i f_i P_i          (fp32 out, [T / seq_len]).
+ * Routing outputs as in moe_route.  Errors: MOE_ERR_INVALID_ARG unless 1 <= seq_len <= 16384
+ * divides T and seq_loss is non-null (plus moe_route's checks); nothing is launched then. */
+moe_status moe_route_balance(const moe_shape* shape, int32_t seq_len, float alpha, const void* u,
+                             const float* centroids, const float* bias, int32_t* topk_idx,
+                             float* topk_gate, int32_t* expert_load, float* seq_loss,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Expert half of the layer (方法 §2, the h'_t equation): permutes tokens into per-expert
  * segments, runs every routed expert on its tokens and every shared expert on all tokens
  * (grouped SwiGLU GEMMs), and combines out_t = u_t + sum_s FFN_s(u_t) + sum_k gate FFN(u_t).

@@ -63,6 +63,8 @@ _SIG = {
     "moe_update_bias": [ctypes.c_int32, ctypes.c_int64, _P, _P, ctypes.c_float, _P],
     "moe_quantize_weights": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
     "moe_quantize_act": [ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
+    "moe_route_balance": [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P,
+                          ctypes.c_size_t, _P],
     "moe_backward_workspace_size": [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)],
     "moe_backward": [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(Weights), _P, _P, _P, _P, _P,
                      ctypes.POINTER(WeightGrads), _P, ctypes.c_size_t, _P],
@@ -104,6 +106,13 @@ def make_weights(w_gate, w_up, w_down, sh_gate=None, sh_up=None, sh_down=None, s
     for k, t in (scales or {}).items():
         setattr(w, k, t.data_ptr() if t is not None else None)
     return w
+
+
+def moe_route_balance(shape, seq_len, alpha, u, centroids, bias, topk_idx, topk_gate, expert_load, seq_loss,
+                      workspace, stream=None):
+    _check("moe_route_balance", _lib.moe_route_balance(
+        ctypes.byref(shape), seq_len, ctypes.c_float(alpha), _ptr(u), _ptr(centroids), _ptr(bias), _ptr(topk_idx),
+        _ptr(topk_gate), _ptr(expert_load), _ptr(seq_loss), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def make_weight_grads(w_gate, w_up, w_down, sh_gate=None, sh_up=None, sh_down=None) -> WeightGrads:

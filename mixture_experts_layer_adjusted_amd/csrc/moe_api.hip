@@ -51,7 +51,7 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.route_e_hi = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
   p.route_e_mid = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
   p.route_e_lo = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
-  p.route_scores = take(mfma_route ? (size_t)T * N * 4 : 0);
+  p.route_scores = take((size_t)T * N * 4);   // the fp32 path writes it only for the balance statistic
   p.route_bytes = o;
   o = 0;
   p.chunk_counts = take((size_t)p.chunks * N * 4);
@@ -213,7 +213,7 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
 
 static moe_status route_impl(const moe_shape* shape, GroupLimit gl, const void* u, const float* centroids,
                              const float* bias, int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream, bool keep_scores = false) {
   moe_status rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!expert_load) return MOE_ERR_INVALID_ARG;
@@ -225,6 +225,8 @@ static moe_status route_impl(const moe_shape* shape, GroupLimit gl, const void* 
   RouteWorkspace rw{reinterpret_cast<int32_t*>(wsb + p.route_partial), reinterpret_cast<uint16_t*>(wsb + p.route_e_hi),
                     reinterpret_cast<uint16_t*>(wsb + p.route_e_mid), reinterpret_cast<uint16_t*>(wsb + p.route_e_lo),
                     reinterpret_cast<float*>(wsb + p.route_scores)};
+  // the MFMA path always stages the affinities there; the fp32 path only when asked
+  if (!keep_scores && !route_uses_mfma(*shape)) rw.scores = nullptr;
   return hip_status(launch_route(*shape, u, centroids, bias, gl, topk_idx, topk_gate, expert_load, rw, stream));
 }
 
@@ -245,6 +247,23 @@ moe_status moe_route_grouped(const moe_shape* shape, int32_t n_groups, int32_t t
   if ((int64_t)topk_groups * (shape->n_routed / n_groups) < shape->top_k) return MOE_ERR_INVALID_ARG;
   return route_impl(shape, GroupLimit{n_groups, topk_groups}, u, centroids, bias, topk_idx, topk_gate, expert_load,
                     workspace, workspace_bytes, stream);
+}
+
+moe_status moe_route_balance(const moe_shape* shape, int32_t seq_len, float alpha, const void* u,
+                             const float* centroids, const float* bias, int32_t* topk_idx, float* topk_gate,
+                             int32_t* expert_load, float* seq_loss, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  moe_status rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (seq_len < 1 || seq_len > 16384 || shape->tokens % seq_len != 0) return MOE_ERR_INVALID_ARG;
+  if (shape->tokens > 0 && !seq_loss) return MOE_ERR_INVALID_ARG;
+  if ((rc = route_impl(shape, GroupLimit{1, 1}, u, centroids, bias, topk_idx, topk_gate, expert_load, workspace,
+                       workspace_bytes, stream, true)) != MOE_OK)
+    return rc;
+  if (shape->tokens == 0) return MOE_OK;
+  const WorkspacePlan p = plan_workspace(*shape);
+  const float* scores = reinterpret_cast<const float*>(static_cast<char*>(workspace) + p.route_scores);
+  return hip_status(launch_seq_balance(*shape, seq_len, alpha, scores, topk_idx, seq_loss, stream));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* u, const moe_weights* weights, const int32_t* topk_idx,

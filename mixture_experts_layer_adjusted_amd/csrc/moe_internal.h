@@ -82,6 +82,10 @@ hipError_t launch_route(const moe_shape& s, const void* u, const float* centroid
                         GroupLimit gl, int32_t* idx, float* gate, int32_t* load, const RouteWorkspace& w,
                         hipStream_t st);
 
+// per-sequence balance statistic from the affinities the routing call wrote to the workspace
+hipError_t launch_seq_balance(const moe_shape& s, int seq_len, float alpha, const float* scores, const int32_t* idx,
+                              float* loss, hipStream_t st);
+
 hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const WorkspacePlan& p, char* ws,
                           hipStream_t st);
 

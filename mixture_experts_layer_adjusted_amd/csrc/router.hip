@@ -109,7 +109,8 @@ template <int CPL, typename TIn>
 __global__ void __launch_bounds__(kThreads) route_kernel(const TIn* __restrict__ u, const float* __restrict__ E,
                                                          const float* __restrict__ bias, int T, int d, int N, int K,
                                                          GroupLimit gl, int32_t* __restrict__ idx_out,
-                                                         float* __restrict__ gate_out, int32_t* __restrict__ partial) {
+                                                         float* __restrict__ gate_out, int32_t* __restrict__ partial,
+                                                         float* __restrict__ s_out) {
   __shared__ float Us[kSlice][kRouteTokens + 1];
   __shared__ uint32_t gmax[kThreads / 64][64];
   __shared__ float Es[kSlice][kEsPitch];
@@ -178,6 +179,12 @@ __global__ void __launch_bounds__(kThreads) route_kernel(const TIn* __restrict__
   }
   for (int q = tid; q < kRouteTokens * kMaxTopK; q += kThreads) picks[q] = -1;
   __syncthreads();
+  if (s_out) {   // the affinities of the workgroup's tokens, for the balance statistic
+    for (int q = tid; q < kRouteTokens * N; q += kThreads) {
+      const int tt = q / N, e = q % N;
+      if (t0 + tt < T) s_out[(int64_t)(t0 + tt) * N + e] = S[tt][e];
+    }
+  }
 
   // top-K: one wavefront per token
   const int lane = tid & 63;
@@ -489,12 +496,12 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
 template <typename TIn>
 hipError_t launch_route_t(const moe_shape& s, const TIn* u, const float* centroids, const float* bias,
                           GroupLimit gl, int32_t* idx, float* gate, int32_t* load, int32_t* partial, int64_t blocks,
-                          hipStream_t st) {
+                          float* s_out, hipStream_t st) {
   const int N = s.n_routed;
   dim3 grid((unsigned)blocks), block(kThreads);
 #define MOE_ROUTE_CASE(C)                                                                                  \
   hipLaunchKernelGGL((route_kernel<C, TIn>), grid, block, 0, st, u, centroids, bias, s.tokens, s.hidden, N, \
-                     s.top_k, gl, idx, gate, partial)
+                     s.top_k, gl, idx, gate, partial, s_out)
   if (N <= 64) MOE_ROUTE_CASE(1);
   else if (N <= 128) MOE_ROUTE_CASE(2);
   else if (N <= 256) MOE_ROUTE_CASE(4);
@@ -561,9 +568,76 @@ hipError_t launch_route(const moe_shape& s, const void* u, const float* centroid
   }
   if (s.dtype == MOE_DTYPE_F32)
     return launch_route_t(s, static_cast<const float*>(u), centroids, bias, gl, idx, gate, load, partial, blocks,
-                          st);
+                          w.scores, st);
   return launch_route_t(s, static_cast<const uint16_t*>(u), centroids, bias, gl, idx, gate, load, partial, blocks,
-                        st);
+                        w.scores, st);
+}
+
+namespace {
+
+// Sequence-wise balance statistic, one workgroup per sequence of L tokens (the reading of the
+// page's "tiny sequence-level balance loss"): loss = alpha * sum_i f_i P_i with
+// f_i = N_r / (K_r L) * (the sequence's picks of expert i) and P_i = (1/L) sum_t s_{i,t} / S_t,
+// S_t = sum_j s_{j,t}.  Picks are counted with LDS increments (exact); every float sum runs in a
+// fixed order (per-lane strided sums, a fixed tree, then token order), so the result is the
+// same on every run.
+__global__ void __launch_bounds__(256) seq_balance_kernel(const float* __restrict__ s, const int32_t* __restrict__ idx,
+                                                          int N, int K, int L, float alpha,
+                                                          float* __restrict__ loss) {
+  extern __shared__ float dyn[];
+  float* St = dyn;                                          // [L]
+  int32_t* cnt = reinterpret_cast<int32_t*>(dyn + L);       // [N]
+  __shared__ float red[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * L;
+  for (int e = tid; e < N; e += 256) cnt[e] = 0;
+  __syncthreads();
+  for (int q = tid; q < L * K; q += 256) {
+    const int e = idx[t0 * K + q];
+    if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
+  }
+  for (int t = wave; t < L; t += 4) {
+    const float* row = s + (t0 + t) * N;
+    float v = 0.0f;
+    for (int e = lane; e < N; e += 64) v += row[e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) St[t] = v;
+  }
+  __syncthreads();
+  float term = 0.0f;
+  for (int e = tid; e < N; e += 256) {
+    float p = 0.0f;
+    for (int t = 0; t < L; ++t) p += s[(t0 + t) * N + e] / St[t];
+    const float f = (float)cnt[e] * (float)N / ((float)K * (float)L);
+    term += f * (p / (float)L);
+  }
+  red[tid] = term;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) loss[blockIdx.x] = alpha * red[0];
+}
+
+}  // namespace
+
+hipError_t launch_seq_balance(const moe_shape& s, int seq_len, float alpha, const float* scores, const int32_t* idx,
+                              float* loss, hipStream_t st) {
+  const int64_t n_seq = s.tokens / seq_len;
+  if (n_seq == 0) return hipSuccess;
+  const size_t lds = (size_t)seq_len * 4 + (size_t)s.n_routed * 4;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&seq_balance_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 65536 + 4 * kMaxRouted);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(seq_balance_kernel, dim3((unsigned)n_seq), dim3(256), lds, st, scores, idx, s.n_routed, s.top_k,
+                     seq_len, alpha, loss);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -88,6 +88,11 @@ def test_null_and_workspace_errors_before_launch():
     for ng, mg in ((0, 1), (4, 5), (4, 0), (3, 1), (65, 1), (16, 1)):
         rc = lib.moe_route_grouped(ctypes.byref(s), ng, mg, fake, fake, fake, fake, fake, fake, fake, big, None)
         assert rc == 1, (ng, mg)
+    # balance statistic: sequence length must divide T
+    for L in (0, 7, 20000):
+        rc = lib.moe_route_balance(ctypes.byref(s), L, ctypes.c_float(1e-4), fake, fake, fake, fake, fake, fake, fake,
+                                   fake, big, None)
+        assert rc == 1, L
     # backward: bf16 with d, I multiples of 128 only; null pointers, aliasing and a short workspace
     wg = moe.WeightGrads(0x3000, 0x3000, 0x3000, 0x3000, 0x3000, 0x3000)
     sb = moe.make_shape(64, 256, 16, 4, 1, 128, moe.MOE_DTYPE_BF16)

@@ -84,3 +84,35 @@ def test_grouped_routing_feeds_the_forward():
     y_ref = O.layer_forward(hf["u"], idx, O.gates(s, idx), O.stacked(hf["w_gate"], hf["w_up"], hf["w_down"]), shared)
     e_all, e_exp = rel_err(to_host_f32(r.out), y_ref, hf["u"])
     assert e_all <= TOL["bf16"] and e_exp <= TOL["bf16"], (e_all, e_exp)
+
+
+# ----------------------------------------------------------------------------- balance statistic (R15)
+
+@pytest.mark.parametrize("cid,seq_len", [(0, 16), (1, 1024), (1, 4096), (2, 64)])
+def test_seq_balance_parity(cid, seq_len):
+    cfg = CONFIGS[cid]
+    print(f"balance statistic: config {cid}, sequences of {seq_len}", flush=True)
+    h = host.make_host_inputs(cfg, with_weights=False)
+    dev = host_to_device(h)
+    shape = shape_of(cfg)
+    ws = torch.empty(max(moe.moe_workspace_size(shape), 1), dtype=torch.uint8, device="cuda")
+    T, K, N = cfg.tokens, cfg.top_k, cfg.n_routed
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    load = torch.empty((N,), dtype=torch.int32, device="cuda")
+    loss = torch.empty((T // seq_len,), dtype=torch.float32, device="cuda")
+    moe.moe_route_balance(shape, seq_len, 1e-4, dev["u"], dev["centroids"], dev["bias"], idx, gate, load, loss, ws)
+    torch.cuda.synchronize()
+    hf = {k: _f(v) for k, v in h.items()}
+    s = O.affinity(hf["u"], hf["centroids"])
+    want = O.seq_balance_loss(s, idx.cpu().numpy(), seq_len, 1e-4)
+    got = loss.cpu().numpy().astype(np.float64)
+    print("loss per sequence (first 4):", got[:4], "oracle:", want[:4])
+    np.testing.assert_allclose(got, want, rtol=2e-5, atol=0)
+    # the routing it returns is moe_route's
+    idx2 = torch.empty_like(idx)
+    gate2 = torch.empty_like(gate)
+    load2 = torch.empty_like(load)
+    moe.moe_route(shape, dev["u"], dev["centroids"], dev["bias"], idx2, gate2, load2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(gate, gate2) and torch.equal(load, load2)
