@@ -538,33 +538,52 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   }
 }
 
+template <int EPI, int SBK, int SW, int SR, int SG, int SM, int STM>
+hipError_t launch_stream(const GemmOperands& g, hipStream_t st) {
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
+  using SC = StreamCfg<SBK, SW, SR, SG, STM>;
+  const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
+  const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
+  auto kern = &grouped_gemm_bf16_stream_kernel<EPI, SBK, SW, SR, SG, SM, STM>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  const int64_t tiles = EPI == 3 ? (int64_t)g.n_seg * ceil_div(g.wg_m, STM) * NT
+                                 : (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
+  const int64_t span = kXcds * SC::kXcdChunk;
+  const int64_t grid = ceil_div(tiles, span) * span;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SC::kThreads), lds_bytes, st, g, NT);
+  return hipGetLastError();
+}
+
+#ifndef MOE_SMALL_SEGMENT_TILE
+#define MOE_SMALL_SEGMENT_TILE 1
+#endif
+
 template <int EPI>
 hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
-  constexpr int SBK = MOE_STREAM_BK, SW = MOE_STREAM_WAVES, SR = MOE_STREAM_WROWS, SG = MOE_STREAM_WGS;
-  constexpr int SM = MOE_STREAM_WM, STM = MOE_STREAM_TM;
-  using SC = StreamCfg<SBK, SW, SR, SG, STM>;
+  constexpr int SBK = MOE_STREAM_BK;
   // the streaming kernel addresses its sources with 32-bit byte offsets
   const bool offsets_fit =
       EPI == 3 ? (int64_t)g.wg_m * g.lda * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.ldw * 2 < (int64_t(1) << 32)
                : g.act_rows * g.K * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.K * 2 < (int64_t(1) << 32);
   if (g.K % SBK == 0 && offsets_fit) {
-    const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
-    const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
-    auto kern = &grouped_gemm_bf16_stream_kernel<EPI, SBK, SW, SR, SG, SM, STM>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-      if (err != hipSuccess) return err;
-      attr_set = true;
+    if constexpr (EPI >= 2) {
+      // backward modes: 256 x 256 tiles (the SwiGLU-backward epilogue assumes four wavefronts
+      // of one gate and one up block per row)
+      return launch_stream<EPI, 64, 8, 256, 1, 2, 256>(g, st);
+    } else {
+      // segments of a few rows (decode-like batches, expected routed rows per expert below one
+      // M-tile): 128-row tiles x 512 weight rows put 80% of every stage's loads on weights
+      if (MOE_SMALL_SEGMENT_TILE && g.small_segments) return launch_stream<EPI, 64, 8, 512, 1, 2, 128>(g, st);
+      return launch_stream<EPI, SBK, MOE_STREAM_WAVES, MOE_STREAM_WROWS, MOE_STREAM_WGS, MOE_STREAM_WM,
+                           MOE_STREAM_TM>(g, st);
     }
-    const int64_t tiles = EPI == 3 ? (int64_t)g.n_seg * ceil_div(g.wg_m, STM) * NT
-                                   : (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
-    const int64_t span = kXcds * SC::kXcdChunk;
-    const int64_t grid = ceil_div(tiles, span) * span;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SC::kThreads), lds_bytes, st, g, NT);
-    return hipGetLastError();
   }
   if (EPI >= 2) return hipErrorInvalidValue;   // the backward modes exist in the streaming kernel only
   const size_t lds_bytes = 2 * kStageElems * sizeof(uint16_t);

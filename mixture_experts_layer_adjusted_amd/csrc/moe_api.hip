@@ -165,6 +165,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.act_rows = s.tokens;
   g1.max_tiles = p.max_tiles;
   g1.max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + s.n_routed + s.n_shared) / 2);
+  g1.small_segments = (int64_t)s.tokens * s.top_k < (int64_t)kTileM * s.n_routed;
   g1.out = wsb + p.h;
   g1.out_scale = fp8 ? reinterpret_cast<float*>(wsb + p.h_scale) : nullptr;
   if ((rc = hip_status(launch_gemm_swiglu(s.dtype, g1, st))) != MOE_OK) return rc;
@@ -188,6 +189,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g2.act_rows = p.max_rows;
   g2.max_tiles = p.max_tiles;
   g2.max_pairs = g1.max_pairs;
+  g2.small_segments = g1.small_segments;
   g2.out = wsb + p.y;
   if ((rc = hip_status(launch_gemm_down(s.dtype, g2, st))) != MOE_OK) return rc;
   if (mark(4) != hipSuccess) return MOE_ERR_HIP;

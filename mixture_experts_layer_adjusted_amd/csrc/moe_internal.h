@@ -121,6 +121,9 @@ struct GemmOperands {
   // routed segments write out + e M N, shared ones out2 + (e - N_r) M N
   int64_t lda, ldw;
   int wg_m, n_seg;
+  // expected routed rows per expert (T K_r / N_r) below one M-tile: the bf16 forward GEMMs take
+  // 128-row tiles with more weight rows
+  bool small_segments;
 };
 
 // layer backward helpers (backward.hip)
