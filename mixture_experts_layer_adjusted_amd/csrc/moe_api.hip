@@ -52,6 +52,8 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.route_e_mid = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
   p.route_e_lo = take(mfma_route ? (size_t)n_pad * d * 2 : 0);
   p.route_scores = take((size_t)T * N * 4);   // the fp32 path writes it only for the balance statistic
+  const int splits = route_logit_splits(s);
+  p.route_zpart = take(splits > 1 ? (size_t)splits * T * N * 4 : 0);
   p.route_bytes = o;
   o = 0;
   p.chunk_counts = take((size_t)p.chunks * N * 4);
@@ -226,7 +228,7 @@ static moe_status route_impl(const moe_shape* shape, GroupLimit gl, const void* 
   char* wsb = static_cast<char*>(workspace);
   RouteWorkspace rw{reinterpret_cast<int32_t*>(wsb + p.route_partial), reinterpret_cast<uint16_t*>(wsb + p.route_e_hi),
                     reinterpret_cast<uint16_t*>(wsb + p.route_e_mid), reinterpret_cast<uint16_t*>(wsb + p.route_e_lo),
-                    reinterpret_cast<float*>(wsb + p.route_scores)};
+                    reinterpret_cast<float*>(wsb + p.route_scores), reinterpret_cast<float*>(wsb + p.route_zpart)};
   // the MFMA path always stages the affinities there; the fp32 path only when asked
   if (!keep_scores && !route_uses_mfma(*shape)) rw.scores = nullptr;
   return hip_status(launch_route(*shape, u, centroids, bias, gl, topk_idx, topk_gate, expert_load, rw, stream));

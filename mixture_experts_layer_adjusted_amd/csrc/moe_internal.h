@@ -28,6 +28,7 @@ struct WorkspacePlan {
   size_t route_partial;     // int32 [route_blocks, N_r]  per-workgroup pick counts
   size_t route_e_hi, route_e_mid, route_e_lo;  // bf16 [N_pad, d]  exact 3-way split of the centroids
   size_t route_scores;      // fp32 [T, N_r]  affinities s (MFMA path)
+  size_t route_zpart;       // fp32 [splits, T, N_r]  partial logits of a split contraction (small T)
   // forward
   size_t chunk_counts;      // int32 [chunks, N_r]
   size_t chunk_base;        // int32 [chunks, N_r]
@@ -66,11 +67,13 @@ struct RouteWorkspace {
   int32_t* partial;
   uint16_t *e_hi, *e_mid, *e_lo;
   float* scores;
+  float* zpart;
 };
 
 // ---- launchers (return hipSuccess or the launch error) ----
 bool route_uses_mfma(const moe_shape& s);
 int64_t route_mfma_blocks(const moe_shape& s);
+int route_logit_splits(const moe_shape& s);
 // group-limited selection: n_groups equal contiguous expert groups, picks only from the
 // topk_groups best groups (topk_groups >= n_groups: no limit)
 struct GroupLimit {

@@ -304,7 +304,8 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ ehi,
                                                             const uint16_t* __restrict__ emid,
                                                             const uint16_t* __restrict__ elo, int T, int d, int N,
-                                                            float* __restrict__ s_out) {
+                                                            float* __restrict__ s_out, int nk_per,
+                                                            float* __restrict__ z_part) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -349,12 +350,13 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
 #pragma unroll
       for (int v = 0; v < 16; ++v) zsum[a][b][v] = 0.0f;
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int nk = d / kLBK;
-  issue(0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // K-steps [kt0, kt1) of the contraction: all of it, or slice blockIdx.z when it is split
+  const int kt0 = blockIdx.z * nk_per, kt1 = min(d / kLBK, kt0 + nk_per);
+  if (kt0 < kt1) issue(kt0);   // a slice past the end contributes zeros
+  for (int kt = kt0; kt < kt1; ++kt) {
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();  // stage kt landed for every wave; stage kt-1 no longer read
-    if (kt + 1 < nk) issue(kt + 1);
+    if (kt + 1 < kt1) issue(kt + 1);
     const uint16_t* st = lds + (kt & 1) * kLStageElems;
     f32x16 acc[2][2];
 #pragma unroll
@@ -399,6 +401,13 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = e0 + wn * 64 + nb * 32 + q * 8 + khalf * 4;
+        if (z_part) {   // a slice's partial logits, summed in slice order by logit_reduce_kernel
+          float* zrow = z_part + ((int64_t)blockIdx.z * T + t) * N;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (e + v < N) zrow[e + v] = zsum[mb][nb][q * 4 + v];
+          continue;
+        }
         float4 o;
         o.x = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 0]));
         o.y = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 1]));
@@ -413,6 +422,15 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
             if (e + v < N) s_out[(int64_t)t * N + e + v] = ov[v];
         }
       }
+  }
+}
+
+// s = sigmoid(sum of the slices' partial logits, in slice order)
+__global__ void logit_reduce_kernel(const float* __restrict__ z_part, int splits, int64_t n, float* __restrict__ s_out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float z = 0.0f;
+    for (int q = 0; q < splits; ++q) z += z_part[q * n + i];
+    s_out[i] = 1.0f / (1.0f + expf(-z));
   }
 }
 
@@ -530,9 +548,18 @@ hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float*
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL(router_logits_kernel, dim3((unsigned)ceil_div(T, kLT), (unsigned)(npad / kLE)), dim3(256),
-                     lds_bytes, st, u, w.e_hi, w.e_mid, w.e_lo, T, d, N, w.scores);
+  const int splits = route_logit_splits(s);
+  const int nk = d / kLBK, nk_per = (int)ceil_div(nk, splits);
+  hipLaunchKernelGGL(router_logits_kernel, dim3((unsigned)ceil_div(T, kLT), (unsigned)(npad / kLE), (unsigned)splits),
+                     dim3(256), lds_bytes, st, u, w.e_hi, w.e_mid, w.e_lo, T, d, N, w.scores, nk_per,
+                     splits > 1 ? w.zpart : nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (splits > 1) {
+    const int64_t n = (int64_t)T * N;
+    hipLaunchKernelGGL(logit_reduce_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(n, 256), 2048)), dim3(256), 0, st,
+                       w.zpart, splits, n, w.scores);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   const int64_t blocks = ceil_div(T, kTopkTokens);
   dim3 grid((unsigned)blocks), block(kThreads);
 #define MOE_TOPK_CASE(C) \
@@ -551,6 +578,16 @@ hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float*
 
 bool route_uses_mfma(const moe_shape& s) {
   return s.dtype != MOE_DTYPE_F32 && s.hidden % kLBK == 0 && s.n_routed <= kMaxRouted;
+}
+
+// K slices of the MFMA logits: with few 128 x 128 tiles (small T) the contraction is split so
+// that about 256 workgroups run; the slices' partial sums are added in a fixed order
+int route_logit_splits(const moe_shape& s) {
+  if (!route_uses_mfma(s) || s.tokens == 0) return 1;
+  const int64_t tiles = ceil_div(s.tokens, kLT) * ceil_div(s.n_routed, kLE);
+  if (tiles >= 128) return 1;
+  const int64_t nk = s.hidden / kLBK;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({16, 256 / tiles, nk}));
 }
 
 int64_t route_mfma_blocks(const moe_shape& s) { return ceil_div(s.tokens, kTopkTokens); }
