@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true", help="skip the layer-backward timing (bf16 workloads)")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the measured reference peaks (plain copy, large library GEMMs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return p.parse_args()
@@ -91,6 +93,49 @@ def cpu_baseline(cfg, n_tokens):
             "sample": f"first {n_tokens} of the {cfg.tokens} tokens: float64 route + layer forward "
                       f"({len(np.unique(idx))} distinct routed experts), {wall:.1f} s; weight generation excluded",
             "seconds": round(wall, 2)}
+
+
+def measured_peaks(torch):
+    """Peaks measured on this GPU for context next to the published ones: a plain 1 GiB
+    device-to-device copy (torch's copy kernel) and large dense library GEMMs (hipBLASLt
+    through torch): bf16 8192^3, fp8 e4m3 8192^3 with per-tensor scales where torch offers it."""
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), 20)
+    out["copy_GBs"] = round(2 * 4 * n / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    b = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    ms = timed(lambda: torch.mm(a, b), 20)
+    out["gemm_bf16_8192_TFLOPs"] = round(2.0 * m ** 3 / (ms * 1e-3) / 1e12, 1)
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.t().contiguous().to(torch.float8_e4m3fn)
+        one = torch.ones((), dtype=torch.float32, device="cuda")
+        ms = timed(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 20)
+        out["gemm_fp8_8192_TFLOPs"] = round(2.0 * m ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a8, b8
+    except (RuntimeError, AttributeError, TypeError) as e:
+        out["gemm_fp8_8192_TFLOPs"] = None
+        out["gemm_fp8_note"] = str(e).splitlines()[0][:160]
+    del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -259,11 +304,49 @@ def main():
     flops_router = 2.0 * T * N * d
     flops_step = flops_router + flops_gemm1 + flops_gemm2
     g1_ms = float(st[:, 3].mean())
-    achieved = flops_gemm1 / (g1_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
     tok_s = T / (ms_step * 1e-3)
     elem = 4 if cfg.dtype == "f32" else 2
+    wbytes = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.dtype]
+    # experts that received rows, from the measured loads of each timed step
+    n_active = float(np.mean([(r > 0).sum() for r in ld])) + Ns
+    # gate/up GEMM bytes: the weights of every expert with rows (+ fp8 block scales), the
+    # gathered activation rows (+ fp8 row-tile scales) and the H rows written
+    g1_bytes = n_active * 2 * d * I * wbytes + rows * d * wbytes + rows * I * (1 if cfg.dtype == "fp8" else elem)
+    if cfg.dtype == "fp8":
+        g1_bytes += n_active * 2 * (d // 128) * (I // 128) * 4 + rows * (d // 128) * 4 + rows * (I // 128) * 4
+    t_mfma, t_hbm = flops_gemm1 / (peak * 1e12), g1_bytes / (HBM_PEAK_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(flops_gemm1 / (g1_ms * 1e-3) / 1e12, 2), "peak": peak,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(g1_bytes / (g1_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+
+    def hbm(nbytes, ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bytes": int(nbytes), "ms": round(ms, 4), "achieved_GBs": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    # algorithmic bytes of the memory-side stages (the row gather of the permutation is fused
+    # into the gate/up GEMM's loads, so the permutation itself only moves indices)
+    route_bytes = T * d * elem + N * d * 4 + N * 4 + T * K * 8 + N * 4
+    permute_bytes = T * K * 4 + N * 4 + 2 * rows * 4
+    quant_bytes = T * d * (elem + 1) + T * (d // 128) * 4
     combine_bytes = T * d * elem * (K + Ns + 2) + T * K * 8
+    hbm_stages = {"route": hbm(route_bytes, float(st[:, 0].mean())),
+                  "permute": hbm(permute_bytes, float(st[:, 1].mean())),
+                  "combine": hbm(combine_bytes, float(st[:, 5].mean()))}
+    if cfg.dtype == "fp8":
+        hbm_stages["quantize_act"] = hbm(quant_bytes, float(st[:, 2].mean()))
+    route_ms = float(st[:, 0].mean())
+    # the logit contraction runs as three bf16 MFMA products (hi, mid, lo parts of the centroids)
+    route_compute = {"flops_fp32_equivalent": flops_router,
+                     "tflops_executed_bf16": round(3 * flops_router / (route_ms * 1e-3) / 1e12, 1),
+                     "mfma_bf16_frac": round(3 * flops_router / (route_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+                                             4)} if cfg.dtype != "f32" else None
+    step_ms_all = [events[i][0].elapsed_time(events[i][7]) for i in range(args.steps)]
     result = {
         "metric": "MoE layer fwd tokens/sec at V3 shape (T=16384); % of MFMA peak",
         "workload_note": None if args.workload == "v3-prefill-bf16-zipf" else
@@ -274,6 +357,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(float(np.median(step_ms_all)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -283,22 +367,27 @@ def main():
                    "inter": I, "step": "moe_route + moe_forward + moe_update_bias"},
         "tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
         "mfma_peak_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / peak, 4),
-        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", **roof,
                      "traffic": measured_traffic(args.workload),
-                     "avg_ms": round(g1_ms, 4), "flops_per_launch": flops_gemm1},
+                     "avg_ms": round(g1_ms, 4), "flops_per_launch": flops_gemm1,
+                     "algorithmic_bytes_per_launch": int(g1_bytes),
+                     "mfma_bound_ms": round(t_mfma * 1e3, 4), "hbm_bound_ms": round(t_hbm * 1e3, 4),
+                     "experts_with_rows": round(n_active, 1)},
         "stages_ms": stage_ms,
         "gemm_down": {"achieved_tflops": round(flops_gemm2 / (float(st[:, 4].mean()) * 1e-3) / 1e12, 2),
                       "frac": round(flops_gemm2 / (float(st[:, 4].mean()) * 1e-3) / 1e12 / peak, 4)},
-        "combine_hbm": {"achieved_GBs": round(combine_bytes / (float(st[:, 5].mean()) * 1e-3) / 1e9, 1),
-                        "frac": round(combine_bytes / (float(st[:, 5].mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "hbm_stages": hbm_stages,
+        "route_compute": route_compute,
         "load_max_over_mean": ratios,
         "route_grouped": route_grouped,
         "route_balance": route_balance,
         "backward": backward,
         "wall_s_timed": round(t_wall, 3),
+        "measured_peaks": None,
         "cpu_baseline": None,
     }
+    if not args.no_peaks:
+        result["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

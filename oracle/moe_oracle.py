@@ -54,6 +54,20 @@ R14 backward: gradients of L = <dout, h'> with the selection (idx) held fixed, a
     is piecewise constant; the bias gets no gradient (it never enters a gate); the
     gate path is differentiated through the unbiased s of the gate equation with s
     evaluated in float64 (no fp32 rounding, so that finite differences can pin it).
+R16 FP8 backward (the page's FP8 paragraph names the forward GEMM and both backward
+    GEMMs, input gradient and weight gradient, as FP8 and fixes only the tile and block
+    shapes): a weight operand is quantised per 128x128 block of its stored matrix, so a
+    transposed weight carries the transposed codes and scales; every other operand per
+    1x128 tile along that GEMM's contraction axis: u and dout along d, [dA dB] along 2I
+    for the input-gradient products, and, for the weight-gradient products, whose
+    contraction runs over an expert's rows, along those rows taken in token order in runs
+    of 128 (the last run zero-padded).  A tensor is quantised from the precision it is held
+    in between two steps, the same on both sides so that equal inputs give equal codes:
+    u, dout and the stored H, dA, dB and dH (= dout W_down before the gate) in bf16,
+    gate * dout in fp32.  Gates, the router and the residual are not quantised (R14).
+    Parity of this reading is pinned by its reduction to R14 with every quantiser and
+    rounding replaced by the identity, by exact scaling under powers of two, and by the
+    distance to R14 that the E4M3 grid allows.
 """
 from __future__ import annotations
 
@@ -417,3 +431,132 @@ def layer_forward_fp8(u, idx, gate, routed_q, shared_q) -> np.ndarray:
     u32 = np.asarray(u, dtype=np.float32)
     x = dequant_act(*quantize_act_1x128(u32))
     return layer_forward(u32, idx, gate, routed_q, shared_q, ffn=swiglu_ffn_fp8, x=x)
+
+
+# ----------------------------------------------------------------------------- FP8 backward (R16)
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (nearest, ties to even) through fp32, returned as float64."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    r = (((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def quantize_runs_of_rows(x: np.ndarray) -> np.ndarray:
+    """Fake-quantise [rows, C] along the rows: each column is cut into runs of 128 consecutive
+    rows (the last run zero-padded), and each run is one 1x128 tile of R8.  Returns the
+    dequantised values, float64 [rows, C]."""
+    x32 = np.asarray(x, dtype=np.float32)
+    r, c = x32.shape
+    rp = -(-r // 128) * 128
+    t = np.zeros((c, rp), dtype=np.float32)
+    t[:, :r] = x32.T
+    return dequant_act(*quantize_act_1x128(t))[:, :r].T
+
+
+class ExactPolicy:
+    """Every quantiser and storage rounding of R16 replaced by the identity: the steps of
+    layer_backward_steps then state the R14 backward."""
+
+    @staticmethod
+    def tiles(x):          # 1x128 tiles along the last axis
+        return np.asarray(x, dtype=np.float64)
+
+    @staticmethod
+    def runs(x):           # runs of 128 rows
+        return np.asarray(x, dtype=np.float64)
+
+    @staticmethod
+    def held(x):           # storage between steps
+        return np.asarray(x, dtype=np.float64)
+
+    @staticmethod
+    def scaled(g, x):      # gate * dout
+        return np.asarray(g, dtype=np.float64)[:, None] * np.asarray(x, dtype=np.float64)
+
+
+class Fp8Policy:
+    """The quantisers and storage precisions of R16."""
+
+    @staticmethod
+    def tiles(x):
+        return dequant_act(*quantize_act_1x128(np.asarray(x, dtype=np.float32)))
+
+    runs = staticmethod(quantize_runs_of_rows)
+    held = staticmethod(bf16_round)
+
+    @staticmethod
+    def scaled(g, x):      # one fp32 product per element
+        return (np.asarray(g, dtype=np.float32)[:, None] * np.asarray(x, dtype=np.float32)).astype(np.float64)
+
+
+def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
+    """The R14 backward taken step by step, each GEMM operand passed through policy q (R16).
+
+    routed(e) / shared[i] give float64 (w_gate [I, d], w_up [I, d], w_down [d, I]); for the FP8
+    backward these are the dequantised 128x128-block weights.  Per expert, with its rows in
+    token order and gate column g (1 for a shared expert), x = tiles(u), dy = tiles(dout):
+      a = x Wg^T, b = x Wu^T, dH = held(dy Wd), h = SiLU(a) b, dg = sum dH h,
+      dA = held(g dH b SiLU'(a)), dB = held(g dH SiLU(a)), dx = tiles([dA dB]) [Wg; Wu],
+      dWd = runs(scaled(g, dout))^T runs(held(h)), dWg = runs(dA)^T runs(u), dWu = runs(dB)^T runs(u).
+    The router part and the residual follow layer_backward.  Returns the same tuple.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    e = np.asarray(centroids, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    idx = np.asarray(idx)
+    t_n, k_n = idx.shape
+    s = affinity64(u, e)
+    ssel = np.take_along_axis(s, idx, axis=1)
+    ssum = ssel.sum(axis=1, keepdims=True)
+    gate = ssel / ssum
+    xq = q.tiles(u)
+    dyq = q.tiles(dout)
+
+    def expert(rows, g, wg, wu, wd):
+        wg, wu, wd = (np.asarray(w, dtype=np.float64) for w in (wg, wu, wd))
+        x = xq[rows]
+        a = x @ wg.T
+        b = x @ wu.T
+        dh_pre = q.held(dyq[rows] @ wd)
+        sg = 1.0 / (1.0 + np.exp(-a))
+        h = a * sg * b
+        dg = np.sum(dh_pre * h, axis=1)
+        dh = g[:, None] * dh_pre
+        da = q.held(dh * b * sg * (1.0 + a * (1.0 - sg)))
+        db = q.held(dh * a * sg)
+        dx = q.tiles(np.concatenate([da, db], axis=1)) @ np.concatenate([wg, wu], axis=0)
+        uo = q.runs(u[rows])
+        dwd = q.runs(q.scaled(g, dout[rows])).T @ q.runs(q.held(h))
+        return dx, dg, (q.runs(da).T @ uo, q.runs(db).T @ uo, dwd)
+
+    du = dout.copy()
+    d_shared = []
+    all_rows = np.arange(t_n)
+    for wg, wu, wd in shared:
+        dx, _, grads = expert(all_rows, np.ones(t_n), wg, wu, wd)
+        du += dx
+        d_shared.append(grads)
+    dg = np.zeros((t_n, k_n))
+    d_routed = {}
+    for ex in np.unique(idx):
+        rows, slots = np.nonzero(idx == ex)          # rows ascend: token order
+        dx, dg_e, grads = expert(rows, gate[rows, slots], *routed(int(ex)))
+        dg[rows, slots] = dg_e
+        du[rows] += dx
+        d_routed[int(ex)] = grads
+    ds = dg / ssum - np.sum(dg * ssel, axis=1, keepdims=True) / ssum ** 2
+    dz = ds * ssel * (1.0 - ssel)
+    de = np.zeros_like(e)
+    for k in range(k_n):
+        du += dz[:, k:k + 1] * e[idx[:, k]]
+        np.add.at(de, idx[:, k], dz[:, k:k + 1] * u)
+    return du, de, d_routed, d_shared
+
+
+def layer_backward_fp8(u, centroids, idx, routed_q, shared_q, dout):
+    """FP8 backward of R16.  routed_q(e) / shared_q entries are ((codes, scale) x 3) from
+    quantize_weight_128x128 of (w_gate, w_up, w_down); u and dout as held (bf16 values)."""
+    deq = lambda ws: tuple(dequant_weight(*w) for w in ws)  # noqa: E731
+    return layer_backward_steps(u, centroids, idx, lambda ex: deq(routed_q(ex)), [deq(w) for w in shared_q], dout,
+                                Fp8Policy)
