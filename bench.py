@@ -256,16 +256,18 @@ def main():
         route_balance = {"seq_len": seq, "route_balance_ms": round(ev_s[0].elapsed_time(ev_s[1]) / 10, 4),
                          "loss_first_sequences": [round(float(x), 8) for x in bl[:4].cpu()]}
 
-    # layer backward (bf16): gradients of <dout, h'> for the routing of the last step, timed on its own
+    # layer backward (bf16 or FP8 GEMMs): gradients of <dout, h'> for the routing of the last step,
+    # timed on its own
     backward = None
-    if cfg.dtype == "bf16" and not args.no_backward:
+    if cfg.dtype in ("bf16", "fp8") and not args.no_backward:
         from synth import TAG_DOUT, stream_key
         from synth.device import fill_normal_
         dout = fill_normal_(torch.empty((T, d), dtype=torch.bfloat16, device="cuda"),
                             stream_key(cfg.seed, cfg.cid, TAG_DOUT, 0), 1.0)
         du = torch.empty_like(dout)
         dcent = torch.empty((N, d), dtype=torch.float32, device="cuda")
-        grads = {k: torch.empty_like(dev[k]) for k in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")}
+        grads = {k: torch.empty(dev[k].shape, dtype=torch.bfloat16, device="cuda")
+                 for k in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")}
         wgr = moe.make_weight_grads(grads["w_gate"], grads["w_up"], grads["w_down"], grads["sh_gate"] if Ns else None,
                                     grads["sh_up"] if Ns else None, grads["sh_down"] if Ns else None)
         ws_b = torch.empty(moe.moe_backward_workspace_size(shape), dtype=torch.uint8, device="cuda")
@@ -286,7 +288,7 @@ def main():
         backward = {"ms": round(b_ms, 3), "tokens_per_s": round(T / (b_ms * 1e-3), 1),
                     "tflops_algorithmic": round(fl_alg / (b_ms * 1e-3) / 1e12, 1),
                     "tflops_executed": round(fl_exec / (b_ms * 1e-3) / 1e12, 1),
-                    "mfma_peak_frac_executed": round(fl_exec / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+                    "mfma_peak_frac_executed": round(fl_exec / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS[cfg.dtype], 4)}
         del grads, ws_b, du, dout, dcent
         torch.cuda.empty_cache()
 

@@ -170,23 +170,32 @@ typedef struct {
   void* sh_down;
 } moe_weight_grads;
 
-/* Bytes of device workspace moe_backward needs for `shape` (BF16 only; d and I multiples of
- * 128).  MOE_ERR_UNSUPPORTED for other shapes. */
+/* Bytes of device workspace moe_backward needs for `shape` (BF16 or FP8_B128; d and I multiples
+ * of 128).  MOE_ERR_UNSUPPORTED for other shapes. */
 moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Layer backward (方法 §2, the h'_t, s_{i,t} and g'_{i,t} equations): gradients of
  * L = <dout, h'> with the routing (topk_idx) held fixed — the Topk is piecewise constant — and
  * none for the bias, which never enters a gate.  With g_k = s_k / S (S = sum of the selected
  * s) the gate gradient flows through the unbiased s into u and the centroids.
- *   u, centroids, weights, topk_idx, topk_gate   as given to moe_route / moe_forward (BF16)
+ *   u, centroids, weights, topk_idx, topk_gate   as given to moe_route / moe_forward
  *   dout        [T, d]   bf16 dL/dh'
  *   du          [T, d]   bf16 out: dL/du (residual + every expert's input gradient + router term)
  *   d_centroids [N_r, d] fp32 out (rows of experts no token picked are zero)
  *   dw          bf16 out, every routed and shared expert's gate/up/down gradient (zero for
  *               experts no token picked)
- * Errors: MOE_ERR_UNSUPPORTED unless dtype == BF16, d % 128 == 0, I % 128 == 0;
- * MOE_ERR_INVALID_ARG for a null pointer or du aliasing u or dout; MOE_ERR_WORKSPACE if
- * workspace_bytes < moe_backward_workspace_size.  Nothing is launched on an error. */
+ * FP8_B128 (section 方法, FP8 Mixed Precision Training: the forward and both backward GEMM
+ * kinds in FP8; 核心概念, FP8 item: E4M3, 1x128 activation tiles, 128x128 weight blocks): the
+ * weights are the E4M3 codes and block scales of moe_forward; every product runs on E4M3
+ * operands with fp32 accumulation: dout and u in 1x128 tiles along d, [dA dB] along 2I, the
+ * weights transposed per 128x128 block (codes and scales carry over), and for the weight
+ * gradients the transposed activations in runs of 128 of each expert's rows (token order);
+ * quantised from bf16 (u, dout, H, dA, dB) or fp32 (gate * dout).  Gates, router and residual
+ * stay unquantised, and every output is bf16 / fp32 as for BF16.
+ * Errors: MOE_ERR_UNSUPPORTED unless dtype is BF16 or FP8_B128, d % 128 == 0, I % 128 == 0;
+ * MOE_ERR_INVALID_ARG for a null pointer (FP8_B128: also a null weight scale) or du aliasing
+ * u or dout; MOE_ERR_WORKSPACE if workspace_bytes < moe_backward_workspace_size.  Nothing is
+ * launched on an error. */
 moe_status moe_backward(const moe_shape* shape, const void* u, const float* centroids,
                         const moe_weights* weights, const int32_t* topk_idx, const float* topk_gate,
                         const void* dout, void* du, float* d_centroids, const moe_weight_grads* dw,

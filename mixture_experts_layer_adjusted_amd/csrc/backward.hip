@@ -15,6 +15,7 @@
 //              per-tile partials the gate/up backward GEMM wrote, then dz, and du_t summed in a
 //              fixed order (residual, routed rows, shared rows, centroid terms);
 //  dcentroid:  de_i by a fixed-order loop over the rows of segment i.
+#include "fp8_codec.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -240,6 +241,111 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
   }
 }
 
+// FP8 weights transposed with their block scales: dst[b][c * ldd + off + r] = src[b][r * lds + c]
+// (bytes) for r < R, c < C, R and C multiples of 128.  A 128 x 128 tile goes through LDS as
+// 32-bit words tile[c][p] that pack rows 4p..4p+3 of column c: each thread loads 16 columns of
+// four rows (four 16-byte loads); the store phase writes 16 consecutive rows of one column.
+// A 128 x 128 block of the stored matrix is a block of the transposed one, so its E4M3 codes
+// and its scale carry over unchanged.
+__global__ void __launch_bounds__(256) transpose_b8_kernel(TransposeB8Args a) {
+  __shared__ uint32_t tile[128][33];
+  const int64_t b = blockIdx.z;
+  const int r0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
+  const uint8_t* src = a.src + b * a.src_bstride;
+  uint8_t* dst = a.dst + b * a.dst_bstride;
+  const int tid = threadIdx.x;
+  {
+    const int p = tid & 31, cg = tid >> 5;       // rows 4p..4p+3, columns 16cg..16cg+15
+    uint32_t w[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 q = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + 4 * p + j) * a.lds + c0 + 16 * cg);
+      w[j][0] = q.x;
+      w[j][1] = q.y;
+      w[j][2] = q.z;
+      w[j][3] = q.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int sh = 8 * (k & 3);
+      const uint32_t v = ((w[0][k >> 2] >> sh) & 0xFFu) | (((w[1][k >> 2] >> sh) & 0xFFu) << 8) |
+                         (((w[2][k >> 2] >> sh) & 0xFFu) << 16) | (((w[3][k >> 2] >> sh) & 0xFFu) << 24);
+      tile[16 * cg + k][p] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = tid + 256 * i;                  // 1024 stores of 16 rows
+    const int c = v >> 3, q = v & 7;
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * a.ldd + a.off + r0 + 16 * q) =
+        make_uint4(tile[c][4 * q], tile[c][4 * q + 1], tile[c][4 * q + 2], tile[c][4 * q + 3]);
+  }
+  // the block's scale: [R/128][C/128] -> [C/128][ldds] at column off/128
+  if (tid == 0)
+    a.dst_scale[b * a.dst_scale_bstride + (int64_t)blockIdx.y * a.ldds + a.off / 128 + blockIdx.x] =
+        a.src_scale[b * a.src_scale_bstride + (int64_t)blockIdx.x * (a.C / 128) + blockIdx.y];
+}
+
+// Activations transposed and quantised along the rows: for column c and each run of 128 rows
+// j0..j0+127 (j0 a multiple of 128), v[j] = scale[j] * src[gather ? row_token[j] : j][c] in fp32
+// (0 where row_token[j] < 0), one scale amax / 448 (1 when the run is all zero) and the E4M3 codes
+// of v / scale: dst[c * ldd + j], dst_scale[c * (ldd / 128) + j / 128].  A 128-row x 64-column
+// block goes through LDS as fp32 [64][129]: each thread loads 32 columns of one row (four 16-byte
+// loads), then four consecutive threads take one column's 128 rows, 32 each.
+__global__ void __launch_bounds__(256) transpose_quant_kernel(TransposeQuantArgs a) {
+  __shared__ float tile[64][129];
+  const int64_t j0 = (int64_t)blockIdx.x * 128;
+  const int c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  {
+    const int jl = tid >> 1, half = tid & 1;
+    const int64_t j = j0 + jl;
+    const int tok = a.row_token[j];
+    float v[32];
+    if (tok < 0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+    } else {
+      const int64_t srow = a.gather ? (int64_t)tok : j;
+      const float sc = a.scale ? a.scale[j] : 1.0f;
+      const uint16_t* p = a.src + srow * a.lds + c0 + 32 * half;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float w[8];
+        load8(p + 8 * q, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[8 * q + i] = w[i] * sc;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) tile[32 * half + i][jl] = v[i];
+  }
+  __syncthreads();
+  const int c = tid >> 2, q = tid & 3;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = tile[c][32 * q + i];
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const float scale = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    w[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[k] |= e4m3_from_f32(__fdiv_rn(v[4 * k + i], scale)) << (8 * i);
+  }
+  uint8_t* drow = a.dst + (int64_t)(c0 + c) * a.ldd + j0 + 32 * q;
+  *reinterpret_cast<uint4*>(drow) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(drow + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  if (q == 0) a.dst_scale[(int64_t)(c0 + c) * (a.ldd / 128) + j0 / 128] = scale;
+}
+
 }  // namespace
 
 hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const float* gate, const int32_t* seg_off,
@@ -277,6 +383,22 @@ hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* ro
 }  // namespace moe
 
 namespace moe {
+
+hipError_t launch_transpose_b8(const TransposeB8Args& a, int batch, hipStream_t st) {
+  if (a.R == 0 || a.C == 0 || batch == 0) return hipSuccess;
+  if (a.R % 128 != 0 || a.C % 128 != 0 || a.off % 128 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_b8_kernel, dim3((unsigned)(a.R / 128), (unsigned)(a.C / 128), (unsigned)batch),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_quant(const TransposeQuantArgs& a, hipStream_t st) {
+  if (a.rows == 0 || a.C == 0) return hipSuccess;
+  if (a.rows % 128 != 0 || a.C % 64 != 0 || a.ldd < a.rows || a.ldd % 128 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_quant_kernel, dim3((unsigned)(a.rows / 128), (unsigned)(a.C / 64)), dim3(256), 0, st,
+                     a);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose(const TransposeArgs& a, int batch, hipStream_t st) {
   if (a.R == 0 || a.C == 0 || batch == 0) return hipSuccess;

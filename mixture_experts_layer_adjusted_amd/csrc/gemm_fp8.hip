@@ -17,13 +17,26 @@
 //             amax is a reduction across the four wavefronts that share the row
 //   down:     Y[r, n] = H[r] . Wd[e][n] in bf16
 //
+// The layer backward runs its three GEMM kinds through the same kernel (the page lists the
+// input-gradient and weight-gradient products as FP8 GEMMs too):
+//   plain:    the down form above with other operands: dH = dout W_down (weights transposed
+//             to [I, d] blocks) and dX = [dA dB] [W_gate; W_up] (transposed to [d, 2I])
+//   SwiGLU backward: the gate/up products recomputed, then from dH (before the gate, bf16)
+//             and the row gate: H, dA = g dH b SiLU'(a), dB = g dH SiLU(a) (bf16) and per row
+//             and 128-feature tile the partial sum of dH * H
+//   weight gradient: out_e[m, n] = sum over the rows k of segment e of A[m, k] B[n, k] with
+//             both operands transposed activations quantised per 1x128 run of rows, so the
+//             second operand also has one scale per row and K block, and K runs over the
+//             segment's rows only
+//
 // Tiling: 512 threads (8 wavefronts, two per SIMD), 256 rows (two M-tiles of one segment;
 // a segment with an odd M-tile count ends in a half tile whose upper wavefronts idle) x
 // 256 weight rows (gate/up: 128 gate + the matching 128 up features; down: 256 output
 // features).  Wavefront (wm, wn) of the 2 x 4 grid owns 128 rows x 64 weight rows as 8 x 4
 // blocks of 16 x 16.  One K-step is one 128-byte scale block of every row, staged in LDS
 // with a 16-byte-chunk XOR swizzle (conflict-free 16-lane reads) by direct global->LDS loads
-// one K-step ahead, in the XCD-aware tile order of the bf16 kernels.
+// one K-step ahead, in the XCD-aware tile order of the bf16 kernels.  The weight-gradient form
+// tiles each segment's M x N output in 256 x 256 blocks.
 #include "fp8_codec.h"
 #include "moe_internal.h"
 
@@ -76,28 +89,48 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-template <bool SWIGLU>
+// EPI: 0 plain bf16 store, 1 SwiGLU with H quantised, 2 SwiGLU backward, 3 weight gradient
+template <int EPI>
 __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands g, int NT) {
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ float row_amax[kTM][4];
+  __shared__ float row_red[kTM][4];   // per-row reductions across the four wavefronts of a row
   // ---- logical tile (same XCD-aware order as the bf16 streaming kernels, over 256-row tiles)
   const int b = blockIdx.x;
   const int64_t L = (int64_t)(b / (kXcds * kXcdChunk)) * (kXcds * kXcdChunk) + (b % kXcds) * kXcdChunk +
                     (b / kXcds) % kXcdChunk;
-  const int64_t slot = L / NT;
-  if (slot >= g.max_tiles) return;
-  const int seg = g.pair_seg[slot];
-  if (seg < 0) return;
-  const int seg_first = g.pair_off[seg];
-  const int seg_count = g.pair_off[seg + 1] - seg_first;
-  const int64_t lam = L - (int64_t)seg_first * NT;
-  const int grp = (int)(lam / (kGroupM * NT));
-  const int gm = min(kGroupM, seg_count - grp * kGroupM);
-  const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
-  const int local = grp * kGroupM + rem % gm;
-  const int nt = rem / gm;
-  const int64_t m0 = (int64_t)g.seg_off[seg] + (int64_t)local * kTM;
-  const int tile_rows = min(kTM, g.seg_off[seg + 1] - (int)m0);  // 256, or 128 for a half tile
+  int seg, nt, tile_rows, nk;
+  int64_t m0, k_base;
+  if constexpr (EPI == 3) {
+    // weight gradient: segment seg's M x N matrix, K over the segment's rows
+    const int MT = (g.wg_m + kTM - 1) / kTM;
+    const int64_t per = (int64_t)MT * NT;
+    seg = (int)(L / per);
+    if (seg >= g.n_seg) return;
+    const int rem = (int)(L - (int64_t)seg * per);
+    nt = rem / MT;
+    m0 = (int64_t)(rem % MT) * kTM;
+    tile_rows = min(kTM, g.wg_m - (int)m0);
+    k_base = g.seg_off[seg];
+    nk = (g.seg_off[seg + 1] - g.seg_off[seg]) / kBK;
+  } else {
+    const int64_t slot = L / NT;
+    if (slot >= g.max_tiles) return;
+    seg = g.pair_seg[slot];
+    if (seg < 0) return;
+    const int seg_first = g.pair_off[seg];
+    const int seg_count = g.pair_off[seg + 1] - seg_first;
+    const int64_t lam = L - (int64_t)seg_first * NT;
+    const int grp = (int)(lam / (kGroupM * NT));
+    const int gm = min(kGroupM, seg_count - grp * kGroupM);
+    const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
+    const int local = grp * kGroupM + rem % gm;
+    nt = rem / gm;
+    m0 = (int64_t)g.seg_off[seg] + (int64_t)local * kTM;
+    tile_rows = min(kTM, g.seg_off[seg + 1] - (int)m0);  // 256, or 128 for a half tile
+    k_base = 0;
+    nk = g.K / kBK;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,14 +139,18 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   const int n0 = nt * (SWIGLU ? kWRows / 2 : kWRows);
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
+  // row strides in bytes: the forward forms read rows of length K; the weight-gradient form reads
+  // transposed activations, rows of lda / ldw bytes, from column k_base on
+  const int64_t lda = EPI == 3 ? g.lda : K, ldw = EPI == 3 ? g.ldw : K;
   const size_t wstride = (size_t)N * K;
   const size_t sstride = (size_t)(N / kBK) * KB;  // scales per expert matrix
-  const uint8_t* W0 = static_cast<const uint8_t*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride;
+  const uint8_t* W0 = EPI == 3 ? static_cast<const uint8_t*>(g.w_routed[0]) + k_base
+                               : static_cast<const uint8_t*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride;
   const uint8_t* W1 =
       SWIGLU ? static_cast<const uint8_t*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride : nullptr;
-  const float* S0 = (shared ? g.s_shared[0] : g.s_routed[0]) + e * sstride;
+  const float* S0 = EPI == 3 ? nullptr : (shared ? g.s_shared[0] : g.s_routed[0]) + e * sstride;
   const float* S1 = SWIGLU ? (shared ? g.s_shared[1] : g.s_routed[1]) + e * sstride : nullptr;
-  const uint8_t* act = static_cast<const uint8_t*>(g.act);
+  const uint8_t* act = static_cast<const uint8_t*>(g.act) + k_base;
 
   // ---- direct-load sources as 32-bit byte offsets (the launcher checks the sizes): wave w fills
   // activation rows [32w, 32w+32) and weight-tile rows [32w, 32w+32), 8 rows of 128 bytes per
@@ -126,7 +163,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     const int64_t r = m0 + (row < tile_rows ? row : 0);  // rows past a half tile: a valid row
     int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;  // padding row: any valid row (outputs never read)
-    aoff[i] = (uint32_t)(tok * K) + ((lslot ^ swz(row)) << 4);
+    aoff[i] = (uint32_t)(tok * lda) + ((lslot ^ swz(row)) << 4);
   }
   uint32_t woff[kWDma];
 #pragma unroll
@@ -134,20 +171,27 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;  // 0..255 within the weight tile
     int n = n0 + (SWIGLU ? (r & (kWRows / 2 - 1)) : r);
     if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-    woff[i] = (uint32_t)n * (uint32_t)K + ((lslot ^ swz(kTM + r)) << 4);
+    woff[i] = (uint32_t)((int64_t)n * ldw) + ((lslot ^ swz(kTM + r)) << 4);
   }
   // gate rows (waves 0-3) come from W0, up rows (waves 4-7) from W1
   const uint8_t* wbase = (SWIGLU && wave >= kWaves / 2) ? W1 : W0;
   // ---- scale sources: lanes 0..31 of wave w load the activation scales of rows [32w, 32w+32)
   // into the stage's scale area; wave 7's lanes 32 and 33 load the scales of the tile's two
-  // 128-row weight blocks, landing right after the 256 row scales
+  // 128-row weight blocks, landing right after the 256 row scales.  In the weight-gradient form
+  // lanes 32..63 of wave w load the scales of weight-tile rows [32w, 32w+32) in the same
+  // all-lane load, so wave w's 64 dwords hold its 32 activation-row scales, then its 32
+  // weight-row scales (index sidx_a / sidx_w below).
   const float* ssrc = nullptr;
+  const int64_t lsa = EPI == 3 ? lda / kBK : KB;   // scale-row strides
   if (lane < 32) {
     const int row = wave * 32 + lane;
     const int64_t r = m0 + (row < tile_rows ? row : 0);
     int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;
-    ssrc = g.act_scale + tok * KB;
+    ssrc = g.act_scale + tok * lsa + k_base / kBK;
+  } else if (EPI == 3) {
+    const int n = min(n0 + wave * 32 + lane - 32, N - 1);
+    ssrc = g.s_routed[0] + (int64_t)n * (ldw / kBK) + k_base / kBK;
   } else if (wave == kWaves - 1 && lane < 34) {
     const int nb = lane - 32;
     if (SWIGLU) {
@@ -171,8 +215,14 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
           wbase + k0 + woff[i], (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
           0);
     // every wave has active lanes here, so every wave issues this load
-    if (ssrc) __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
+    if (EPI == 3)
+      __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 256), 4, 0, 0);
+    else if (ssrc)
+      __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
   };
+  // scale-area index of activation-tile row r and (weight-gradient form) weight-tile row j
+  auto sidx_a = [](int r) { return EPI == 3 ? 64 * (r >> 5) + (r & 31) : r; };
+  auto sidx_w = [](int j) { return 64 * (j >> 5) + 32 + (j & 31); };
 
   // weight rows of the wave's four 16-row blocks, and the 128-row scale block each falls in
   int wrow[kNB], wblk[kNB];
@@ -197,8 +247,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     for (int c = 0; c < kNB; ++c) acc[a][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = KB;
-  issue_stage(0);
+  if (nk > 0) issue_stage(0);
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmcnt<0>();
     // a bare barrier: every wave's loads of stage kt have landed and stage kt-1 is no longer read
@@ -209,23 +258,32 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
       i32x8 wf[kNB];
       float sw[kNB];
+      f32x4 swr[kNB];   // weight-gradient form: the scales of the lane's four weight rows
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
-        sw[nb] = sc[kTM + wblk[nb]];
+        if (EPI == 3)  // four consecutive weight rows of one group of 32
+          swr[nb] = *reinterpret_cast<const f32x4*>(sc + sidx_w(wrow[nb] + kq * 4));
+        else
+          sw[nb] = sc[kTM + wblk[nb]];
       }
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         const int r = mrow0 + mb * 16 + l16;
         const i32x8 xf = frag32(st, r, kq * 2);
-        const float sa = sc[r];
+        const float sa = sc[sidx_a(r)];
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
           const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb], xf, zero, 0, 0, 0, kE8M0One, 0,
                                                                               kE8M0One);
-          const float f = sa * sw[nb];
+          if (EPI == 3) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], f, acc[mb][nb][v]);
+            for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], sa * swr[nb][v], acc[mb][nb][v]);
+          } else {
+            const float f = sa * sw[nb];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], f, acc[mb][nb][v]);
+          }
         }
       }
     }
@@ -233,7 +291,53 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
 
   // ---- epilogue.  Lane holds, for token row mrow0 + 16 mb + l16, features 4 kq + (0..3) of
   // each 16-row weight block
-  if (SWIGLU) {
+  if constexpr (EPI == 2) {
+    // gate block nb and up block nb + 2 hold the same features
+    const uint16_t* dhp = static_cast<const uint16_t*>(g.dh);
+    uint16_t* dab = static_cast<uint16_t*>(g.out);
+    uint16_t* hout = static_cast<uint16_t*>(g.out2);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int rl = mrow0 + mb * 16 + l16;
+      const int64_t r = m0 + rl;
+      float part = 0.0f;
+      if (active) {
+        const float rg = g.row_gate[r];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int f = n0 + wn * 32 + nb * 16 + kq * 4;
+          const uint2 dq = *reinterpret_cast<const uint2*>(dhp + r * N + f);
+          const float dhu[4] = {__uint_as_float(dq.x << 16), __uint_as_float(dq.x & 0xFFFF0000u),
+                                __uint_as_float(dq.y << 16), __uint_as_float(dq.y & 0xFFFF0000u)};
+          uint16_t da[4], db[4], hh[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float a = acc[mb][nb][v], bu = acc[mb][nb + 2][v];
+            const float sg = 1.0f / (1.0f + __expf(-a));
+            const float h = a * sg * bu;
+            const float dh = rg * dhu[v];
+            da[v] = f32_to_bf16(dh * bu * sg * (1.0f + a * (1.0f - sg)));
+            db[v] = f32_to_bf16(dh * a * sg);
+            hh[v] = f32_to_bf16(h);
+            part += dhu[v] * h;
+          }
+          *reinterpret_cast<uint2*>(dab + r * 2 * N + f) =
+              make_uint2((uint32_t)da[0] | ((uint32_t)da[1] << 16), (uint32_t)da[2] | ((uint32_t)da[3] << 16));
+          *reinterpret_cast<uint2*>(dab + r * 2 * N + N + f) =
+              make_uint2((uint32_t)db[0] | ((uint32_t)db[1] << 16), (uint32_t)db[2] | ((uint32_t)db[3] << 16));
+          *reinterpret_cast<uint2*>(hout + r * N + f) =
+              make_uint2((uint32_t)hh[0] | ((uint32_t)hh[1] << 16), (uint32_t)hh[2] | ((uint32_t)hh[3] << 16));
+        }
+      }
+      // lanes of one row: l16 + 16 kq
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (kq == 0) row_red[rl][wn] = part;
+    }
+    __syncthreads();
+    for (int row = tid; row < tile_rows; row += kThreads)
+      g.dg_part[(m0 + row) * (N / kBK) + nt] = row_red[row][0] + row_red[row][1] + row_red[row][2] + row_red[row][3];
+  } else if constexpr (EPI == 1) {
     uint8_t* out = static_cast<uint8_t*>(g.out);
     const int IB = N / kBK;
 #pragma unroll
@@ -248,14 +352,14 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
         }
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      if (kq == 0) row_amax[mrow0 + mb * 16 + l16][wn] = amax;
+      if (kq == 0) row_red[mrow0 + mb * 16 + l16][wn] = amax;
     }
     __syncthreads();
     if (active) {
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         const int r = mrow0 + mb * 16 + l16;
-        const float a = fmaxf(fmaxf(row_amax[r][0], row_amax[r][1]), fmaxf(row_amax[r][2], row_amax[r][3]));
+        const float a = fmaxf(fmaxf(row_red[r][0], row_red[r][1]), fmaxf(row_red[r][2], row_red[r][3]));
         const float scale = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
         uint8_t* orow = out + (m0 + r) * N;
 #pragma unroll
@@ -270,7 +374,9 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       }
     }
   } else if (active) {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
+    // weight gradient: segment e's matrix of the routed or shared output
+    uint16_t* out = EPI == 3 ? static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N
+                             : static_cast<uint16_t*>(g.out);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       uint16_t* orow = out + (m0 + mrow0 + mb * 16 + l16) * N;
@@ -286,29 +392,39 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   }
 }
 
-template <bool SWIGLU>
+template <int EPI>
 hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
   if (g.K % kBK != 0 || g.N % kBK != 0) return hipErrorInvalidValue;
   // 32-bit byte offsets address the activation matrix and one expert's weight matrix
-  if (g.act_rows * g.K >= (int64_t(1) << 32) || (int64_t)g.N * g.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  if (EPI == 3) {
+    if (g.wg_m % kBK != 0 || g.lda % kBK != 0 || g.ldw % kBK != 0) return hipErrorInvalidValue;
+    if ((int64_t)g.wg_m * g.lda >= (int64_t(1) << 32) || (int64_t)g.N * g.ldw >= (int64_t(1) << 32))
+      return hipErrorInvalidValue;
+  } else if (g.act_rows * g.K >= (int64_t(1) << 32) || (int64_t)g.N * g.K >= (int64_t(1) << 32)) {
+    return hipErrorInvalidValue;
+  }
   const size_t lds_bytes = kStages * kStageBytes;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_fp8_kernel<SWIGLU>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_fp8_kernel<EPI>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
   const int NT = (int)ceil_div(g.N, SWIGLU ? kWRows / 2 : kWRows);
-  const int64_t tiles = g.max_pairs * NT;
+  const int64_t tiles = EPI == 3 ? (int64_t)g.n_seg * ceil_div(g.wg_m, kTM) * NT : g.max_pairs * NT;
   const int64_t grid = ceil_div(tiles, kXcds * kXcdChunk) * (kXcds * kXcdChunk);
-  hipLaunchKernelGGL(grouped_gemm_fp8_kernel<SWIGLU>, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_gemm_fp8_kernel<EPI>, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st) { return launch_fp8<true>(g, st); }
-hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st) { return launch_fp8<false>(g, st); }
+hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st) { return launch_fp8<1>(g, st); }
+hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st) { return launch_fp8<0>(g, st); }
+hipError_t launch_gemm_fp8_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_fp8<2>(g, st); }
+hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st) { return launch_fp8<3>(g, st); }
 
 }  // namespace moe

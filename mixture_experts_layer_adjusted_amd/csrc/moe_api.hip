@@ -14,6 +14,8 @@ hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_fp8_swiglu_bwd(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st);
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st) {
   if (dtype == MOE_DTYPE_F32) return launch_gemm_f32_swiglu(g, st);
@@ -54,6 +56,8 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.route_scores = take((size_t)T * N * 4);   // the fp32 path writes it only for the balance statistic
   const int splits = route_logit_splits(s);
   p.route_zpart = take(splits > 1 ? (size_t)splits * T * N * 4 : 0);
+  // sequences of L >= 64 tokens: T/L sequences of ceil(L/64) chunks, at most T/64 + T/L <= T/32
+  p.route_bal_part = take((size_t)ceil_div(T, 32) * N * 4);
   p.route_bytes = o;
   o = 0;
   p.chunk_counts = take((size_t)p.chunks * N * 4);
@@ -77,12 +81,25 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.bwd_row_gate = take((size_t)p.max_rows * 4);
   p.bwd_row_dz = take((size_t)p.max_rows * 4);
   p.bwd_dg_part = take((size_t)p.max_rows * (I / 128 > 0 ? I / 128 : 1) * 4);
-  p.bwd_wd_t = take((size_t)(N + Ns) * I * d * 2);
-  p.bwd_wc_t = take((size_t)(N + Ns) * d * 2 * I * 2);
-  p.bwd_dy_t = take((size_t)d * p.max_rows * 2);
-  p.bwd_h_t = take((size_t)I * p.max_rows * 2);
-  p.bwd_dab_t = take((size_t)2 * I * p.max_rows * 2);
-  p.bwd_x_t = take((size_t)d * p.max_rows * 2);
+  const size_t eb = fp8 ? 1 : 2;   // bytes per element of the transposed copies
+  const int64_t P = p.max_rows, d8 = d / 128, i8 = I / 128, p8 = P / 128;
+  p.bwd_wd_t = take((size_t)(N + Ns) * I * d * eb);
+  p.bwd_wc_t = take((size_t)(N + Ns) * d * 2 * I * eb);
+  p.bwd_dy_t = take((size_t)d * P * eb);
+  p.bwd_h_t = take((size_t)I * P * eb);
+  p.bwd_dab_t = take((size_t)2 * I * P * eb);
+  p.bwd_x_t = take((size_t)d * P * eb);
+  p.bwd_dhu = take(fp8 ? (size_t)P * I * 2 : 0);
+  p.bwd_wd_ts = take(fp8 ? (size_t)(N + Ns) * i8 * d8 * 4 : 0);
+  p.bwd_wc_ts = take(fp8 ? (size_t)(N + Ns) * d8 * 2 * i8 * 4 : 0);
+  p.bwd_dy_ts = take(fp8 ? (size_t)d * p8 * 4 : 0);
+  p.bwd_h_ts = take(fp8 ? (size_t)I * p8 * 4 : 0);
+  p.bwd_dab_ts = take(fp8 ? (size_t)2 * I * p8 * 4 : 0);
+  p.bwd_x_ts = take(fp8 ? (size_t)d * p8 * 4 : 0);
+  p.bwd_dout_q = take(fp8 ? (size_t)T * d : 0);
+  p.bwd_dout_s = take(fp8 ? (size_t)T * d8 * 4 : 0);
+  p.bwd_dab_q = take(fp8 ? (size_t)P * 2 * I : 0);
+  p.bwd_dab_s = take(fp8 ? (size_t)P * 2 * i8 * 4 : 0);
   p.backward_total = o;
   return p;
 }
@@ -267,7 +284,8 @@ moe_status moe_route_balance(const moe_shape* shape, int32_t seq_len, float alph
   if (shape->tokens == 0) return MOE_OK;
   const WorkspacePlan p = plan_workspace(*shape);
   const float* scores = reinterpret_cast<const float*>(static_cast<char*>(workspace) + p.route_scores);
-  return hip_status(launch_seq_balance(*shape, seq_len, alpha, scores, topk_idx, seq_loss, stream));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.route_bal_part);
+  return hip_status(launch_seq_balance(*shape, seq_len, alpha, scores, topk_idx, part, seq_loss, stream));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* u, const moe_weights* weights, const int32_t* topk_idx,
@@ -284,10 +302,173 @@ moe_status moe_forward_profiled(const moe_shape* shape, const void* u, const moe
                       n_events);
 }
 
+// FP8_B128 backward GEMMs (every product on E4M3 operands, fp32 accumulation): input gradients
+// with the weights transposed per 128 x 128 block, the gate/up products recomputed from the
+// quantised u, and weight gradients on activations transposed and quantised per run of 128 rows
+// of each segment.  Runs after the permutation and the row gates; ends with du (router_bwd).
+static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char* wsb, const void* u,
+                               const float* centroids, const moe_weights* w, const int32_t* topk_idx,
+                               const void* dout, void* du, const moe_weight_grads* dw, hipStream_t stream) {
+  moe_status rc;
+  const int64_t T = s.tokens, d = s.hidden, I = s.inter, Nr = s.n_routed, Ns = s.n_shared, P = p.max_rows;
+  const int64_t d8 = d / 128, i8 = I / 128, p8 = P / 128;
+  auto at = [&](size_t off) { return wsb + off; };
+  const int32_t* row_token = reinterpret_cast<const int32_t*>(at(p.row_token));
+  const int32_t* perm_row = reinterpret_cast<const int32_t*>(at(p.perm_row));
+  const int32_t* seg_off = reinterpret_cast<const int32_t*>(at(p.seg_off));
+  const float* row_gate = reinterpret_cast<const float*>(at(p.bwd_row_gate));
+  float* row_dz = reinterpret_cast<float*>(at(p.bwd_row_dz));
+  float* dg_part = reinterpret_cast<float*>(at(p.bwd_dg_part));
+  uint8_t* u_q = reinterpret_cast<uint8_t*>(at(p.u_q));
+  float* u_s = reinterpret_cast<float*>(at(p.u_scale));
+  uint8_t* dout_q = reinterpret_cast<uint8_t*>(at(p.bwd_dout_q));
+  float* dout_s = reinterpret_cast<float*>(at(p.bwd_dout_s));
+  uint16_t* dhu = reinterpret_cast<uint16_t*>(at(p.bwd_dhu));
+  uint16_t* hb = reinterpret_cast<uint16_t*>(at(p.bwd_h));
+  uint16_t* dab = reinterpret_cast<uint16_t*>(at(p.bwd_dab));
+  uint8_t* dab_q = reinterpret_cast<uint8_t*>(at(p.bwd_dab_q));
+  float* dab_s = reinterpret_cast<float*>(at(p.bwd_dab_s));
+  uint16_t* dx = reinterpret_cast<uint16_t*>(at(p.y));
+  uint8_t* wd_t = reinterpret_cast<uint8_t*>(at(p.bwd_wd_t));
+  float* wd_ts = reinterpret_cast<float*>(at(p.bwd_wd_ts));
+  uint8_t* wc_t = reinterpret_cast<uint8_t*>(at(p.bwd_wc_t));
+  float* wc_ts = reinterpret_cast<float*>(at(p.bwd_wc_ts));
+  uint8_t* dy_t = reinterpret_cast<uint8_t*>(at(p.bwd_dy_t));
+  float* dy_ts = reinterpret_cast<float*>(at(p.bwd_dy_ts));
+  uint8_t* h_t = reinterpret_cast<uint8_t*>(at(p.bwd_h_t));
+  float* h_ts = reinterpret_cast<float*>(at(p.bwd_h_ts));
+  uint8_t* dab_t = reinterpret_cast<uint8_t*>(at(p.bwd_dab_t));
+  float* dab_ts = reinterpret_cast<float*>(at(p.bwd_dab_ts));
+  uint8_t* x_t = reinterpret_cast<uint8_t*>(at(p.bwd_x_t));
+  float* x_ts = reinterpret_cast<float*>(at(p.bwd_x_ts));
+  const int64_t max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + Nr + Ns) / 2);
+  auto b8 = [](const void* q) { return static_cast<const uint8_t*>(q); };
+
+  auto wgrad = [&](const uint8_t* a_t, const float* a_s, int M, const uint8_t* b_t, const float* b_s, int N,
+                   void* out_r, void* out_s) {
+    GemmOperands g{};
+    g.act = a_t;
+    g.act_scale = a_s;
+    g.w_routed[0] = b_t;
+    g.s_routed[0] = b_s;
+    g.seg_off = seg_off;
+    g.n_routed = s.n_routed;
+    g.K = (int)P;
+    g.N = N;
+    g.lda = P;
+    g.ldw = P;
+    g.wg_m = M;
+    g.n_seg = (int)(Nr + Ns);
+    g.out = out_r;
+    g.out2 = out_s;
+    return hip_status(launch_gemm_fp8_wgrad(g, stream));
+  };
+  if (T > 0) {
+    // E4M3 copies of u and dout (1 x 128 tiles along d)
+    if ((rc = hip_status(launch_quantize_act(T, (int)d, u, u_q, u_s, stream))) != MOE_OK) return rc;
+    if ((rc = hip_status(launch_quantize_act(T, (int)d, dout, dout_q, dout_s, stream))) != MOE_OK) return rc;
+    // transposed weight codes and block scales: W_down^T [I][d], [W_gate; W_up]^T [d][2I]
+    auto tw = [&](const void* src, const float* ss, int64_t R, int64_t C, uint8_t* dst, float* ds, int64_t ldd,
+                  int64_t off, int64_t n) {
+      TransposeB8Args a{b8(src), C, R * C, ss, (R / 128) * (C / 128), dst, ldd, off, C * ldd,
+                        ds, ldd / 128, (C / 128) * (ldd / 128), (int)R, (int)C};
+      return hip_status(launch_transpose_b8(a, (int)n, stream));
+    };
+    if ((rc = tw(w->w_down, w->w_down_scale, d, I, wd_t, wd_ts, d, 0, Nr)) != MOE_OK) return rc;
+    if ((rc = tw(w->w_gate, w->w_gate_scale, I, d, wc_t, wc_ts, 2 * I, 0, Nr)) != MOE_OK) return rc;
+    if ((rc = tw(w->w_up, w->w_up_scale, I, d, wc_t, wc_ts, 2 * I, I, Nr)) != MOE_OK) return rc;
+    if (Ns > 0) {
+      if ((rc = tw(w->sh_down, w->sh_down_scale, d, I, wd_t + Nr * I * d, wd_ts + Nr * i8 * d8, d, 0, Ns)) != MOE_OK)
+        return rc;
+      if ((rc = tw(w->sh_gate, w->sh_gate_scale, I, d, wc_t + Nr * d * 2 * I, wc_ts + Nr * d8 * 2 * i8, 2 * I, 0,
+                   Ns)) != MOE_OK)
+        return rc;
+      if ((rc = tw(w->sh_up, w->sh_up_scale, I, d, wc_t + Nr * d * 2 * I, wc_ts + Nr * d8 * 2 * i8, 2 * I, I, Ns)) !=
+          MOE_OK)
+        return rc;
+    }
+    GemmOperands g{};
+    g.tile_seg = reinterpret_cast<const int32_t*>(at(p.tile_seg));
+    g.seg_off = seg_off;
+    g.pair_seg = reinterpret_cast<const int32_t*>(at(p.pair_seg));
+    g.pair_off = reinterpret_cast<const int32_t*>(at(p.pair_off));
+    g.n_routed = s.n_routed;
+    g.max_tiles = p.max_tiles;
+    g.max_pairs = max_pairs;
+    // dH (before the gate) = dout[token] W_down
+    GemmOperands g1 = g;
+    g1.act = dout_q;
+    g1.act_scale = dout_s;
+    g1.row_token = row_token;
+    g1.act_rows = T;
+    g1.w_routed[0] = wd_t;
+    g1.w_shared[0] = wd_t + Nr * I * d;
+    g1.s_routed[0] = wd_ts;
+    g1.s_shared[0] = wd_ts + Nr * i8 * d8;
+    g1.K = (int)d;
+    g1.N = (int)I;
+    g1.out = dhu;
+    if ((rc = hip_status(launch_gemm_fp8_down(g1, stream))) != MOE_OK) return rc;
+    // gate/up recomputed from the quantised u: [dA dB], H and the gate-gradient partials
+    GemmOperands g2 = g;
+    g2.act = u_q;
+    g2.act_scale = u_s;
+    g2.row_token = row_token;
+    g2.act_rows = T;
+    g2.w_routed[0] = w->w_gate;
+    g2.w_routed[1] = w->w_up;
+    g2.w_shared[0] = w->sh_gate;
+    g2.w_shared[1] = w->sh_up;
+    g2.s_routed[0] = w->w_gate_scale;
+    g2.s_routed[1] = w->w_up_scale;
+    g2.s_shared[0] = w->sh_gate_scale;
+    g2.s_shared[1] = w->sh_up_scale;
+    g2.K = (int)d;
+    g2.N = (int)I;
+    g2.dh = dhu;
+    g2.row_gate = row_gate;
+    g2.out = dab;
+    g2.out2 = hb;
+    g2.dg_part = dg_part;
+    if ((rc = hip_status(launch_gemm_fp8_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
+    // dX = [dA dB] [W_gate; W_up], [dA dB] in 1 x 128 tiles along 2I
+    if ((rc = hip_status(launch_quantize_act(P, (int)(2 * I), dab, dab_q, dab_s, stream))) != MOE_OK) return rc;
+    GemmOperands g3 = g;
+    g3.act = dab_q;
+    g3.act_scale = dab_s;
+    g3.act_rows = P;
+    g3.w_routed[0] = wc_t;
+    g3.w_shared[0] = wc_t + Nr * d * 2 * I;
+    g3.s_routed[0] = wc_ts;
+    g3.s_shared[0] = wc_ts + Nr * d8 * 2 * i8;
+    g3.K = (int)(2 * I);
+    g3.N = (int)d;
+    g3.out = dx;
+    if ((rc = hip_status(launch_gemm_fp8_down(g3, stream))) != MOE_OK) return rc;
+    if ((rc = hip_status(launch_router_bwd(s, u, centroids, topk_idx, perm_row, dg_part, seg_off, dout, dx, du,
+                                           row_dz, stream))) != MOE_OK)
+      return rc;
+    // weight-gradient operands: (g dout)^T, H^T, [dA dB]^T, X^T, quantised per run of 128 rows
+    auto tq = [&](const void* src, int64_t lds, bool gather, const float* scale, uint8_t* dst, float* ds, int64_t C) {
+      TransposeQuantArgs a{static_cast<const uint16_t*>(src), lds, row_token, gather, scale, dst, ds, P, P, (int)C};
+      return hip_status(launch_transpose_quant(a, stream));
+    };
+    if ((rc = tq(dout, d, true, row_gate, dy_t, dy_ts, d)) != MOE_OK) return rc;
+    if ((rc = tq(hb, I, false, nullptr, h_t, h_ts, I)) != MOE_OK) return rc;
+    if ((rc = tq(dab, 2 * I, false, nullptr, dab_t, dab_ts, 2 * I)) != MOE_OK) return rc;
+    if ((rc = tq(u, d, true, nullptr, x_t, x_ts, d)) != MOE_OK) return rc;
+  }
+  // dW_down = (g dY)^T H, dW_gate = dA^T X, dW_up = dB^T X over each segment's rows (an empty
+  // segment writes zeros)
+  if ((rc = wgrad(dy_t, dy_ts, (int)d, h_t, h_ts, (int)I, dw->w_down, dw->sh_down)) != MOE_OK) return rc;
+  if ((rc = wgrad(dab_t, dab_ts, (int)I, x_t, x_ts, (int)d, dw->w_gate, dw->sh_gate)) != MOE_OK) return rc;
+  return wgrad(dab_t + I * P, dab_ts + I * p8, (int)I, x_t, x_ts, (int)d, dw->w_up, dw->sh_up);
+}
+
 static moe_status check_backward_shape(const moe_shape* s) {
   moe_status rc = check_shape(s);
   if (rc != MOE_OK) return rc;
-  if (s->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->dtype != MOE_DTYPE_BF16 && s->dtype != MOE_DTYPE_FP8_B128) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 128 != 0 || s->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
   // the streaming and backward GEMMs address their operands with 32-bit byte offsets
   const int64_t max_rows =
@@ -320,6 +501,10 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
   if (s.n_shared > 0 && (!w->sh_gate || !w->sh_up || !w->sh_down || !dw->sh_gate || !dw->sh_up || !dw->sh_down))
     return MOE_ERR_INVALID_ARG;
   if (du == u || du == dout) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = s.dtype == MOE_DTYPE_FP8_B128;
+  if (fp8 && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return MOE_ERR_INVALID_ARG;
+  if (fp8 && s.n_shared > 0 && (!w->sh_gate_scale || !w->sh_up_scale || !w->sh_down_scale))
+    return MOE_ERR_INVALID_ARG;
   const WorkspacePlan p = plan_workspace(s);
   if (workspace_bytes < p.backward_total) return MOE_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
@@ -346,6 +531,10 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
   if ((rc = hip_status(launch_row_gate(s, perm_row, topk_gate, seg_off, p.max_rows, row_gate, row_dz, stream))) !=
       MOE_OK)
     return rc;
+  if (fp8) {
+    if ((rc = fp8_backward(s, p, wsb, u, centroids, w, topk_idx, dout, du, dw, stream)) != MOE_OK) return rc;
+    return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, seg_rows, d_centroids, stream));
+  }
   const int64_t Nr = s.n_routed, Ns = s.n_shared, P = p.max_rows;
   uint16_t* wd_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_wd_t);   // [N_r + N_s][I][d]
   uint16_t* wc_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_wc_t);   // [N_r + N_s][d][2I]

@@ -29,6 +29,7 @@ struct WorkspacePlan {
   size_t route_e_hi, route_e_mid, route_e_lo;  // bf16 [N_pad, d]  exact 3-way split of the centroids
   size_t route_scores;      // fp32 [T, N_r]  affinities s (MFMA path)
   size_t route_zpart;       // fp32 [splits, T, N_r]  partial logits of a split contraction (small T)
+  size_t route_bal_part;    // fp32 [ceil(T / 32), N_r] balance-statistic partials per chunk of 64 tokens
   // forward
   size_t chunk_counts;      // int32 [chunks, N_r]
   size_t chunk_base;        // int32 [chunks, N_r]
@@ -51,12 +52,26 @@ struct WorkspacePlan {
   size_t bwd_row_gate;      // fp32 [max_rows]
   size_t bwd_row_dz;        // fp32 [max_rows]
   size_t bwd_dg_part;       // fp32 [max_rows, I / 128]
-  size_t bwd_wd_t;          // bf16 [N_r + N_s, I, d]   W_down transposed
-  size_t bwd_wc_t;          // bf16 [N_r + N_s, d, 2 I] [W_gate; W_up] transposed
-  size_t bwd_dy_t;          // bf16 [d, max_rows]      (gate * dout of each row) transposed
-  size_t bwd_h_t;           // bf16 [I, max_rows]
-  size_t bwd_dab_t;         // bf16 [2 I, max_rows]
-  size_t bwd_x_t;           // bf16 [d, max_rows]
+  // transposed copies: bf16, or E4M3 codes for FP8_B128 (weights per 128 x 128 block, activations
+  // per run of 128 rows, with the scales below)
+  size_t bwd_wd_t;          // [N_r + N_s, I, d]   W_down transposed
+  size_t bwd_wc_t;          // [N_r + N_s, d, 2 I] [W_gate; W_up] transposed
+  size_t bwd_dy_t;          // [d, max_rows]      (gate * dout of each row) transposed
+  size_t bwd_h_t;           // [I, max_rows]
+  size_t bwd_dab_t;         // [2 I, max_rows]
+  size_t bwd_x_t;           // [d, max_rows]
+  // FP8_B128 only
+  size_t bwd_dhu;           // bf16 [max_rows, I]      dL/dH before the gate
+  size_t bwd_wd_ts;         // fp32 [N_r + N_s, I/128, d/128]
+  size_t bwd_wc_ts;         // fp32 [N_r + N_s, d/128, 2I/128]
+  size_t bwd_dy_ts;         // fp32 [d, max_rows/128]
+  size_t bwd_h_ts;          // fp32 [I, max_rows/128]
+  size_t bwd_dab_ts;        // fp32 [2 I, max_rows/128]
+  size_t bwd_x_ts;          // fp32 [d, max_rows/128]
+  size_t bwd_dout_q;        // e4m3 [T, d]
+  size_t bwd_dout_s;        // fp32 [T, d/128]
+  size_t bwd_dab_q;         // e4m3 [max_rows, 2 I]
+  size_t bwd_dab_s;         // fp32 [max_rows, 2I/128]
   size_t backward_total;
   int64_t route_blocks, chunks, max_tiles, max_rows;
 };
@@ -86,8 +101,9 @@ hipError_t launch_route(const moe_shape& s, const void* u, const float* centroid
                         hipStream_t st);
 
 // per-sequence balance statistic from the affinities the routing call wrote to the workspace
+// part: fp32 [ceil(T / 32), N_r] chunk partials (sequences of 64 tokens or more)
 hipError_t launch_seq_balance(const moe_shape& s, int seq_len, float alpha, const float* scores, const int32_t* idx,
-                              float* loss, hipStream_t st);
+                              float* part, float* loss, hipStream_t st);
 
 hipError_t launch_permute(const moe_shape& s, const int32_t* idx, const WorkspacePlan& p, char* ws,
                           hipStream_t st);
@@ -142,6 +158,36 @@ struct TransposeArgs {
   int R, C;
 };
 hipError_t launch_transpose(const TransposeArgs& a, int batch, hipStream_t st);
+// E4M3 weight codes transposed per 128 x 128 block with their scales:
+// dst[b][c * ldd + off + r] = src[b][r * lds + c] (bytes), r < R, c < C, all multiples of 128;
+// dst_scale[b][(c / 128) * ldds + (off + r) / 128] = src_scale[b][(r / 128) * (C / 128) + c / 128]
+struct TransposeB8Args {
+  const uint8_t* src;
+  int64_t lds, src_bstride;
+  const float* src_scale;
+  int64_t src_scale_bstride;
+  uint8_t* dst;
+  int64_t ldd, off, dst_bstride;
+  float* dst_scale;
+  int64_t ldds, dst_scale_bstride;
+  int R, C;
+};
+hipError_t launch_transpose_b8(const TransposeB8Args& a, int batch, hipStream_t st);
+// bf16 activations transposed and quantised per run of 128 rows: for j < rows, c < C,
+// v = scale[j] * src[(gather ? row_token[j] : j) * lds + c] (0 where row_token[j] < 0);
+// dst[c * ldd + j] = E4M3(v / s), dst_scale[c * (ldd / 128) + j / 128] = s = amax / 448 of the run
+struct TransposeQuantArgs {
+  const uint16_t* src;
+  int64_t lds;
+  const int32_t* row_token;
+  bool gather;
+  const float* scale;
+  uint8_t* dst;
+  float* dst_scale;
+  int64_t ldd, rows;
+  int C;
+};
+hipError_t launch_transpose_quant(const TransposeQuantArgs& a, hipStream_t st);
 hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const float* gate, const int32_t* seg_off,
                            int64_t max_rows, float* row_gate, float* row_dz, hipStream_t st);
 hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* centroids, const int32_t* idx,

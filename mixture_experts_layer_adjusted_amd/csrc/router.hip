@@ -658,12 +658,80 @@ __global__ void __launch_bounds__(256) seq_balance_kernel(const float* __restric
   if (tid == 0) loss[blockIdx.x] = alpha * red[0];
 }
 
+// Long sequences (L >= 64) in two passes so that the whole chip takes part: the first pass gives
+// every chunk of up to 64 tokens of a sequence its own workgroup, which writes the chunk's
+// partial sum over its tokens of s_{i,t} / S_t for every expert (S_t summed as above); the
+// second adds the chunk partials of each sequence in chunk order and forms the loss.
+__global__ void __launch_bounds__(256) seq_balance_part_kernel(const float* __restrict__ s, int N, int L, int cps,
+                                                               float* __restrict__ part) {
+  __shared__ float St[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c = blockIdx.x;
+  const int64_t seq = c / cps;
+  const int ci = (int)(c % cps);
+  const int64_t t0 = seq * L + (int64_t)ci * 64;
+  const int nt = min(64, L - ci * 64);
+  for (int t = wave; t < nt; t += 4) {
+    const float* row = s + (t0 + t) * N;
+    float v = 0.0f;
+    for (int e = lane; e < N; e += 64) v += row[e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) St[t] = v;
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += 256) {
+    float p = 0.0f;
+    for (int t = 0; t < nt; ++t) p += s[(t0 + t) * N + e] / St[t];
+    part[c * N + e] = p;
+  }
+}
+
+__global__ void __launch_bounds__(256) seq_balance_final_kernel(const float* __restrict__ part,
+                                                                const int32_t* __restrict__ idx, int N, int K, int L,
+                                                                int cps, float alpha, float* __restrict__ loss) {
+  extern __shared__ int32_t cnt[];   // [N]
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * L;
+  for (int e = tid; e < N; e += 256) cnt[e] = 0;
+  __syncthreads();
+  for (int q = tid; q < L * K; q += 256) {
+    const int e = idx[t0 * K + q];
+    if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  float term = 0.0f;
+  const float* pc = part + (int64_t)blockIdx.x * cps * N;
+  for (int e = tid; e < N; e += 256) {
+    float p = 0.0f;
+    for (int c = 0; c < cps; ++c) p += pc[(int64_t)c * N + e];
+    const float f = (float)cnt[e] * (float)N / ((float)K * (float)L);
+    term += f * (p / (float)L);
+  }
+  red[tid] = term;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) loss[blockIdx.x] = alpha * red[0];
+}
+
 }  // namespace
 
 hipError_t launch_seq_balance(const moe_shape& s, int seq_len, float alpha, const float* scores, const int32_t* idx,
-                              float* loss, hipStream_t st) {
+                              float* part, float* loss, hipStream_t st) {
   const int64_t n_seq = s.tokens / seq_len;
   if (n_seq == 0) return hipSuccess;
+  if (seq_len >= 64) {
+    const int cps = (int)ceil_div(seq_len, 64);
+    hipLaunchKernelGGL(seq_balance_part_kernel, dim3((unsigned)(n_seq * cps)), dim3(256), 0, st, scores, s.n_routed,
+                       seq_len, cps, part);
+    hipLaunchKernelGGL(seq_balance_final_kernel, dim3((unsigned)n_seq), dim3(256), (size_t)s.n_routed * 4, st, part,
+                       idx, s.n_routed, s.top_k, seq_len, cps, alpha, loss);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)seq_len * 4 + (size_t)s.n_routed * 4;
   static bool attr_set = false;
   if (!attr_set) {

@@ -357,7 +357,7 @@ def e4m3_encode(q: np.ndarray) -> np.ndarray:
     return code | sign
 
 
-def e4m3_decode(code: np.ndarray) -> np.ndarray:
+def _e4m3_values(code: np.ndarray) -> np.ndarray:
     code = np.asarray(code, dtype=np.uint8).astype(np.int64)
     s = np.where(code & 0x80, -1.0, 1.0)
     e = (code >> 3) & 0xF
@@ -365,6 +365,14 @@ def e4m3_decode(code: np.ndarray) -> np.ndarray:
     v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
     v = np.where((e == 15) & (m == 7), np.nan, v)
     return s * v
+
+
+_E4M3_TABLE = _e4m3_values(np.arange(256))
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """Values of E4M3FN bit patterns (through the 256-entry table of the formula above)."""
+    return _E4M3_TABLE[np.asarray(code, dtype=np.uint8)]
 
 
 def _quant_block(x32: np.ndarray, axis_len_elems):
@@ -490,6 +498,27 @@ class Fp8Policy:
         return (np.asarray(g, dtype=np.float32)[:, None] * np.asarray(x, dtype=np.float32)).astype(np.float64)
 
 
+def expert_backward(x, dy, u_rows, dout_rows, g, wg, wu, wd, q):
+    """One expert's part of layer_backward_steps over its rows (token order): x = tiles(u) and
+    dy = tiles(dout) of those rows, their held u and dout, and their gates g.
+    Returns (dx [rows, d], dg [rows], (dWg, dWu, dWd))."""
+    wg, wu, wd = (np.asarray(w, dtype=np.float64) for w in (wg, wu, wd))
+    g = np.asarray(g, dtype=np.float64)
+    a = x @ wg.T
+    b = x @ wu.T
+    dh_pre = q.held(dy @ wd)
+    sg = 1.0 / (1.0 + np.exp(-a))
+    h = a * sg * b
+    dg = np.sum(dh_pre * h, axis=1)
+    dh = g[:, None] * dh_pre
+    da = q.held(dh * b * sg * (1.0 + a * (1.0 - sg)))
+    db = q.held(dh * a * sg)
+    dx = q.tiles(np.concatenate([da, db], axis=1)) @ np.concatenate([wg, wu], axis=0)
+    uo = q.runs(u_rows)
+    dwd = q.runs(q.scaled(g, dout_rows)).T @ q.runs(q.held(h))
+    return dx, dg, (q.runs(da).T @ uo, q.runs(db).T @ uo, dwd)
+
+
 def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
     """The R14 backward taken step by step, each GEMM operand passed through policy q (R16).
 
@@ -514,21 +543,7 @@ def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
     dyq = q.tiles(dout)
 
     def expert(rows, g, wg, wu, wd):
-        wg, wu, wd = (np.asarray(w, dtype=np.float64) for w in (wg, wu, wd))
-        x = xq[rows]
-        a = x @ wg.T
-        b = x @ wu.T
-        dh_pre = q.held(dyq[rows] @ wd)
-        sg = 1.0 / (1.0 + np.exp(-a))
-        h = a * sg * b
-        dg = np.sum(dh_pre * h, axis=1)
-        dh = g[:, None] * dh_pre
-        da = q.held(dh * b * sg * (1.0 + a * (1.0 - sg)))
-        db = q.held(dh * a * sg)
-        dx = q.tiles(np.concatenate([da, db], axis=1)) @ np.concatenate([wg, wu], axis=0)
-        uo = q.runs(u[rows])
-        dwd = q.runs(q.scaled(g, dout[rows])).T @ q.runs(q.held(h))
-        return dx, dg, (q.runs(da).T @ uo, q.runs(db).T @ uo, dwd)
+        return expert_backward(xq[rows], dyq[rows], u[rows], dout[rows], g, wg, wu, wd, q)
 
     du = dout.copy()
     d_shared = []

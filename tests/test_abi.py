@@ -106,6 +106,13 @@ def test_null_and_workspace_errors_before_launch():
     assert lib.moe_backward(ctypes.byref(sb), *args, None, big, None) == 1                  # null workspace
     alias = [fake, fake, ctypes.byref(w), fake, fake, fake, fake, fake, ctypes.byref(wg)]  # du == u
     assert lib.moe_backward(ctypes.byref(sb), *alias, fake, big, None) == 1
+    # FP8_B128 backward: same shape rules; the weights must carry their block scales
+    s8 = moe.make_shape(64, 256, 16, 4, 1, 128, moe.MOE_DTYPE_FP8_B128)
+    n8 = ctypes.c_size_t(0)
+    assert lib.moe_backward_workspace_size(ctypes.byref(s8), ctypes.byref(n8)) == 0 and n8.value > 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(moe.make_shape(64, 256, 16, 4, 1, 192, moe.MOE_DTYPE_FP8_B128)),
+                                           ctypes.byref(n8)) == 2                           # I % 128
+    assert lib.moe_backward(ctypes.byref(s8), *args, fake, big, None) == 1                  # no weight scales
     assert lib.moe_update_bias(0, 10, fake, fake, ctypes.c_float(0.001), None) == 1
     assert lib.moe_quantize_weights(1, 100, 128, fake, fake, fake, None) == 2
     assert lib.moe_quantize_act(4, 130, fake, fake, fake, None) == 2

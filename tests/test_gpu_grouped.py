@@ -13,7 +13,7 @@ import torch
 import mixture_experts_layer_adjusted_amd as moe
 from oracle import moe_oracle as O
 from synth import bf16_bits_to_f32, host
-from synth.configs import CONFIGS
+from synth.configs import CONFIGS, LayerConfig
 from synth.device import host_to_device
 
 pytestmark = pytest.mark.gpu
@@ -88,9 +88,11 @@ def test_grouped_routing_feeds_the_forward():
 
 # ----------------------------------------------------------------------------- balance statistic (R15)
 
-@pytest.mark.parametrize("cid,seq_len", [(0, 16), (1, 1024), (1, 4096), (2, 64)])
+@pytest.mark.parametrize("cid,seq_len", [(0, 16), (1, 1024), (1, 4096), (2, 64), ("ragged", 96)])
 def test_seq_balance_parity(cid, seq_len):
-    cfg = CONFIGS[cid]
+    # "ragged": sequences of 96 tokens, one full and one partial chunk of 64 each
+    cfg = LayerConfig(75, "bal-ragged", 960, 256, 32, 4, 0, 128, "bf16", "uniform0.01") if cid == "ragged" \
+        else CONFIGS[cid]
     print(f"balance statistic: config {cid}, sequences of {seq_len}", flush=True)
     h = host.make_host_inputs(cfg, with_weights=False)
     dev = host_to_device(h)
