@@ -17,17 +17,17 @@
 //             amax is a reduction across the four wavefronts that share the row
 //   down:     Y[r, n] = H[r] . Wd[e][n] in bf16
 //
-// The layer backward runs its three GEMM kinds through the same kernel (the page lists the
+// The layer backward runs its three GEMM kinds on the same operand path (the page lists the
 // input-gradient and weight-gradient products as FP8 GEMMs too):
 //   plain:    the down form above with other operands: dH = dout W_down (weights transposed
 //             to [I, d] blocks) and dX = [dA dB] [W_gate; W_up] (transposed to [d, 2I])
 //   SwiGLU backward: the gate/up products recomputed, then from dH (before the gate, bf16)
 //             and the row gate: H, dA = g dH b SiLU'(a), dB = g dH SiLU(a) (bf16) and per row
 //             and 128-feature tile the partial sum of dH * H
-//   weight gradient: out_e[m, n] = sum over the rows k of segment e of A[m, k] B[n, k] with
-//             both operands transposed activations quantised per 1x128 run of rows, so the
-//             second operand also has one scale per row and K block, and K runs over the
-//             segment's rows only
+//   weight gradient (grouped_wgrad_fp8_kernel, persistent): out_e[m, n] = sum over the rows k
+//             of segment e of A[m, k] B[n, k] with both operands transposed activations
+//             quantised per 1x128 run of rows, so the second operand also has one scale per
+//             row and K block, and K runs over the segment's rows only
 //
 // Tiling: 512 threads (8 wavefronts, two per SIMD), 256 rows (two M-tiles of one segment;
 // a segment with an odd M-tile count ends in a half tile whose upper wavefronts idle) x
@@ -89,7 +89,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-// EPI: 0 plain bf16 store, 1 SwiGLU with H quantised, 2 SwiGLU backward, 3 weight gradient
+// EPI: 0 plain bf16 store, 1 SwiGLU with H quantised, 2 SwiGLU backward
 template <int EPI>
 __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands g, int NT) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
@@ -99,38 +99,21 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   const int b = blockIdx.x;
   const int64_t L = (int64_t)(b / (kXcds * kXcdChunk)) * (kXcds * kXcdChunk) + (b % kXcds) * kXcdChunk +
                     (b / kXcds) % kXcdChunk;
-  int seg, nt, tile_rows, nk;
-  int64_t m0, k_base;
-  if constexpr (EPI == 3) {
-    // weight gradient: segment seg's M x N matrix, K over the segment's rows
-    const int MT = (g.wg_m + kTM - 1) / kTM;
-    const int64_t per = (int64_t)MT * NT;
-    seg = (int)(L / per);
-    if (seg >= g.n_seg) return;
-    const int rem = (int)(L - (int64_t)seg * per);
-    nt = rem / MT;
-    m0 = (int64_t)(rem % MT) * kTM;
-    tile_rows = min(kTM, g.wg_m - (int)m0);
-    k_base = g.seg_off[seg];
-    nk = (g.seg_off[seg + 1] - g.seg_off[seg]) / kBK;
-  } else {
-    const int64_t slot = L / NT;
-    if (slot >= g.max_tiles) return;
-    seg = g.pair_seg[slot];
-    if (seg < 0) return;
-    const int seg_first = g.pair_off[seg];
-    const int seg_count = g.pair_off[seg + 1] - seg_first;
-    const int64_t lam = L - (int64_t)seg_first * NT;
-    const int grp = (int)(lam / (kGroupM * NT));
-    const int gm = min(kGroupM, seg_count - grp * kGroupM);
-    const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
-    const int local = grp * kGroupM + rem % gm;
-    nt = rem / gm;
-    m0 = (int64_t)g.seg_off[seg] + (int64_t)local * kTM;
-    tile_rows = min(kTM, g.seg_off[seg + 1] - (int)m0);  // 256, or 128 for a half tile
-    k_base = 0;
-    nk = g.K / kBK;
-  }
+  const int64_t slot = L / NT;
+  if (slot >= g.max_tiles) return;
+  const int seg = g.pair_seg[slot];
+  if (seg < 0) return;
+  const int seg_first = g.pair_off[seg];
+  const int seg_count = g.pair_off[seg + 1] - seg_first;
+  const int64_t lam = L - (int64_t)seg_first * NT;
+  const int grp = (int)(lam / (kGroupM * NT));
+  const int gm = min(kGroupM, seg_count - grp * kGroupM);
+  const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
+  const int local = grp * kGroupM + rem % gm;
+  const int nt = rem / gm;
+  const int64_t m0 = (int64_t)g.seg_off[seg] + (int64_t)local * kTM;
+  const int tile_rows = min(kTM, g.seg_off[seg + 1] - (int)m0);  // 256, or 128 for a half tile
+  const int nk = g.K / kBK;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -139,18 +122,14 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   const int n0 = nt * (SWIGLU ? kWRows / 2 : kWRows);
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
-  // row strides in bytes: the forward forms read rows of length K; the weight-gradient form reads
-  // transposed activations, rows of lda / ldw bytes, from column k_base on
-  const int64_t lda = EPI == 3 ? g.lda : K, ldw = EPI == 3 ? g.ldw : K;
   const size_t wstride = (size_t)N * K;
   const size_t sstride = (size_t)(N / kBK) * KB;  // scales per expert matrix
-  const uint8_t* W0 = EPI == 3 ? static_cast<const uint8_t*>(g.w_routed[0]) + k_base
-                               : static_cast<const uint8_t*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride;
+  const uint8_t* W0 = static_cast<const uint8_t*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride;
   const uint8_t* W1 =
       SWIGLU ? static_cast<const uint8_t*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride : nullptr;
-  const float* S0 = EPI == 3 ? nullptr : (shared ? g.s_shared[0] : g.s_routed[0]) + e * sstride;
+  const float* S0 = (shared ? g.s_shared[0] : g.s_routed[0]) + e * sstride;
   const float* S1 = SWIGLU ? (shared ? g.s_shared[1] : g.s_routed[1]) + e * sstride : nullptr;
-  const uint8_t* act = static_cast<const uint8_t*>(g.act) + k_base;
+  const uint8_t* act = static_cast<const uint8_t*>(g.act);
 
   // ---- direct-load sources as 32-bit byte offsets (the launcher checks the sizes): wave w fills
   // activation rows [32w, 32w+32) and weight-tile rows [32w, 32w+32), 8 rows of 128 bytes per
@@ -163,7 +142,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     const int64_t r = m0 + (row < tile_rows ? row : 0);  // rows past a half tile: a valid row
     int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;  // padding row: any valid row (outputs never read)
-    aoff[i] = (uint32_t)(tok * lda) + ((lslot ^ swz(row)) << 4);
+    aoff[i] = (uint32_t)(tok * K) + ((lslot ^ swz(row)) << 4);
   }
   uint32_t woff[kWDma];
 #pragma unroll
@@ -171,27 +150,20 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;  // 0..255 within the weight tile
     int n = n0 + (SWIGLU ? (r & (kWRows / 2 - 1)) : r);
     if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-    woff[i] = (uint32_t)((int64_t)n * ldw) + ((lslot ^ swz(kTM + r)) << 4);
+    woff[i] = (uint32_t)n * (uint32_t)K + ((lslot ^ swz(kTM + r)) << 4);
   }
   // gate rows (waves 0-3) come from W0, up rows (waves 4-7) from W1
   const uint8_t* wbase = (SWIGLU && wave >= kWaves / 2) ? W1 : W0;
   // ---- scale sources: lanes 0..31 of wave w load the activation scales of rows [32w, 32w+32)
   // into the stage's scale area; wave 7's lanes 32 and 33 load the scales of the tile's two
-  // 128-row weight blocks, landing right after the 256 row scales.  In the weight-gradient form
-  // lanes 32..63 of wave w load the scales of weight-tile rows [32w, 32w+32) in the same
-  // all-lane load, so wave w's 64 dwords hold its 32 activation-row scales, then its 32
-  // weight-row scales (index sidx_a / sidx_w below).
+  // 128-row weight blocks, landing right after the 256 row scales
   const float* ssrc = nullptr;
-  const int64_t lsa = EPI == 3 ? lda / kBK : KB;   // scale-row strides
   if (lane < 32) {
     const int row = wave * 32 + lane;
     const int64_t r = m0 + (row < tile_rows ? row : 0);
     int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;
-    ssrc = g.act_scale + tok * lsa + k_base / kBK;
-  } else if (EPI == 3) {
-    const int n = min(n0 + wave * 32 + lane - 32, N - 1);
-    ssrc = g.s_routed[0] + (int64_t)n * (ldw / kBK) + k_base / kBK;
+    ssrc = g.act_scale + tok * KB;
   } else if (wave == kWaves - 1 && lane < 34) {
     const int nb = lane - 32;
     if (SWIGLU) {
@@ -215,14 +187,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
           wbase + k0 + woff[i], (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
           0);
     // every wave has active lanes here, so every wave issues this load
-    if (EPI == 3)
-      __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 256), 4, 0, 0);
-    else if (ssrc)
-      __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
+    if (ssrc) __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
   };
-  // scale-area index of activation-tile row r and (weight-gradient form) weight-tile row j
-  auto sidx_a = [](int r) { return EPI == 3 ? 64 * (r >> 5) + (r & 31) : r; };
-  auto sidx_w = [](int j) { return 64 * (j >> 5) + 32 + (j & 31); };
 
   // weight rows of the wave's four 16-row blocks, and the 128-row scale block each falls in
   int wrow[kNB], wblk[kNB];
@@ -247,7 +213,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     for (int c = 0; c < kNB; ++c) acc[a][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (nk > 0) issue_stage(0);
+  issue_stage(0);
   for (int kt = 0; kt < nk; ++kt) {
     wait_vmcnt<0>();
     // a bare barrier: every wave's loads of stage kt have landed and stage kt-1 is no longer read
@@ -258,32 +224,23 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
       i32x8 wf[kNB];
       float sw[kNB];
-      f32x4 swr[kNB];   // weight-gradient form: the scales of the lane's four weight rows
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
-        if (EPI == 3)  // four consecutive weight rows of one group of 32
-          swr[nb] = *reinterpret_cast<const f32x4*>(sc + sidx_w(wrow[nb] + kq * 4));
-        else
-          sw[nb] = sc[kTM + wblk[nb]];
+        sw[nb] = sc[kTM + wblk[nb]];
       }
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         const int r = mrow0 + mb * 16 + l16;
         const i32x8 xf = frag32(st, r, kq * 2);
-        const float sa = sc[sidx_a(r)];
+        const float sa = sc[r];
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
           const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb], xf, zero, 0, 0, 0, kE8M0One, 0,
                                                                               kE8M0One);
-          if (EPI == 3) {
+          const float f = sa * sw[nb];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], sa * swr[nb][v], acc[mb][nb][v]);
-          } else {
-            const float f = sa * sw[nb];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], f, acc[mb][nb][v]);
-          }
+          for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], f, acc[mb][nb][v]);
         }
       }
     }
@@ -374,9 +331,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       }
     }
   } else if (active) {
-    // weight gradient: segment e's matrix of the routed or shared output
-    uint16_t* out = EPI == 3 ? static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N
-                             : static_cast<uint16_t*>(g.out);
+    uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       uint16_t* orow = out + (m0 + mrow0 + mb * 16 + l16) * N;
@@ -392,18 +347,213 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   }
 }
 
+// Weight gradient, persistent: out_e[m, n] = sum over the rows k of segment e of A[m, k] B[n, k]
+// (both operands transposed activations, one scale per row and 128-row K block).  An expert's
+// segment holds a few hundred rows, so a 256 x 256 output tile has only a few K-steps and a
+// one-tile workgroup spends most of its time filling its pipeline and draining its stores.
+// Here each workgroup walks a fixed sequence of tiles (logical tile i * G + 32 x + j for the
+// workgroup in slot j of XCD x, G workgroups, so an XCD keeps a run of one expert's tiles) and
+// the loads of a tile's first K-step go out during the last K-step of the tile before it, so
+// they overlap that tile's stores.  The stage ring runs on across tiles: the consumed and
+// issued stage counts pick the LDS buffer.
+__global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperands g, int NT, int64_t n_tiles) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int N = g.N;
+  const int64_t lda = g.lda, ldw = g.ldw;
+  const int MT = (g.wg_m + kTM - 1) / kTM;
+  const int64_t per = (int64_t)MT * NT;
+  const int64_t G = gridDim.x;
+  int64_t L = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+  if (L >= n_tiles) return;
+
+  struct Tile {
+    int seg, nt, tile_rows, nk;
+    int64_t m0, k_base;
+  };
+  auto describe = [&](int64_t l) {
+    Tile t;
+    t.seg = (int)(l / per);
+    const int rem = (int)(l - (int64_t)t.seg * per);
+    t.nt = rem / MT;
+    t.m0 = (int64_t)(rem % MT) * kTM;
+    t.tile_rows = min(kTM, g.wg_m - (int)t.m0);
+    t.k_base = g.seg_off[t.seg];
+    t.nk = (int)((g.seg_off[t.seg + 1] - t.k_base) / kBK);
+    return t;
+  };
+  // per-lane load sources of the tile being loaded (as in grouped_gemm_fp8_kernel): 32-bit byte
+  // offsets from the wave-uniform bases act_base / w_base; lanes 0..31 load activation-row scales,
+  // lanes 32..63 weight-row scales, wave w's 64 dwords landing at [64w, 64w + 64)
+  const int lrow = lane >> 3, lslot = lane & 7;
+  uint32_t aoff[kADma], woff[kWDma];
+  const uint8_t* act_base = nullptr;
+  const uint8_t* w_base = nullptr;
+  const float* ssrc = nullptr;
+  auto prepare = [&](const Tile& t) {
+    const int n0 = t.nt * kWRows;
+#pragma unroll
+    for (int i = 0; i < kADma; ++i) {
+      const int row = wave * (kTM / kWaves) + i * kRowsPerDma + lrow;
+      aoff[i] = (uint32_t)((t.m0 + (row < t.tile_rows ? row : 0)) * lda) + ((lslot ^ swz(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < kWDma; ++i) {
+      const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;
+      woff[i] = (uint32_t)((int64_t)min(n0 + r, N - 1) * ldw) + ((lslot ^ swz(kTM + r)) << 4);
+    }
+    act_base = static_cast<const uint8_t*>(g.act) + t.k_base;
+    w_base = static_cast<const uint8_t*>(g.w_routed[0]) + t.k_base;
+    if (lane < 32) {
+      const int row = wave * 32 + lane;
+      ssrc = g.act_scale + (t.m0 + (row < t.tile_rows ? row : 0)) * (lda / kBK) + t.k_base / kBK;
+    } else {
+      ssrc = g.s_routed[0] + (int64_t)min(n0 + wave * 32 + lane - 32, N - 1) * (ldw / kBK) + t.k_base / kBK;
+    }
+  };
+  int issued = 0, consumed = 0;
+  auto issue = [&](int kt) {
+    uint8_t* st = lds + (issued % kStages) * kStageBytes;
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < kADma; ++i)
+      __builtin_amdgcn_global_load_lds(act_base + k0 + aoff[i],
+                                       (lds_void_t*)(st + (wave * (kTM / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
+                                       0);
+#pragma unroll
+    for (int i = 0; i < kWDma; ++i)
+      __builtin_amdgcn_global_load_lds(
+          w_base + k0 + woff[i], (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
+          0);
+    __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 256), 4, 0, 0);
+    ++issued;
+  };
+
+  int wrow[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) wrow[nb] = wn * 64 + nb * 16;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int mrow0 = wm * (kTM / 2);
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  Tile cur = describe(L);
+  prepare(cur);
+  if (cur.nk > 0) issue(0);
+  while (true) {
+    const int64_t Ln = L + G;
+    const bool has_next = Ln < n_tiles;
+    // the next tile's first K-step, issued once this tile's last one is being computed
+    auto prefetch_next = [&]() {
+      if (!has_next) return;
+      const Tile t = describe(Ln);
+      if (t.nk > 0) {
+        prepare(t);
+        issue(0);
+      }
+    };
+    const bool active = mrow0 < cur.tile_rows;   // false only for the upper half of a half tile
+    f32x4 acc[kMB][kNB];
+#pragma unroll
+    for (int a = 0; a < kMB; ++a)
+#pragma unroll
+      for (int c = 0; c < kNB; ++c) acc[a][c] = zero;
+    for (int kt = 0; kt < cur.nk; ++kt) {
+      wait_vmcnt<0>();
+      // a bare barrier: stage `consumed` has landed and the other buffer is no longer read
+      __builtin_amdgcn_s_barrier();
+      if (kt + 1 < cur.nk)
+        issue(kt + 1);
+      else
+        prefetch_next();
+      if (active) {
+        const uint8_t* st = lds + (consumed % kStages) * kStageBytes;
+        const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
+        i32x8 wf[kNB];
+        f32x4 swr[kNB];   // scales of the lane's four weight rows (one group of 32)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
+          const int j = wrow[nb] + kq * 4;
+          swr[nb] = *reinterpret_cast<const f32x4*>(sc + 64 * (j >> 5) + 32 + (j & 31));
+        }
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) {
+          const int r = mrow0 + mb * 16 + l16;
+          const i32x8 xf = frag32(st, r, kq * 2);
+          const float sa = sc[64 * (r >> 5) + (r & 31)];
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) {
+            const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb], xf, zero, 0, 0, 0, kE8M0One,
+                                                                                0, kE8M0One);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[mb][nb][v] = fmaf(part[v], sa * swr[nb][v], acc[mb][nb][v]);
+          }
+        }
+      }
+      ++consumed;
+    }
+    // a tile without K-steps (an empty segment) prefetched nothing for the next one
+    if (cur.nk == 0) prefetch_next();
+    // ---- epilogue: segment cur.seg's matrix of the routed or shared output (an empty segment
+    // writes zeros); lane holds row mrow0 + 16 mb + l16, features 4 kq + (0..3) of each block
+    if (active) {
+      const bool shared = cur.seg >= g.n_routed;
+      const int e = shared ? cur.seg - g.n_routed : cur.seg;
+      uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
+      const int n0 = cur.nt * kWRows;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        uint16_t* orow = out + (cur.m0 + mrow0 + mb * 16 + l16) * N;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const int f = n0 + wrow[nb] + kq * 4;  // N is a multiple of 128, so f < N covers f + 3
+          if (f < N)
+            *reinterpret_cast<uint2*>(orow + f) =
+                make_uint2((uint32_t)f32_to_bf16(acc[mb][nb][0]) | ((uint32_t)f32_to_bf16(acc[mb][nb][1]) << 16),
+                           (uint32_t)f32_to_bf16(acc[mb][nb][2]) | ((uint32_t)f32_to_bf16(acc[mb][nb][3]) << 16));
+        }
+      }
+    }
+    if (!has_next) break;
+    cur = describe(Ln);
+    L = Ln;
+  }
+}
+
+hipError_t launch_wgrad_fp8(const GemmOperands& g, hipStream_t st) {
+  if (g.K % kBK != 0 || g.N % kBK != 0 || g.wg_m % kBK != 0 || g.lda % kBK != 0 || g.ldw % kBK != 0)
+    return hipErrorInvalidValue;
+  if ((int64_t)g.wg_m * g.lda >= (int64_t(1) << 32) || (int64_t)g.N * g.ldw >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
+  const size_t lds_bytes = kStages * kStageBytes;
+  static bool attr_set = false;
+  static int n_cu = 0;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_fp8_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (err != hipSuccess) return err;
+    int dev = 0;
+    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+    if ((err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
+    attr_set = true;
+  }
+  const int NT = (int)ceil_div(g.N, kWRows);
+  const int64_t tiles = (int64_t)g.n_seg * ceil_div(g.wg_m, kTM) * NT;
+  if (tiles == 0) return hipSuccess;
+  // one workgroup per CU (the LDS stages allow no more), a multiple of the XCD count
+  const int64_t grid = std::max<int64_t>(kXcds, (int64_t)n_cu / kXcds * kXcds);
+  hipLaunchKernelGGL(grouped_wgrad_fp8_kernel, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT, tiles);
+  return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
   if (g.K % kBK != 0 || g.N % kBK != 0) return hipErrorInvalidValue;
   // 32-bit byte offsets address the activation matrix and one expert's weight matrix
-  if (EPI == 3) {
-    if (g.wg_m % kBK != 0 || g.lda % kBK != 0 || g.ldw % kBK != 0) return hipErrorInvalidValue;
-    if ((int64_t)g.wg_m * g.lda >= (int64_t(1) << 32) || (int64_t)g.N * g.ldw >= (int64_t(1) << 32))
-      return hipErrorInvalidValue;
-  } else if (g.act_rows * g.K >= (int64_t(1) << 32) || (int64_t)g.N * g.K >= (int64_t(1) << 32)) {
-    return hipErrorInvalidValue;
-  }
+  if (g.act_rows * g.K >= (int64_t(1) << 32) || (int64_t)g.N * g.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const size_t lds_bytes = kStages * kStageBytes;
   static bool attr_set = false;
   if (!attr_set) {
@@ -413,7 +563,7 @@ hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
     attr_set = true;
   }
   const int NT = (int)ceil_div(g.N, SWIGLU ? kWRows / 2 : kWRows);
-  const int64_t tiles = EPI == 3 ? (int64_t)g.n_seg * ceil_div(g.wg_m, kTM) * NT : g.max_pairs * NT;
+  const int64_t tiles = g.max_pairs * NT;
   const int64_t grid = ceil_div(tiles, kXcds * kXcdChunk) * (kXcds * kXcdChunk);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_fp8_kernel<EPI>, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT);
@@ -425,6 +575,6 @@ hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
 hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st) { return launch_fp8<1>(g, st); }
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st) { return launch_fp8<0>(g, st); }
 hipError_t launch_gemm_fp8_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_fp8<2>(g, st); }
-hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st) { return launch_fp8<3>(g, st); }
+hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st) { return launch_wgrad_fp8(g, st); }
 
 }  // namespace moe
