@@ -63,6 +63,14 @@ constexpr int kStageElems = (kTileM + kWRows) * kBK;  // bf16 elements per LDS s
 #endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// K-major weight tile in LDS: BK rows of 256 features (512 bytes); the 16-byte feature chunk c
+// of row r sits at slot c ^ kn_swz(r), so that the eight rows a transposing read touches (rows
+// kb..kb+3 and kb+8..kb+11 at one 32-feature block) fall on distinct bank groups
+__device__ __forceinline__ int kn_swz(int r) { return 4 * (r & 3); }
+__device__ __forceinline__ int kn_off(int r, int col) { return r * 256 + (((col >> 3) ^ kn_swz(r)) << 3) + (col & 7); }
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -351,9 +359,13 @@ __device__ __forceinline__ void store_swiglu_bwd(const f32x16 (&acc)[MB][2], con
 }
 
 // EPI: 0 plain store (down GEMM), 1 SwiGLU (gate/up GEMM), 2 SwiGLU backward (gate/up recomputed)
-template <int EPI, int BK, int WAVES, int WROWS, int WGS, int WM, int TM>
+// WKN: the weight operand is stored with K as its row index ([K][N], N contiguous), as a
+// weight matrix is for an input-gradient product; see kn_off below
+template <int EPI, int BK, int WAVES, int WROWS, int WGS, int WM, int TM, bool WKN = false>
 __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kernel(GemmOperands g, int NT) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
+  static_assert(!WKN || (EPI == 0 && BK == 64 && WROWS == 256 && WAVES == 8 && TM == 256),
+                "K-major weights: the 256 x 256 plain-store tile");
   using C = StreamCfg<BK, WAVES, WROWS, WGS, TM>;
   constexpr int WN = WAVES / WM;           // wavefront grid WM x WN
   constexpr int RW = TM / WM;              // rows per wavefront
@@ -409,14 +421,19 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   const int n0 = nt * (SWIGLU ? WROWS / 2 : WROWS);
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
-  const size_t wstride = (size_t)N * K;
+  // K-major weights may be two matrices stacked along K: rows [0, kn_split) of the first,
+  // the rest of the second (the gate and up weights of one expert)
+  const int kn_split = WKN ? g.kn_split : K;
+  const size_t wstride = (size_t)N * (WKN ? kn_split : K);
   // row strides (elements): the forward reads rows of length K; the weight-gradient mode reads
-  // the transposed activations, rows of length lda / ldw, from column k_base on
-  const int64_t lda = EPI == 3 ? g.lda : K, ldw = EPI == 3 ? g.ldw : K;
+  // the transposed activations, rows of length lda / ldw, from column k_base on; K-major
+  // weights have rows of length N
+  const int64_t lda = EPI == 3 ? g.lda : K, ldw = EPI == 3 ? g.ldw : (WKN ? N : K);
   const char* W0 = EPI == 3 ? static_cast<const char*>(g.w_routed[0]) + k_base * 2
                             : static_cast<const char*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride * 2;
-  const char* W1 = SWIGLU ? static_cast<const char*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride * 2
-                          : nullptr;
+  const char* W1 = SWIGLU || (WKN && kn_split < K)
+                       ? static_cast<const char*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride * 2
+                       : nullptr;
   const char* act = static_cast<const char*>(g.act) + k_base * 2;
 
   // ---- per-lane sources, as 32-bit byte offsets from a wave-uniform base (the launcher checks that
@@ -438,10 +455,19 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   uint32_t woff[C::kWDma];
 #pragma unroll
   for (int i = 0; i < C::kWDma; ++i) {
-    const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;  // row within the weight tile
-    int n = n0 + (SWIGLU ? r % (WROWS / 2) : r);
-    if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-    woff[i] = (uint32_t)(n * ldw * 2) + ((lslot ^ C::swz(TM + r)) << 4);
+    if constexpr (WKN) {
+      // K-major weight tile: BK rows of WROWS features (512 bytes), two rows per 1 KB load; lane
+      // l fills row 2 (4 w + i) + l / 32 at slot l % 32, which holds feature chunk slot ^ kn_swz(row)
+      const int kr = 2 * (wave * C::kWDma + i) + (lane >> 5);
+      int n = n0 + 8 * ((lane & 31) ^ kn_swz(kr));
+      if (n + 8 > N) n = N - 8;  // beyond the last feature: any valid chunk (outputs masked)
+      woff[i] = (uint32_t)((kr * ldw + n) * 2);
+    } else {
+      const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;  // row within the weight tile
+      int n = n0 + (SWIGLU ? r % (WROWS / 2) : r);
+      if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
+      woff[i] = (uint32_t)(n * ldw * 2) + ((lslot ^ C::swz(TM + r)) << 4);
+    }
   }
   // gate rows come from W0, up rows from W1; the split falls on a wave boundary
   const char* wbase = (SWIGLU && wave * (WROWS / WAVES) >= WROWS / 2) ? W1 : W0;
@@ -451,9 +477,13 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
 #pragma unroll
     for (int i = 0; i < C::kADma; ++i)
       lds_dma16(act + k0 + aoff[i], st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
+    // K-major weights advance by BK rows per step, switching matrix at kn_split
+    const int kr0 = kt * BK;
+    const char* wb = !WKN ? wbase + k0
+                          : (kr0 < kn_split ? W0 + (int64_t)kr0 * ldw * 2 : W1 + (int64_t)(kr0 - kn_split) * ldw * 2);
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i)
-      lds_dma16(wbase + k0 + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
+      lds_dma16(wb + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
   };
 
   f32x16 acc[MB][NBW];
@@ -497,8 +527,23 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
         for (int mb = 0; mb < MB; ++mb)
           xf[buf][mb] = *reinterpret_cast<const bf16x8*>(st + C::off(mrow0 + mb * 32 + l32, c));
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-          wf[buf][nb] = *reinterpret_cast<const bf16x8*>(st + C::off(TM + wrow[nb] + l32, c));
+        for (int nb = 0; nb < NBW; ++nb) {
+          if constexpr (WKN) {
+            // two transposing reads (ds_read_b64_tr_b16) give the lane K rows kb..kb+3 and
+            // kb+4..kb+7 of feature wrow + l32: within each 16-lane group, lane s names row
+            // kb + s / 4 at features +4 (s % 4)..+3 of the group's 16, and receives its own
+            // feature's four rows
+            const int kb = kk * 16 + khalf * 8;
+            const int col = wrow[nb] + (l32 & 16) + 4 * (lane & 3);
+            const int r0 = kb + ((lane & 15) >> 2);
+            const uint16_t* wt = st + TM * BK;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wt + kn_off(r0, col)));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wt + kn_off(r0 + 4, col)));
+            wf[buf][nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            wf[buf][nb] = *reinterpret_cast<const bf16x8*>(st + C::off(TM + wrow[nb] + l32, c));
+          }
+        }
       };
       load_frags(0, 0);
 #pragma unroll
@@ -538,13 +583,13 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   }
 }
 
-template <int EPI, int SBK, int SW, int SR, int SG, int SM, int STM>
+template <int EPI, int SBK, int SW, int SR, int SG, int SM, int STM, bool WKN = false>
 hipError_t launch_stream(const GemmOperands& g, hipStream_t st) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
   using SC = StreamCfg<SBK, SW, SR, SG, STM>;
   const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
   const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
-  auto kern = &grouped_gemm_bf16_stream_kernel<EPI, SBK, SW, SR, SG, SM, STM>;
+  auto kern = &grouped_gemm_bf16_stream_kernel<EPI, SBK, SW, SR, SG, SM, STM, WKN>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -605,5 +650,15 @@ hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st) { retu
 hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st) { return launch_bf16<0>(g, st); }
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_bf16<2>(g, st); }
 hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st) { return launch_bf16<3>(g, st); }
+
+// Input-gradient product on K-major weights (as stored), no transposed copy: out[r, n] =
+// sum_k act[r, k] W[k, n] with W = rows [0, kn_split) of w_*[0] then the rest of w_*[1]
+hipError_t launch_gemm_bf16_dgrad(const GemmOperands& g, hipStream_t st) {
+  if (g.K % 64 != 0 || g.N % 128 != 0 || g.kn_split % 64 != 0 || g.kn_split <= 0 || g.kn_split > g.K)
+    return hipErrorInvalidValue;
+  // 32-bit byte offsets: the activation matrix; the weight offsets stay within one stage's rows
+  if (g.act_rows * g.K * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  return launch_stream<0, 64, 8, 256, 1, 2, 256, true>(g, st);
+}
 
 }  // namespace moe

@@ -14,6 +14,7 @@ hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_bf16_dgrad(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_swiglu_bwd(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st);
 
@@ -83,8 +84,9 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.bwd_dg_part = take((size_t)p.max_rows * (I / 128 > 0 ? I / 128 : 1) * 4);
   const size_t eb = fp8 ? 1 : 2;   // bytes per element of the transposed copies
   const int64_t P = p.max_rows, d8 = d / 128, i8 = I / 128, p8 = P / 128;
-  p.bwd_wd_t = take((size_t)(N + Ns) * I * d * eb);
-  p.bwd_wc_t = take((size_t)(N + Ns) * d * 2 * I * eb);
+  // transposed weight copies: FP8 only (the bf16 input-gradient products read the weights as stored)
+  p.bwd_wd_t = take(fp8 ? (size_t)(N + Ns) * I * d * eb : 0);
+  p.bwd_wc_t = take(fp8 ? (size_t)(N + Ns) * d * 2 * I * eb : 0);
   p.bwd_dy_t = take((size_t)d * P * eb);
   p.bwd_h_t = take((size_t)I * P * eb);
   p.bwd_dab_t = take((size_t)2 * I * P * eb);
@@ -536,8 +538,6 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
     return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, seg_rows, d_centroids, stream));
   }
   const int64_t Nr = s.n_routed, Ns = s.n_shared, P = p.max_rows;
-  uint16_t* wd_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_wd_t);   // [N_r + N_s][I][d]
-  uint16_t* wc_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_wc_t);   // [N_r + N_s][d][2I]
   uint16_t* dy_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_dy_t);   // [d][P]
   uint16_t* h_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_h_t);     // [I][P]
   uint16_t* dab_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_dab_t); // [2I][P]
@@ -588,24 +588,10 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
   };
 
   if (T > 0) {
-    // K-contiguous copies of the weights for the input-gradient GEMMs:
-    // W_down^T [I][d] and [W_gate; W_up]^T [d][2I] per expert
-    if ((rc = transpose(w->w_down, I, d * I, nullptr, nullptr, wd_t, d, 0, I * d, d, I, Nr)) != MOE_OK) return rc;
-    if ((rc = transpose(w->w_gate, d, I * d, nullptr, nullptr, wc_t, 2 * I, 0, d * 2 * I, I, d, Nr)) != MOE_OK) return rc;
-    if ((rc = transpose(w->w_up, d, I * d, nullptr, nullptr, wc_t, 2 * I, I, d * 2 * I, I, d, Nr)) != MOE_OK) return rc;
-    if (Ns > 0) {
-      if ((rc = transpose(w->sh_down, I, d * I, nullptr, nullptr, wd_t + Nr * I * d, d, 0, I * d, d, I, Ns)) != MOE_OK)
-        return rc;
-      if ((rc = transpose(w->sh_gate, d, I * d, nullptr, nullptr, wc_t + Nr * d * 2 * I, 2 * I, 0, d * 2 * I, I, d,
-                          Ns)) != MOE_OK)
-        return rc;
-      if ((rc = transpose(w->sh_up, d, I * d, nullptr, nullptr, wc_t + Nr * d * 2 * I, 2 * I, I, d * 2 * I, I, d,
-                          Ns)) != MOE_OK)
-        return rc;
-    }
-    // dH (before the gate) = dout[token] W_down
-    GemmOperands g1 = grouped(dout, row_token, T, wd_t, wd_t + Nr * I * d, (int)d, (int)I, dhu);
-    if ((rc = hip_status(launch_gemm_bf16_down(g1, stream))) != MOE_OK) return rc;
+    // dH (before the gate) = dout[token] W_down, W_down [d][I] read K-major as stored
+    GemmOperands g1 = grouped(dout, row_token, T, bf(w->w_down), bf(w->sh_down), (int)d, (int)I, dhu);
+    g1.kn_split = (int)d;
+    if ((rc = hip_status(launch_gemm_bf16_dgrad(g1, stream))) != MOE_OK) return rc;
     // gate/up recomputed: [dA dB], H and the gate-gradient partials
     GemmOperands g2 = grouped(u, row_token, T, nullptr, nullptr, (int)d, (int)I, dab);
     g2.w_routed[0] = w->w_gate;
@@ -617,9 +603,12 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
     g2.out2 = hb;
     g2.dg_part = dg_part;
     if ((rc = hip_status(launch_gemm_bf16_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
-    // dX = [dA dB] [W_gate; W_up]
-    GemmOperands g3 = grouped(dab, nullptr, P, wc_t, wc_t + Nr * d * 2 * I, (int)(2 * I), (int)d, dx);
-    if ((rc = hip_status(launch_gemm_bf16_down(g3, stream))) != MOE_OK) return rc;
+    // dX = [dA dB] [W_gate; W_up]: K rows [0, I) from W_gate [I][d], [I, 2I) from W_up, as stored
+    GemmOperands g3 = grouped(dab, nullptr, P, bf(w->w_gate), bf(w->sh_gate), (int)(2 * I), (int)d, dx);
+    g3.w_routed[1] = w->w_up;
+    g3.w_shared[1] = w->sh_up;
+    g3.kn_split = (int)I;
+    if ((rc = hip_status(launch_gemm_bf16_dgrad(g3, stream))) != MOE_OK) return rc;
     // router backward and du
     if ((rc = hip_status(launch_router_bwd(s, u, centroids, topk_idx, perm_row, dg_part, seg_off, dout, dx, du,
                                            row_dz, stream))) != MOE_OK)

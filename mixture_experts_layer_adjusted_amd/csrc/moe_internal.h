@@ -140,6 +140,9 @@ struct GemmOperands {
   // routed segments write out + e M N, shared ones out2 + (e - N_r) M N
   int64_t lda, ldw;
   int wg_m, n_seg;
+  // input-gradient mode (bf16): the weights are read K-major, as stored ([K rows][N features] per
+  // expert, the w_*[0] matrix for K rows [0, kn_split), the w_*[1] matrix for the rest)
+  int kn_split;
   // expected routed rows per expert (T K_r / N_r) below one M-tile: the bf16 forward GEMMs take
   // 128-row tiles with more weight rows
   bool small_segments;
