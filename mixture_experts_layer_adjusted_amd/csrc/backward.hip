@@ -241,52 +241,6 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
   }
 }
 
-// FP8 weights transposed with their block scales: dst[b][c * ldd + off + r] = src[b][r * lds + c]
-// (bytes) for r < R, c < C, R and C multiples of 128.  A 128 x 128 tile goes through LDS as
-// 32-bit words tile[c][p] that pack rows 4p..4p+3 of column c: each thread loads 16 columns of
-// four rows (four 16-byte loads); the store phase writes 16 consecutive rows of one column.
-// A 128 x 128 block of the stored matrix is a block of the transposed one, so its E4M3 codes
-// and its scale carry over unchanged.
-__global__ void __launch_bounds__(256) transpose_b8_kernel(TransposeB8Args a) {
-  __shared__ uint32_t tile[128][33];
-  const int64_t b = blockIdx.z;
-  const int r0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
-  const uint8_t* src = a.src + b * a.src_bstride;
-  uint8_t* dst = a.dst + b * a.dst_bstride;
-  const int tid = threadIdx.x;
-  {
-    const int p = tid & 31, cg = tid >> 5;       // rows 4p..4p+3, columns 16cg..16cg+15
-    uint32_t w[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 q = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + 4 * p + j) * a.lds + c0 + 16 * cg);
-      w[j][0] = q.x;
-      w[j][1] = q.y;
-      w[j][2] = q.z;
-      w[j][3] = q.w;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int sh = 8 * (k & 3);
-      const uint32_t v = ((w[0][k >> 2] >> sh) & 0xFFu) | (((w[1][k >> 2] >> sh) & 0xFFu) << 8) |
-                         (((w[2][k >> 2] >> sh) & 0xFFu) << 16) | (((w[3][k >> 2] >> sh) & 0xFFu) << 24);
-      tile[16 * cg + k][p] = v;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = tid + 256 * i;                  // 1024 stores of 16 rows
-    const int c = v >> 3, q = v & 7;
-    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * a.ldd + a.off + r0 + 16 * q) =
-        make_uint4(tile[c][4 * q], tile[c][4 * q + 1], tile[c][4 * q + 2], tile[c][4 * q + 3]);
-  }
-  // the block's scale: [R/128][C/128] -> [C/128][ldds] at column off/128
-  if (tid == 0)
-    a.dst_scale[b * a.dst_scale_bstride + (int64_t)blockIdx.y * a.ldds + a.off / 128 + blockIdx.x] =
-        a.src_scale[b * a.src_scale_bstride + (int64_t)blockIdx.x * (a.C / 128) + blockIdx.y];
-}
-
 // Activations transposed and quantised along the rows: for column c and each run of 128 rows
 // j0..j0+127 (j0 a multiple of 128), v[j] = scale[j] * src[gather ? row_token[j] : j][c] in fp32
 // (0 where row_token[j] < 0), one scale amax / 448 (1 when the run is all zero) and the E4M3 codes
@@ -383,14 +337,6 @@ hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* ro
 }  // namespace moe
 
 namespace moe {
-
-hipError_t launch_transpose_b8(const TransposeB8Args& a, int batch, hipStream_t st) {
-  if (a.R == 0 || a.C == 0 || batch == 0) return hipSuccess;
-  if (a.R % 128 != 0 || a.C % 128 != 0 || a.off % 128 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_b8_kernel, dim3((unsigned)(a.R / 128), (unsigned)(a.C / 128), (unsigned)batch),
-                     dim3(256), 0, st, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_transpose_quant(const TransposeQuantArgs& a, hipStream_t st) {
   if (a.rows == 0 || a.C == 0) return hipSuccess;

@@ -9,27 +9,23 @@
 // GEMM reads token rows straight from u through row_token, so the permuted
 // activation matrix is never materialised.
 //
-// Tiling: a workgroup of 256 threads (4 wavefronts) owns 128 rows x 256 weight
-// rows (gate/up: 128 gate + the matching 128 up features; down: 256 output
-// features) and walks K in 64-wide steps through a double-buffered LDS stage
-// (16 KB activations + 32 KB weights per stage).  Each wavefront computes 64 rows x
-// 4 blocks of 32 weight rows with 8 MFMA accumulators; the MFMA's A operand is the
-// weight tile and its B operand the activation tile, so each lane ends up holding
-// four runs of 4 consecutive output features of one row.  LDS rows are 128 bytes,
-// XOR-swizzled in 16-byte chunks so that fragment reads are free of bank conflicts.
-//
-// Two variants share that tiling:
-//  * the streaming kernel (contraction length a multiple of 64; 8 wavefronts on a
-//    128 x 512 tile) fills two LDS stages with direct global->LDS loads
-//    (global_load_lds_dwordx4) one K-step ahead of the MFMAs, and takes its tile
-//    from an XCD-aware order: the 8 XCDs
-//    of MI355X each receive workgroups round-robin, so workgroup b runs on XCD
-//    b % 8; logical tiles are handed out so that the 32 workgroups an XCD holds at
-//    once form one block of 4 M-tiles x 8 N-tiles of the same expert (operands
-//    reused through that XCD's L2), and tiles are ordered expert by expert (each
-//    expert's weights pass through the shared last-level cache about once);
-//  * the register-staged kernel (any contraction length that is a multiple of 8)
-//    loads through registers with zero fill of the K tail, in plain grid order.
+// Two kernels:
+//  * the streaming kernel (contraction length a multiple of 64): a workgroup of 8 wavefronts
+//    owns 256 rows (two M-tiles of one segment) x 256 weight rows (gate/up: 128 gate + the
+//    matching 128 up features; down: 256 output features), or 128 rows x 512 weight rows when
+//    segments hold few rows (decode-like batches).  Each wavefront computes 128 x 64 with
+//    v_mfma_f32_32x32x16_bf16; the MFMA's A operand is the weight tile and its B operand the
+//    activation tile, so a lane ends with runs of four consecutive output features of one row.
+//    Two 64 KB LDS stages are filled by direct global->LDS loads (global_load_lds_dwordx4) one
+//    K-step ahead; LDS rows are XOR-swizzled in 16-byte chunks so that fragment reads are free
+//    of bank conflicts.  Tiles come in an XCD-aware order: the 8 XCDs of MI355X each receive
+//    workgroups round-robin, so workgroup b runs on XCD b % 8, and logical tiles are handed out
+//    so that the 32 workgroups an XCD holds at once form one block of M-tiles x N-tiles of the
+//    same expert (operands reused through that XCD's L2), experts in order.  The backward uses
+//    it with other epilogues (SwiGLU backward, weight gradients) and, for the input-gradient
+//    products, with the weights read K-major as stored through transposing LDS reads;
+//  * the register-staged kernel (any contraction length that is a multiple of 8): 4 wavefronts
+//    on 128 x 256, loads through registers with zero fill of the K tail, in plain grid order.
 #include "moe_internal.h"
 
 namespace moe {

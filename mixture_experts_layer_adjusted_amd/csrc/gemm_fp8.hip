@@ -63,11 +63,19 @@ constexpr int kMB = 8;              // 16-row token blocks per wavefront
 constexpr int kNB = 4;              // 16-row weight blocks per wavefront
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// K-major weight tile (input-gradient products): 128 K rows of 256 feature bytes; the 16-byte
+// feature chunk c of row r sits at slot c ^ kn8_swz(r), so that the 32 rows one transposing read
+// touches (8 j + 0..7 in each K quarter) fall on each bank group twice
+__device__ __forceinline__ int kn8_swz(int r) { return (r & 7) | (((r >> 5) & 1) << 3); }
+__device__ __forceinline__ int kn8_off(int r, int col) { return r * 256 + (((col >> 4) ^ kn8_swz(r)) << 4) + (col & 15); }
 __device__ __forceinline__ int boff(int r, int c) { return r * kBK + ((c ^ swz(r)) << 4); }  // c: 16-byte chunk
 
 template <int N>
@@ -89,10 +97,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-// EPI: 0 plain bf16 store, 1 SwiGLU with H quantised, 2 SwiGLU backward
-template <int EPI>
+// EPI: 0 plain bf16 store, 1 SwiGLU with H quantised, 2 SwiGLU backward.
+// WKN (with EPI 0): the weight codes are read K-major as stored ([K rows][N features] per
+// expert, rows [0, kn_split) of w_*[0] and the rest of w_*[1]; block scales [K/128][N/128]),
+// through transposing LDS reads, for the input-gradient products of the backward
+template <int EPI, bool WKN = false>
 __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands g, int NT) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
+  static_assert(!WKN || EPI == 0, "K-major weights: plain store");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ float row_red[kTM][4];   // per-row reductions across the four wavefronts of a row
   // ---- logical tile (same XCD-aware order as the bf16 streaming kernels, over 256-row tiles)
@@ -122,13 +134,15 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   const int n0 = nt * (SWIGLU ? kWRows / 2 : kWRows);
   const bool shared = seg >= g.n_routed;
   const int e = shared ? seg - g.n_routed : seg;
-  const size_t wstride = (size_t)N * K;
-  const size_t sstride = (size_t)(N / kBK) * KB;  // scales per expert matrix
+  const int kn_split = WKN ? g.kn_split : K;   // K rows of the first stacked matrix
+  const size_t wstride = (size_t)N * kn_split;
+  const size_t sstride = (size_t)(N / kBK) * (kn_split / kBK);  // scales per expert matrix
+  const bool two = SWIGLU || (WKN && kn_split < K);
   const uint8_t* W0 = static_cast<const uint8_t*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride;
   const uint8_t* W1 =
-      SWIGLU ? static_cast<const uint8_t*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride : nullptr;
+      two ? static_cast<const uint8_t*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride : nullptr;
   const float* S0 = (shared ? g.s_shared[0] : g.s_routed[0]) + e * sstride;
-  const float* S1 = SWIGLU ? (shared ? g.s_shared[1] : g.s_routed[1]) + e * sstride : nullptr;
+  const float* S1 = two ? (shared ? g.s_shared[1] : g.s_routed[1]) + e * sstride : nullptr;
   const uint8_t* act = static_cast<const uint8_t*>(g.act);
 
   // ---- direct-load sources as 32-bit byte offsets (the launcher checks the sizes): wave w fills
@@ -147,10 +161,19 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   uint32_t woff[kWDma];
 #pragma unroll
   for (int i = 0; i < kWDma; ++i) {
-    const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;  // 0..255 within the weight tile
-    int n = n0 + (SWIGLU ? (r & (kWRows / 2 - 1)) : r);
-    if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-    woff[i] = (uint32_t)n * (uint32_t)K + ((lslot ^ swz(kTM + r)) << 4);
+    if constexpr (WKN) {
+      // K-major weight tile: 128 K rows of 256 feature bytes, four rows per 1 KB load; lane l
+      // fills row 4 (4 w + i) + l / 16 at slot l % 16, which holds feature chunk slot ^ kn8_swz(row)
+      const int kr = 4 * (wave * kWDma + i) + (lane >> 4);
+      int n = n0 + 16 * ((lane & 15) ^ kn8_swz(kr));
+      if (n + 16 > N) n = N - 16;  // beyond the last feature: any valid chunk (outputs masked)
+      woff[i] = (uint32_t)(kr * N + n);
+    } else {
+      const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;  // 0..255 within the weight tile
+      int n = n0 + (SWIGLU ? (r & (kWRows / 2 - 1)) : r);
+      if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
+      woff[i] = (uint32_t)n * (uint32_t)K + ((lslot ^ swz(kTM + r)) << 4);
+    }
   }
   // gate rows (waves 0-3) come from W0, up rows (waves 4-7) from W1
   const uint8_t* wbase = (SWIGLU && wave >= kWaves / 2) ? W1 : W0;
@@ -168,6 +191,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     const int nb = lane - 32;
     if (SWIGLU) {
       ssrc = (nb == 0 ? S0 : S1) + (size_t)(n0 / kBK) * KB;  // gate block, then the matching up block
+    } else if (WKN) {
+      ssrc = S0 + min(n0 + nb * kBK, N - 1) / kBK;  // row 0 of the [K/128][N/128] scales; see issue_stage
     } else {
       const int n = min(n0 + nb * kBK, N - 1);
       ssrc = S0 + (size_t)(n / kBK) * KB;
@@ -181,13 +206,20 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       __builtin_amdgcn_global_load_lds(act + k0 + aoff[i],
                                        (lds_void_t*)(st + (wave * (kTM / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
                                        0);
+    // K-major weights advance by 128 rows per step, switching matrix at kn_split
+    const uint8_t* wb = !WKN ? wbase + k0
+                             : (k0 < kn_split ? W0 + (int64_t)k0 * N : W1 + (int64_t)(k0 - kn_split) * N);
 #pragma unroll
     for (int i = 0; i < kWDma; ++i)
       __builtin_amdgcn_global_load_lds(
-          wbase + k0 + woff[i], (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
-          0);
-    // every wave has active lanes here, so every wave issues this load
-    if (ssrc) __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
+          wb + woff[i], (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, 0, 0);
+    // every wave has active lanes here, so every wave issues this load; K-major weight scales
+    // step by a row of N/128 blocks per K block
+    const float* sp = ssrc + kt;
+    if (WKN && lane >= 32 && ssrc)
+      sp = kt < kn_split / kBK ? ssrc + (int64_t)kt * (N / kBK)
+                               : (S1 - S0) + ssrc + (int64_t)(kt - kn_split / kBK) * (N / kBK);
+    if (ssrc) __builtin_amdgcn_global_load_lds(sp, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
   };
 
   // weight rows of the wave's four 16-row blocks, and the 128-row scale block each falls in
@@ -226,7 +258,24 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       float sw[kNB];
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
+        if constexpr (WKN) {
+          // four transposing reads (ds_read_b64_tr_b8) give the lane K rows 32 kq + 8 j + (0..7)
+          // of feature wrow + l16: within each 16-lane group, lane s names row 8 j + s / 2 at
+          // features +8 (s % 2)..+7 of the group's 16, and receives its own feature's eight rows
+          const uint8_t* wt = st + kTM * kBK;
+          const int col = wrow[nb] + 8 * (lane & 1);
+          i32x8 f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 32 * kq + 8 * j + ((lane & 15) >> 1);
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(wt + kn8_off(r, col)));
+            f[2 * j] = v[0];
+            f[2 * j + 1] = v[1];
+          }
+          wf[nb] = f;
+        } else {
+          wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
+        }
         sw[nb] = sc[kTM + wblk[nb]];
       }
 #pragma unroll
@@ -548,16 +597,17 @@ hipError_t launch_wgrad_fp8(const GemmOperands& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool WKN = false>
 hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
+  if (WKN && (g.kn_split % kBK != 0 || g.kn_split <= 0 || g.kn_split > g.K)) return hipErrorInvalidValue;
   if (g.K % kBK != 0 || g.N % kBK != 0) return hipErrorInvalidValue;
   // 32-bit byte offsets address the activation matrix and one expert's weight matrix
   if (g.act_rows * g.K >= (int64_t(1) << 32) || (int64_t)g.N * g.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const size_t lds_bytes = kStages * kStageBytes;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_fp8_kernel<EPI>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_fp8_kernel<EPI, WKN>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (err != hipSuccess) return err;
     attr_set = true;
@@ -566,7 +616,8 @@ hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
   const int64_t tiles = g.max_pairs * NT;
   const int64_t grid = ceil_div(tiles, kXcds * kXcdChunk) * (kXcds * kXcdChunk);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_fp8_kernel<EPI>, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT);
+  auto kern = &grouped_gemm_fp8_kernel<EPI, WKN>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT);
   return hipGetLastError();
 }
 
@@ -576,5 +627,6 @@ hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st) { retur
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st) { return launch_fp8<0>(g, st); }
 hipError_t launch_gemm_fp8_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_fp8<2>(g, st); }
 hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st) { return launch_wgrad_fp8(g, st); }
+hipError_t launch_gemm_fp8_dgrad(const GemmOperands& g, hipStream_t st) { return launch_fp8<0, true>(g, st); }
 
 }  // namespace moe

@@ -17,6 +17,7 @@ hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_dgrad(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_swiglu_bwd(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_fp8_dgrad(const GemmOperands& g, hipStream_t st);
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st) {
   if (dtype == MOE_DTYPE_F32) return launch_gemm_f32_swiglu(g, st);
@@ -84,16 +85,12 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.bwd_dg_part = take((size_t)p.max_rows * (I / 128 > 0 ? I / 128 : 1) * 4);
   const size_t eb = fp8 ? 1 : 2;   // bytes per element of the transposed copies
   const int64_t P = p.max_rows, d8 = d / 128, i8 = I / 128, p8 = P / 128;
-  // transposed weight copies: FP8 only (the bf16 input-gradient products read the weights as stored)
-  p.bwd_wd_t = take(fp8 ? (size_t)(N + Ns) * I * d * eb : 0);
-  p.bwd_wc_t = take(fp8 ? (size_t)(N + Ns) * d * 2 * I * eb : 0);
+
   p.bwd_dy_t = take((size_t)d * P * eb);
   p.bwd_h_t = take((size_t)I * P * eb);
   p.bwd_dab_t = take((size_t)2 * I * P * eb);
   p.bwd_x_t = take((size_t)d * P * eb);
   p.bwd_dhu = take(fp8 ? (size_t)P * I * 2 : 0);
-  p.bwd_wd_ts = take(fp8 ? (size_t)(N + Ns) * i8 * d8 * 4 : 0);
-  p.bwd_wc_ts = take(fp8 ? (size_t)(N + Ns) * d8 * 2 * i8 * 4 : 0);
   p.bwd_dy_ts = take(fp8 ? (size_t)d * p8 * 4 : 0);
   p.bwd_h_ts = take(fp8 ? (size_t)I * p8 * 4 : 0);
   p.bwd_dab_ts = take(fp8 ? (size_t)2 * I * p8 * 4 : 0);
@@ -313,7 +310,7 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
                                const void* dout, void* du, const moe_weight_grads* dw, hipStream_t stream) {
   moe_status rc;
   const int64_t T = s.tokens, d = s.hidden, I = s.inter, Nr = s.n_routed, Ns = s.n_shared, P = p.max_rows;
-  const int64_t d8 = d / 128, i8 = I / 128, p8 = P / 128;
+  const int64_t p8 = P / 128;
   auto at = [&](size_t off) { return wsb + off; };
   const int32_t* row_token = reinterpret_cast<const int32_t*>(at(p.row_token));
   const int32_t* perm_row = reinterpret_cast<const int32_t*>(at(p.perm_row));
@@ -331,10 +328,6 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
   uint8_t* dab_q = reinterpret_cast<uint8_t*>(at(p.bwd_dab_q));
   float* dab_s = reinterpret_cast<float*>(at(p.bwd_dab_s));
   uint16_t* dx = reinterpret_cast<uint16_t*>(at(p.y));
-  uint8_t* wd_t = reinterpret_cast<uint8_t*>(at(p.bwd_wd_t));
-  float* wd_ts = reinterpret_cast<float*>(at(p.bwd_wd_ts));
-  uint8_t* wc_t = reinterpret_cast<uint8_t*>(at(p.bwd_wc_t));
-  float* wc_ts = reinterpret_cast<float*>(at(p.bwd_wc_ts));
   uint8_t* dy_t = reinterpret_cast<uint8_t*>(at(p.bwd_dy_t));
   float* dy_ts = reinterpret_cast<float*>(at(p.bwd_dy_ts));
   uint8_t* h_t = reinterpret_cast<uint8_t*>(at(p.bwd_h_t));
@@ -344,7 +337,6 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
   uint8_t* x_t = reinterpret_cast<uint8_t*>(at(p.bwd_x_t));
   float* x_ts = reinterpret_cast<float*>(at(p.bwd_x_ts));
   const int64_t max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + Nr + Ns) / 2);
-  auto b8 = [](const void* q) { return static_cast<const uint8_t*>(q); };
 
   auto wgrad = [&](const uint8_t* a_t, const float* a_s, int M, const uint8_t* b_t, const float* b_s, int N,
                    void* out_r, void* out_s) {
@@ -369,26 +361,6 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
     // E4M3 copies of u and dout (1 x 128 tiles along d)
     if ((rc = hip_status(launch_quantize_act(T, (int)d, u, u_q, u_s, stream))) != MOE_OK) return rc;
     if ((rc = hip_status(launch_quantize_act(T, (int)d, dout, dout_q, dout_s, stream))) != MOE_OK) return rc;
-    // transposed weight codes and block scales: W_down^T [I][d], [W_gate; W_up]^T [d][2I]
-    auto tw = [&](const void* src, const float* ss, int64_t R, int64_t C, uint8_t* dst, float* ds, int64_t ldd,
-                  int64_t off, int64_t n) {
-      TransposeB8Args a{b8(src), C, R * C, ss, (R / 128) * (C / 128), dst, ldd, off, C * ldd,
-                        ds, ldd / 128, (C / 128) * (ldd / 128), (int)R, (int)C};
-      return hip_status(launch_transpose_b8(a, (int)n, stream));
-    };
-    if ((rc = tw(w->w_down, w->w_down_scale, d, I, wd_t, wd_ts, d, 0, Nr)) != MOE_OK) return rc;
-    if ((rc = tw(w->w_gate, w->w_gate_scale, I, d, wc_t, wc_ts, 2 * I, 0, Nr)) != MOE_OK) return rc;
-    if ((rc = tw(w->w_up, w->w_up_scale, I, d, wc_t, wc_ts, 2 * I, I, Nr)) != MOE_OK) return rc;
-    if (Ns > 0) {
-      if ((rc = tw(w->sh_down, w->sh_down_scale, d, I, wd_t + Nr * I * d, wd_ts + Nr * i8 * d8, d, 0, Ns)) != MOE_OK)
-        return rc;
-      if ((rc = tw(w->sh_gate, w->sh_gate_scale, I, d, wc_t + Nr * d * 2 * I, wc_ts + Nr * d8 * 2 * i8, 2 * I, 0,
-                   Ns)) != MOE_OK)
-        return rc;
-      if ((rc = tw(w->sh_up, w->sh_up_scale, I, d, wc_t + Nr * d * 2 * I, wc_ts + Nr * d8 * 2 * i8, 2 * I, I, Ns)) !=
-          MOE_OK)
-        return rc;
-    }
     GemmOperands g{};
     g.tile_seg = reinterpret_cast<const int32_t*>(at(p.tile_seg));
     g.seg_off = seg_off;
@@ -397,20 +369,21 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
     g.n_routed = s.n_routed;
     g.max_tiles = p.max_tiles;
     g.max_pairs = max_pairs;
-    // dH (before the gate) = dout[token] W_down
+    // dH (before the gate) = dout[token] W_down, the W_down codes [d][I] and scales read K-major
     GemmOperands g1 = g;
     g1.act = dout_q;
     g1.act_scale = dout_s;
     g1.row_token = row_token;
     g1.act_rows = T;
-    g1.w_routed[0] = wd_t;
-    g1.w_shared[0] = wd_t + Nr * I * d;
-    g1.s_routed[0] = wd_ts;
-    g1.s_shared[0] = wd_ts + Nr * i8 * d8;
+    g1.w_routed[0] = w->w_down;
+    g1.w_shared[0] = w->sh_down;
+    g1.s_routed[0] = w->w_down_scale;
+    g1.s_shared[0] = w->sh_down_scale;
     g1.K = (int)d;
     g1.N = (int)I;
+    g1.kn_split = (int)d;
     g1.out = dhu;
-    if ((rc = hip_status(launch_gemm_fp8_down(g1, stream))) != MOE_OK) return rc;
+    if ((rc = hip_status(launch_gemm_fp8_dgrad(g1, stream))) != MOE_OK) return rc;
     // gate/up recomputed from the quantised u: [dA dB], H and the gate-gradient partials
     GemmOperands g2 = g;
     g2.act = u_q;
@@ -435,18 +408,24 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
     if ((rc = hip_status(launch_gemm_fp8_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
     // dX = [dA dB] [W_gate; W_up], [dA dB] in 1 x 128 tiles along 2I
     if ((rc = hip_status(launch_quantize_act(P, (int)(2 * I), dab, dab_q, dab_s, stream))) != MOE_OK) return rc;
+    // K rows [0, I) from the W_gate codes [I][d], [I, 2I) from W_up, as stored
     GemmOperands g3 = g;
     g3.act = dab_q;
     g3.act_scale = dab_s;
     g3.act_rows = P;
-    g3.w_routed[0] = wc_t;
-    g3.w_shared[0] = wc_t + Nr * d * 2 * I;
-    g3.s_routed[0] = wc_ts;
-    g3.s_shared[0] = wc_ts + Nr * d8 * 2 * i8;
+    g3.w_routed[0] = w->w_gate;
+    g3.w_routed[1] = w->w_up;
+    g3.w_shared[0] = w->sh_gate;
+    g3.w_shared[1] = w->sh_up;
+    g3.s_routed[0] = w->w_gate_scale;
+    g3.s_routed[1] = w->w_up_scale;
+    g3.s_shared[0] = w->sh_gate_scale;
+    g3.s_shared[1] = w->sh_up_scale;
     g3.K = (int)(2 * I);
     g3.N = (int)d;
+    g3.kn_split = (int)I;
     g3.out = dx;
-    if ((rc = hip_status(launch_gemm_fp8_down(g3, stream))) != MOE_OK) return rc;
+    if ((rc = hip_status(launch_gemm_fp8_dgrad(g3, stream))) != MOE_OK) return rc;
     if ((rc = hip_status(launch_router_bwd(s, u, centroids, topk_idx, perm_row, dg_part, seg_off, dout, dx, du,
                                            row_dz, stream))) != MOE_OK)
       return rc;

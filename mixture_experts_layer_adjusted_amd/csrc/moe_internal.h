@@ -52,18 +52,14 @@ struct WorkspacePlan {
   size_t bwd_row_gate;      // fp32 [max_rows]
   size_t bwd_row_dz;        // fp32 [max_rows]
   size_t bwd_dg_part;       // fp32 [max_rows, I / 128]
-  // transposed copies: bf16, or E4M3 codes for FP8_B128 (weights per 128 x 128 block, activations
-  // per run of 128 rows, with the scales below)
-  size_t bwd_wd_t;          // [N_r + N_s, I, d]   W_down transposed
-  size_t bwd_wc_t;          // [N_r + N_s, d, 2 I] [W_gate; W_up] transposed
+  // transposed activations: bf16, or E4M3 codes for FP8_B128 (per run of 128 rows, with the
+  // scales below)
   size_t bwd_dy_t;          // [d, max_rows]      (gate * dout of each row) transposed
   size_t bwd_h_t;           // [I, max_rows]
   size_t bwd_dab_t;         // [2 I, max_rows]
   size_t bwd_x_t;           // [d, max_rows]
   // FP8_B128 only
   size_t bwd_dhu;           // bf16 [max_rows, I]      dL/dH before the gate
-  size_t bwd_wd_ts;         // fp32 [N_r + N_s, I/128, d/128]
-  size_t bwd_wc_ts;         // fp32 [N_r + N_s, d/128, 2I/128]
   size_t bwd_dy_ts;         // fp32 [d, max_rows/128]
   size_t bwd_h_ts;          // fp32 [I, max_rows/128]
   size_t bwd_dab_ts;        // fp32 [2 I, max_rows/128]
@@ -161,21 +157,6 @@ struct TransposeArgs {
   int R, C;
 };
 hipError_t launch_transpose(const TransposeArgs& a, int batch, hipStream_t st);
-// E4M3 weight codes transposed per 128 x 128 block with their scales:
-// dst[b][c * ldd + off + r] = src[b][r * lds + c] (bytes), r < R, c < C, all multiples of 128;
-// dst_scale[b][(c / 128) * ldds + (off + r) / 128] = src_scale[b][(r / 128) * (C / 128) + c / 128]
-struct TransposeB8Args {
-  const uint8_t* src;
-  int64_t lds, src_bstride;
-  const float* src_scale;
-  int64_t src_scale_bstride;
-  uint8_t* dst;
-  int64_t ldd, off, dst_bstride;
-  float* dst_scale;
-  int64_t ldds, dst_scale_bstride;
-  int R, C;
-};
-hipError_t launch_transpose_b8(const TransposeB8Args& a, int batch, hipStream_t st);
 // bf16 activations transposed and quantised per run of 128 rows: for j < rows, c < C,
 // v = scale[j] * src[(gather ? row_token[j] : j) * lds + c] (0 where row_token[j] < 0);
 // dst[c * ldd + j] = E4M3(v / s), dst_scale[c * (ldd / 128) + j / 128] = s = amax / 448 of the run
