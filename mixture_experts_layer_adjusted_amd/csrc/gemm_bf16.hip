@@ -376,20 +376,8 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   constexpr int kSpan = kXcds * C::kXcdChunk;
   const int64_t L = (int64_t)(b / kSpan) * kSpan + (b % kXcds) * C::kXcdChunk + (b / kXcds) % C::kXcdChunk;
   int seg, nt, tile_rows, nk;
-  int64_t m0, k_base;
-  if constexpr (EPI == 3) {
-    // weight gradient: segment seg's M x N matrix, K over the segment's columns
-    const int MT = (g.wg_m + TM - 1) / TM;
-    const int64_t per = (int64_t)MT * NT;
-    seg = (int)(L / per);
-    if (seg >= g.n_seg) return;
-    const int rem = (int)(L - (int64_t)seg * per);
-    nt = rem / MT;
-    m0 = (int64_t)(rem % MT) * TM;
-    tile_rows = min(TM, g.wg_m - (int)m0);
-    k_base = g.seg_off[seg];
-    nk = (g.seg_off[seg + 1] - g.seg_off[seg]) / BK;
-  } else {
+  int64_t m0;
+  {
     const int64_t slot = L / NT;             // M-tile (TM = 128) or pair of M-tiles (TM = 256)
     if (slot >= g.max_tiles) return;
     seg = TM == kTileM ? g.tile_seg[slot] : g.pair_seg[slot];
@@ -405,7 +393,6 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
     m0 = (int64_t)g.seg_off[seg] + (int64_t)local * TM;
     // rows of this tile that belong to the segment (a half tile has 128)
     tile_rows = TM == kTileM ? TM : min(TM, g.seg_off[seg + 1] - (int)(m0));
-    k_base = 0;
     nk = g.K / BK;
   }
 
@@ -421,16 +408,13 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   // the rest of the second (the gate and up weights of one expert)
   const int kn_split = WKN ? g.kn_split : K;
   const size_t wstride = (size_t)N * (WKN ? kn_split : K);
-  // row strides (elements): the forward reads rows of length K; the weight-gradient mode reads
-  // the transposed activations, rows of length lda / ldw, from column k_base on; K-major
-  // weights have rows of length N
-  const int64_t lda = EPI == 3 ? g.lda : K, ldw = EPI == 3 ? g.ldw : (WKN ? N : K);
-  const char* W0 = EPI == 3 ? static_cast<const char*>(g.w_routed[0]) + k_base * 2
-                            : static_cast<const char*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride * 2;
+  // row strides (elements): rows of length K; K-major weights have rows of length N
+  const int64_t lda = K, ldw = WKN ? N : K;
+  const char* W0 = static_cast<const char*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride * 2;
   const char* W1 = SWIGLU || (WKN && kn_split < K)
                        ? static_cast<const char*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride * 2
                        : nullptr;
-  const char* act = static_cast<const char*>(g.act) + k_base * 2;
+  const char* act = static_cast<const char*>(g.act);
 
   // ---- per-lane sources, as 32-bit byte offsets from a wave-uniform base (the launcher checks that
   // the activation matrix and one expert's weight matrix stay below 4 GiB): wave w fills activation
@@ -570,13 +554,187 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
     static_assert(NBW == 2 && WN == 4, "one gate and one up block per wavefront, four wavefronts per row");
     __shared__ float red[TM][4];
     store_swiglu_bwd<MB>(acc, g, m0, mrow0, n0 + wn * (WRW / 2), nt, wn, tile_rows, active, l32, khalf, red);
-  } else if constexpr (EPI == 3) {
-    uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
-    if (active) store_tile<false, MB, NBW>(acc, out, m0 + mrow0, n0 + wn * WRW, N, l32, khalf);
   } else if (active) {
     store_tile<SWIGLU, MB, NBW>(acc, static_cast<uint16_t*>(g.out), m0 + mrow0,
                                 n0 + wn * (SWIGLU ? WRW / 2 : WRW), N, l32, khalf);
   }
+}
+
+// Weight gradient, persistent: out_e[m, n] = sum over the columns k of segment e of A[m, k] B[n, k]
+// (transposed activations, row strides lda and ldw).  With a few hundred rows per expert a
+// 256 x 256 output tile has only a handful of K-steps, so a one-tile workgroup spends much of its
+// time filling its pipeline and draining its stores.  Each workgroup instead walks a fixed
+// sequence of tiles (logical tile i * G + 32 x + j for the workgroup in slot j of XCD x, G
+// workgroups, so an XCD keeps a run of one expert's tiles) and issues the first K-step of its next
+// tile during the last K-step of the current one, so those loads overlap the stores.  The stage
+// ring runs on across tiles (the issued and consumed stage counts pick the LDS buffer).
+__global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g, int NT, int64_t n_tiles) {
+  constexpr int BK = 64, TM = 256, WROWS = 256, WAVES = 8, WN = 4, RW = 128, MB = 4, WRW = 64, NBW = 2;
+  using C = StreamCfg<BK, WAVES, WROWS, 1, TM>;
+  static_assert(C::kStages == 2, "two LDS stages");
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int N = g.N;
+  const int64_t lda = g.lda, ldw = g.ldw;
+  const int MT = (g.wg_m + TM - 1) / TM;
+  const int64_t per = (int64_t)MT * NT;
+  const int64_t G = gridDim.x;
+  int64_t L = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+  if (L >= n_tiles) return;
+
+  struct Tile {
+    int seg, nt, tile_rows, nk;
+    int64_t m0, k_base;
+  };
+  auto describe = [&](int64_t l) {
+    Tile t;
+    t.seg = (int)(l / per);
+    const int rem = (int)(l - (int64_t)t.seg * per);
+    t.nt = rem / MT;
+    t.m0 = (int64_t)(rem % MT) * TM;
+    t.tile_rows = min(TM, g.wg_m - (int)t.m0);
+    t.k_base = g.seg_off[t.seg];
+    t.nk = (int)((g.seg_off[t.seg + 1] - t.k_base) / BK);
+    return t;
+  };
+  // per-lane load sources of the tile being loaded, as in the streaming kernel
+  const int lrow = lane / C::kChunks, lslot = lane % C::kChunks;
+  uint32_t aoff[C::kADma], woff[C::kWDma];
+  const char* act_base = nullptr;
+  const char* w_base = nullptr;
+  auto prepare = [&](const Tile& t) {
+    const int n0 = t.nt * WROWS;
+#pragma unroll
+    for (int i = 0; i < C::kADma; ++i) {
+      const int row = wave * (TM / WAVES) + i * C::kRowsPerDma + lrow;
+      aoff[i] = (uint32_t)((t.m0 + (row < t.tile_rows ? row : 0)) * lda * 2) + ((lslot ^ C::swz(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kWDma; ++i) {
+      const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;
+      woff[i] = (uint32_t)((int64_t)min(n0 + r, N - 1) * ldw * 2) + ((lslot ^ C::swz(TM + r)) << 4);
+    }
+    act_base = static_cast<const char*>(g.act) + t.k_base * 2;
+    w_base = static_cast<const char*>(g.w_routed[0]) + t.k_base * 2;
+  };
+  int issued = 0, consumed = 0;
+  auto issue = [&](int kt) {
+    uint16_t* st = lds + (issued % C::kStages) * C::kStageElems;
+    const int k0 = kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < C::kADma; ++i)
+      lds_dma16(act_base + k0 + aoff[i], st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
+#pragma unroll
+    for (int i = 0; i < C::kWDma; ++i)
+      lds_dma16(w_base + k0 + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
+    ++issued;
+  };
+
+  int wrow[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) wrow[nb] = wn * WRW + nb * 32;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int mrow0 = wm * RW;
+
+  Tile cur = describe(L);
+  prepare(cur);
+  if (cur.nk > 0) issue(0);
+  while (true) {
+    const int64_t Ln = L + G;
+    const bool has_next = Ln < n_tiles;
+    // the next tile's first K-step, issued once this tile's last one is being computed
+    auto prefetch_next = [&]() {
+      if (!has_next) return;
+      const Tile t = describe(Ln);
+      if (t.nk > 0) {
+        prepare(t);
+        issue(0);
+      }
+    };
+    const bool active = mrow0 < cur.tile_rows;   // false only for the upper half of a half tile
+    f32x16 acc[MB][NBW];
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int c = 0; c < NBW; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+    for (int kt = 0; kt < cur.nk; ++kt) {
+      wait_vmcnt<0>();
+      // a bare barrier: stage `consumed` has landed and the other buffer is no longer read
+      __builtin_amdgcn_s_barrier();
+      if (kt + 1 < cur.nk)
+        issue(kt + 1);
+      else
+        prefetch_next();
+      if (active) {
+        const uint16_t* st = lds + (consumed % C::kStages) * C::kStageElems;
+        bf16x8 xf[2][MB], wf[2][NBW];
+        auto load_frags = [&](int buf, int kk) {
+          const int c = kk * 2 + khalf;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            xf[buf][mb] = *reinterpret_cast<const bf16x8*>(st + C::off(mrow0 + mb * 32 + l32, c));
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb)
+            wf[buf][nb] = *reinterpret_cast<const bf16x8*>(st + C::off(TM + wrow[nb] + l32, c));
+        };
+        load_frags(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const int cb = kk & 1;
+          if (kk + 1 < BK / 16) load_frags(cb ^ 1, kk + 1);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][nb], xf[cb][mb], acc[mb][nb], 0, 0, 0);
+        }
+      }
+      ++consumed;
+    }
+    // a tile without K-steps (an empty segment) prefetched nothing for the next one
+    if (cur.nk == 0) prefetch_next();
+    // segment cur.seg's matrix of the routed or shared output (an empty segment writes zeros)
+    if (active) {
+      const bool shared = cur.seg >= g.n_routed;
+      const int e = shared ? cur.seg - g.n_routed : cur.seg;
+      uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
+      store_tile<false, MB, NBW>(acc, out, cur.m0 + mrow0, cur.nt * WROWS + wn * WRW, N, l32, khalf);
+    }
+    if (!has_next) break;
+    cur = describe(Ln);
+    L = Ln;
+  }
+}
+
+hipError_t launch_wgrad_bf16(const GemmOperands& g, hipStream_t st) {
+  using C = StreamCfg<64, 8, 256, 1, 256>;
+  if (g.wg_m % 128 != 0 || g.N % 8 != 0) return hipErrorInvalidValue;
+  // 32-bit byte offsets address the transposed activation matrices
+  if ((int64_t)g.wg_m * g.lda * 2 >= (int64_t(1) << 32) || (int64_t)g.N * g.ldw * 2 >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
+  const size_t lds_bytes = C::kStages * C::kStageElems * sizeof(uint16_t);
+  static bool attr_set = false;
+  static int n_cu = 0;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_bf16_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (err != hipSuccess) return err;
+    int dev = 0;
+    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+    if ((err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
+    attr_set = true;
+  }
+  const int NT = (int)ceil_div(g.N, 256);
+  const int64_t tiles = (int64_t)g.n_seg * ceil_div(g.wg_m, 256) * NT;
+  if (tiles == 0) return hipSuccess;
+  // one workgroup per CU (the LDS stages allow no more), a multiple of the XCD count
+  const int64_t grid = std::max<int64_t>(kXcds, (int64_t)n_cu / kXcds * kXcds);
+  hipLaunchKernelGGL(grouped_wgrad_bf16_kernel, dim3((unsigned)grid), dim3(512), lds_bytes, st, g, NT, tiles);
+  return hipGetLastError();
 }
 
 template <int EPI, int SBK, int SW, int SR, int SG, int SM, int STM, bool WKN = false>
@@ -593,8 +751,7 @@ hipError_t launch_stream(const GemmOperands& g, hipStream_t st) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  const int64_t tiles = EPI == 3 ? (int64_t)g.n_seg * ceil_div(g.wg_m, STM) * NT
-                                 : (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
+  const int64_t tiles = (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
   const int64_t span = kXcds * SC::kXcdChunk;
   const int64_t grid = ceil_div(tiles, span) * span;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(SC::kThreads), lds_bytes, st, g, NT);
@@ -610,13 +767,11 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
   constexpr bool SWIGLU = EPI == 1 || EPI == 2;
   constexpr int SBK = MOE_STREAM_BK;
   // the streaming kernel addresses its sources with 32-bit byte offsets
-  const bool offsets_fit =
-      EPI == 3 ? (int64_t)g.wg_m * g.lda * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.ldw * 2 < (int64_t(1) << 32)
-               : g.act_rows * g.K * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.K * 2 < (int64_t(1) << 32);
+  const bool offsets_fit = g.act_rows * g.K * 2 < (int64_t(1) << 32) && (int64_t)g.N * g.K * 2 < (int64_t(1) << 32);
   if (g.K % SBK == 0 && offsets_fit) {
-    if constexpr (EPI >= 2) {
-      // backward modes: 256 x 256 tiles (the SwiGLU-backward epilogue assumes four wavefronts
-      // of one gate and one up block per row)
+    if constexpr (EPI == 2) {
+      // 256 x 256 tiles (the SwiGLU-backward epilogue assumes four wavefronts of one gate and
+      // one up block per row)
       return launch_stream<EPI, 64, 8, 256, 1, 2, 256>(g, st);
     } else {
       // segments of a few rows (decode-like batches, expected routed rows per expert below one
@@ -626,7 +781,7 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
                            MOE_STREAM_TM>(g, st);
     }
   }
-  if (EPI >= 2) return hipErrorInvalidValue;   // the backward modes exist in the streaming kernel only
+  if (EPI == 2) return hipErrorInvalidValue;   // the backward mode exists in the streaming kernel only
   const size_t lds_bytes = 2 * kStageElems * sizeof(uint16_t);
   static bool attr_set = false;
   if (!attr_set) {
@@ -645,7 +800,7 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
 hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st) { return launch_bf16<1>(g, st); }
 hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st) { return launch_bf16<0>(g, st); }
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_bf16<2>(g, st); }
-hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st) { return launch_bf16<3>(g, st); }
+hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st) { return launch_wgrad_bf16(g, st); }
 
 // Input-gradient product on K-major weights (as stored), no transposed copy: out[r, n] =
 // sum_k act[r, k] W[k, n] with W = rows [0, kn_split) of w_*[0] then the rest of w_*[1]

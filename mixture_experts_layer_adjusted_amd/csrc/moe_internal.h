@@ -131,7 +131,7 @@ struct GemmOperands {
   const float* row_gate;
   void* out2;
   float* dg_part;
-  // weight-gradient mode (bf16): out_e[m, n] = sum over the columns k of segment e of
+  // weight-gradient kernels (bf16, FP8): out_e[m, n] = sum over the columns k of segment e of
   // act[m, k] * w_routed[0][n, k] (transposed activations, row strides lda and ldw), m < wg_m;
   // routed segments write out + e M N, shared ones out2 + (e - N_r) M N
   int64_t lda, ldw;
