@@ -124,7 +124,7 @@ struct GemmOperands {
   int64_t max_pairs;         // upper bound on the 256-row tiles: min(max_tiles, (max_tiles + N_r + N_s) / 2)
   void* out;                 // [max_rows, N]
   float* out_scale;          // fp8 SwiGLU output: [max_rows, N/128]
-  // SwiGLU backward epilogue (bf16): reads dh (dL/dH before the gate, [max_rows, N]) and
+  // SwiGLU backward epilogue (bf16, FP8): reads dh (dL/dH before the gate, [max_rows, N]) and
   // row_gate, writes out = [dA dB] ([max_rows, 2N]), out2 = H ([max_rows, N]) and
   // dg_part[row, N-tile] = sum over the tile's features of dh * H
   const void* dh;
@@ -136,7 +136,7 @@ struct GemmOperands {
   // routed segments write out + e M N, shared ones out2 + (e - N_r) M N
   int64_t lda, ldw;
   int wg_m, n_seg;
-  // input-gradient mode (bf16): the weights are read K-major, as stored ([K rows][N features] per
+  // input-gradient products (bf16, FP8): the weights are read K-major, as stored ([K rows][N features] per
   // expert, the w_*[0] matrix for K rows [0, kn_split), the w_*[1] matrix for the rest)
   int kn_split;
   // expected routed rows per expert (T K_r / N_r) below one M-tile: the bf16 forward GEMMs take
