@@ -219,6 +219,23 @@ def main():
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
 
+    # the same step captured once in a HIP graph and replayed (launch overhead removed)
+    gbias = bias.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_route(shape, dev["u"], dev["centroids"], gbias, idx, gate, load, ws)
+        moe.moe_forward(shape, dev["u"], weights, idx, gate, out, ws)
+        moe.moe_update_bias(N, T * K, load, gbias, cfg.gamma)
+    graph.replay()
+    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_g[0].record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    ev_g[1].record(stream)
+    torch.cuda.synchronize()
+    graph_ms = ev_g[0].elapsed_time(ev_g[1]) / args.steps
+    del graph
+
     # group-limited routing (8 equal expert groups, 4 eligible per token) on the same batch and
     # bias, timed outside the step: the cost of the limit next to the plain route
     route_grouped = None
@@ -360,6 +377,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_median": round(float(np.median(step_ms_all)), 4),
+        "graph_ms_per_step": round(graph_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
