@@ -560,6 +560,230 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   }
 }
 
+// The streaming kernel's 256 x 256 plain-store and SwiGLU forms (and the K-major input-gradient
+// form), persistent: one workgroup per CU walks logical tiles i * G + 32 x + j (slot j of XCD x,
+// G workgroups: the same tile-to-XCD assignment as the one-tile grid when G = 256) and issues the
+// first K-step of its next tile during the last K-step of the current one, so a tile's pipeline
+// fill and its stores overlap its neighbour's loads.  Tiles past the last 256-row tile end the
+// walk (their slots only grow).
+template <int EPI, bool WKN>
+__global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmOperands g, int NT) {
+  constexpr bool SWIGLU = EPI == 1;
+  static_assert(EPI == 0 || EPI == 1, "plain store or SwiGLU");
+  static_assert(!WKN || EPI == 0, "K-major weights: plain store");
+  constexpr int BK = 64, TM = 256, WROWS = 256, WAVES = 8, WN = 4, RW = 128, MB = 4, WRW = 64, NBW = 2;
+  using C = StreamCfg<BK, WAVES, WROWS, 1, TM>;
+  static_assert(C::kStages == 2, "two LDS stages");
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = g.K, N = g.N, nk = K / BK;
+  const int kn_split = WKN ? g.kn_split : K;
+  const size_t wstride = (size_t)N * kn_split;
+  const int64_t lda = K, ldw = WKN ? N : K;
+  const int64_t G = gridDim.x;
+  int64_t L = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+
+  struct Tile {
+    int seg, nt, tile_rows;
+    int64_t m0;
+  };
+  // the 256-row tile of logical index l, in the XCD-aware within-expert order of the streaming
+  // kernel; seg < 0 past the last one
+  auto describe = [&](int64_t l) {
+    Tile t{-1, 0, 0, 0};
+    const int64_t slot = l / NT;
+    if (slot >= g.max_tiles) return t;
+    const int seg = g.pair_seg[slot];
+    if (seg < 0) return t;
+    const int seg_first = g.pair_off[seg];
+    const int seg_count = g.pair_off[seg + 1] - seg_first;
+    const int64_t lam = l - (int64_t)seg_first * NT;
+    const int grp = (int)(lam / (kGroupM * NT));
+    const int gm = min(kGroupM, seg_count - grp * kGroupM);
+    const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
+    const int local = grp * kGroupM + rem % gm;
+    t.seg = seg;
+    t.nt = rem / gm;
+    t.m0 = (int64_t)g.seg_off[seg] + (int64_t)local * TM;
+    t.tile_rows = min(TM, g.seg_off[seg + 1] - (int)t.m0);
+    return t;
+  };
+  // per-lane load sources of the tile being loaded (as in the streaming kernel)
+  const int lrow = lane / C::kChunks, lslot = lane % C::kChunks;
+  const char* act = static_cast<const char*>(g.act);
+  uint32_t aoff[C::kADma], woff[C::kWDma];
+  const char* W0 = nullptr;
+  const char* W1 = nullptr;
+  auto prepare = [&](const Tile& t) {
+    const int n0 = t.nt * (SWIGLU ? WROWS / 2 : WROWS);
+    const bool shared = t.seg >= g.n_routed;
+    const int e = shared ? t.seg - g.n_routed : t.seg;
+    W0 = static_cast<const char*>(shared ? g.w_shared[0] : g.w_routed[0]) + e * wstride * 2;
+    W1 = SWIGLU || (WKN && kn_split < K)
+             ? static_cast<const char*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride * 2
+             : W0;
+#pragma unroll
+    for (int i = 0; i < C::kADma; ++i) {
+      const int row = wave * (TM / WAVES) + i * C::kRowsPerDma + lrow;
+      const int64_t r = t.m0 + (row < t.tile_rows ? row : 0);  // rows past a half tile: a valid row
+      int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
+      if (tok < 0) tok = 0;  // padding row: any valid row (its outputs are never read)
+      aoff[i] = (uint32_t)(tok * lda * 2) + ((lslot ^ C::swz(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kWDma; ++i) {
+      if constexpr (WKN) {
+        const int kr = 2 * (wave * C::kWDma + i) + (lane >> 5);
+        int n = n0 + 8 * ((lane & 31) ^ kn_swz(kr));
+        if (n + 8 > N) n = N - 8;
+        woff[i] = (uint32_t)((kr * ldw + n) * 2);
+      } else {
+        const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;
+        int n = n0 + (SWIGLU ? r % (WROWS / 2) : r);
+        if (n >= N) n = N - 1;
+        woff[i] = (uint32_t)(n * ldw * 2) + ((lslot ^ C::swz(TM + r)) << 4);
+      }
+    }
+  };
+  int issued = 0, consumed = 0;
+  auto issue = [&](int kt) {
+    uint16_t* st = lds + (issued % C::kStages) * C::kStageElems;
+    const int k0 = kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < C::kADma; ++i)
+      lds_dma16(act + k0 + aoff[i], st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
+    const int kr0 = kt * BK;
+    // gate rows come from W0, up rows from W1 (the split falls on a wave boundary); K-major
+    // weights advance by BK rows per step, switching matrix at kn_split
+    const char* wb = WKN ? (kr0 < kn_split ? W0 + (int64_t)kr0 * ldw * 2 : W1 + (int64_t)(kr0 - kn_split) * ldw * 2)
+                         : ((SWIGLU && wave * (WROWS / WAVES) >= WROWS / 2) ? W1 : W0) + k0;
+#pragma unroll
+    for (int i = 0; i < C::kWDma; ++i)
+      lds_dma16(wb + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
+    ++issued;
+  };
+
+  int wrow[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    if (SWIGLU)
+      wrow[nb] = nb < NBW / 2 ? wn * (WRW / 2) + nb * 32 : WROWS / 2 + wn * (WRW / 2) + (nb - NBW / 2) * 32;
+    else
+      wrow[nb] = wn * WRW + nb * 32;
+  }
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int mrow0 = wm * RW;
+
+  Tile cur = describe(L);
+  if (cur.seg < 0) return;
+  prepare(cur);
+  issue(0);
+  while (true) {
+    const int64_t Ln = L + G;
+    const Tile nxt = describe(Ln);
+    const bool active = mrow0 < cur.tile_rows;   // false only for the upper half of a half tile
+    // the loads of the step after kt: this tile's next one, or the next tile's first
+    auto issue_next = [&](int kt) {
+      if (kt + 1 < nk) {
+        issue(kt + 1);
+      } else if (nxt.seg >= 0) {
+        prepare(nxt);
+        issue(0);
+      }
+    };
+    f32x16 acc[MB][NBW];
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int c = 0; c < NBW; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();
+      // a bare barrier: stage `consumed` has landed and the other buffer is no longer read
+      __builtin_amdgcn_s_barrier();
+      if (active) {
+        const uint16_t* st = lds + (consumed % C::kStages) * C::kStageElems;
+        bf16x8 xf[2][MB], wf[2][NBW];
+        auto load_frags = [&](int buf, int kk) {
+          const int c = kk * 2 + khalf;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            xf[buf][mb] = *reinterpret_cast<const bf16x8*>(st + C::off(mrow0 + mb * 32 + l32, c));
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) {
+            if constexpr (WKN) {
+              const int kb = kk * 16 + khalf * 8;
+              const int col = wrow[nb] + (l32 & 16) + 4 * (lane & 3);
+              const int r0 = kb + ((lane & 15) >> 2);
+              const uint16_t* wt = st + TM * BK;
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wt + kn_off(r0, col)));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wt + kn_off(r0 + 4, col)));
+              wf[buf][nb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+              wf[buf][nb] = *reinterpret_cast<const bf16x8*>(st + C::off(TM + wrow[nb] + l32, c));
+            }
+          }
+        };
+        load_frags(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const int cb = kk & 1;
+          if (kk + 1 < BK / 16) load_frags(cb ^ 1, kk + 1);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][nb], xf[cb][mb], acc[mb][nb], 0, 0, 0);
+          // the next step's loads go out once this sub-step's MFMAs are queued
+          if (kk == 0) issue_next(kt);
+        }
+      } else {
+        issue_next(kt);
+      }
+      ++consumed;
+    }
+    if (active)
+      store_tile<SWIGLU, MB, NBW>(acc, static_cast<uint16_t*>(g.out), cur.m0 + mrow0,
+                                  cur.nt * (SWIGLU ? WROWS / 2 : WROWS) + wn * (SWIGLU ? WRW / 2 : WRW), N, l32,
+                                  khalf);
+    if (nxt.seg < 0) break;
+    cur = nxt;
+    L = Ln;
+  }
+}
+
+#ifndef MOE_PERSISTENT_GEMM
+#define MOE_PERSISTENT_GEMM 1
+#endif
+
+template <int EPI, bool WKN>
+hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
+  using SC = StreamCfg<64, 8, 256, 1, 256>;
+  const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
+  auto kern = &grouped_gemm_bf16_persistent_kernel<EPI, WKN>;
+  static bool attr_set = false;
+  static int n_cu = 0;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (err != hipSuccess) return err;
+    int dev = 0;
+    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+    if ((err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
+    attr_set = true;
+  }
+  const int NT = (int)ceil_div(g.N, EPI == 1 ? 128 : 256);
+  if (g.max_pairs * NT == 0) return hipSuccess;
+  // one workgroup per CU (the LDS stages allow no more), a multiple of the 8 x 32 tile block
+  const int64_t span = kXcds * SC::kXcdChunk;
+  const int64_t grid = std::max<int64_t>(span, (int64_t)n_cu / span * span);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds_bytes, st, g, NT);
+  return hipGetLastError();
+}
+
 // Weight gradient, persistent: out_e[m, n] = sum over the columns k of segment e of A[m, k] B[n, k]
 // (transposed activations, row strides lda and ldw).  With a few hundred rows per expert a
 // 256 x 256 output tile has only a handful of K-steps, so a one-tile workgroup spends much of its
@@ -777,6 +1001,9 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
       // segments of a few rows (decode-like batches, expected routed rows per expert below one
       // M-tile): 128-row tiles x 512 weight rows put 80% of every stage's loads on weights
       if (MOE_SMALL_SEGMENT_TILE && g.small_segments) return launch_stream<EPI, 64, 8, 512, 1, 2, 128>(g, st);
+      if (MOE_PERSISTENT_GEMM && SBK == 64 && MOE_STREAM_WAVES == 8 && MOE_STREAM_WROWS == 256 &&
+          MOE_STREAM_WGS == 1 && MOE_STREAM_WM == 2 && MOE_STREAM_TM == 256)
+        return launch_persistent<EPI, false>(g, st);
       return launch_stream<EPI, SBK, MOE_STREAM_WAVES, MOE_STREAM_WROWS, MOE_STREAM_WGS, MOE_STREAM_WM,
                            MOE_STREAM_TM>(g, st);
     }
@@ -809,6 +1036,7 @@ hipError_t launch_gemm_bf16_dgrad(const GemmOperands& g, hipStream_t st) {
     return hipErrorInvalidValue;
   // 32-bit byte offsets: the activation matrix; the weight offsets stay within one stage's rows
   if (g.act_rows * g.K * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  if (MOE_PERSISTENT_GEMM) return launch_persistent<0, true>(g, st);
   return launch_stream<0, 64, 8, 256, 1, 2, 256, true>(g, st);
 }
 
