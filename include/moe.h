@@ -54,9 +54,11 @@ typedef enum moe_dtype {
   MOE_DTYPE_FP8_B128 = 2   /* u, out: bf16; weights E4M3 codes + fp32 128x128 block scales */
 } moe_dtype;
 
-/* Layer shape.  Limits: tokens >= 0; 1 <= n_routed <= 1024; 1 <= top_k <= min(n_routed, 32);
+/* Layer shape.  Limits: tokens >= 0; 1 <= n_routed <= 512; 1 <= top_k <= min(n_routed, 32);
  * 0 <= n_shared <= 64; hidden, inter >= 1 and multiples of 8 (bf16) or of 128 (fp8);
- * tokens * top_k < 2^31. */
+ * tokens * top_k < 2^31; fp8 also tokens * hidden, (padded permuted rows) * inter and
+ * hidden * inter below 2^32 (the FP8 GEMMs' 32-bit byte offsets).  Outside them the calls
+ * return MOE_ERR_INVALID_ARG (malformed) or MOE_ERR_UNSUPPORTED. */
 typedef struct moe_shape {
   int32_t tokens;    /* T   */
   int32_t hidden;    /* d   */
@@ -90,7 +92,7 @@ typedef struct moe_weights {
 #define MOE_FORWARD_EVENTS 6
 
 /* Bytes of device workspace that moe_route and moe_forward need for `shape`
- * (one buffer serves both).  Never fails for a valid shape. */
+ * (one buffer serves both).  Never fails for a shape within the limits above. */
 moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /* Routing: sigmoid affinities, biased top-K_r selection, normalised gates, per-expert load

@@ -117,6 +117,13 @@ static moe_status check_shape(const moe_shape* s) {
   if (T * K >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   const int64_t max_tiles = (T * K + (int64_t)s->n_routed * (kTileM - 1)) / kTileM + s->n_shared * ceil_div(T, kTileM);
   if (max_tiles * kTileM >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  // the FP8 GEMMs address u codes [T, d], H codes [rows, I] and one expert's weight codes with
+  // 32-bit byte offsets (the bf16 GEMMs fall back to a 64-bit-addressed kernel instead)
+  if (s->dtype == MOE_DTYPE_FP8_B128) {
+    const int64_t lim = int64_t(1) << 32;
+    if (T * s->hidden >= lim || max_tiles * kTileM * s->inter >= lim || (int64_t)s->hidden * s->inter >= lim)
+      return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 

@@ -113,6 +113,9 @@ def test_null_and_workspace_errors_before_launch():
     assert lib.moe_backward_workspace_size(ctypes.byref(moe.make_shape(64, 256, 16, 4, 1, 192, moe.MOE_DTYPE_FP8_B128)),
                                            ctypes.byref(n8)) == 2                           # I % 128
     assert lib.moe_backward(ctypes.byref(s8), *args, fake, big, None) == 1                  # no weight scales
+    # FP8 shapes whose operands exceed the GEMMs' 32-bit byte offsets are refused up front
+    huge = moe.make_shape(700000, 7168, 256, 8, 1, 2048, moe.MOE_DTYPE_FP8_B128)
+    assert lib.moe_workspace_size(ctypes.byref(huge), ctypes.byref(n8)) == 2
     assert lib.moe_update_bias(0, 10, fake, fake, ctypes.c_float(0.001), None) == 1
     assert lib.moe_quantize_weights(1, 100, 128, fake, fake, fake, None) == 2
     assert lib.moe_quantize_act(4, 130, fake, fake, fake, None) == 2
