@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="v3-prefill-bf16-zipf", choices=sorted(WORKLOADS))
-    p.add_argument("--cpu-sample-tokens", type=int, default=256)
+    p.add_argument("--cpu-sample-tokens", type=int, default=384)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true", help="skip the layer-backward timing (bf16 workloads)")
     p.add_argument("--no-peaks", action="store_true",
