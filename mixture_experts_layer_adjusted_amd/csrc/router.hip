@@ -15,8 +15,12 @@
 //     parts as three B operands, 128 x 128 tiles, LDS stages filled by direct global->LDS loads;
 //     each 64-wide K-step starts a fresh accumulator that is then added to an fp32 running sum
 //     (blocked summation keeps the logit error near 1e-7 of the sum of |terms|); s = sigmoid(z)
-//     is written to the workspace;
+//     is written to the workspace; with fewer than 128 output tiles (decode-sized batches) the
+//     contraction splits into up to 16 K-slices whose partial logits a second kernel adds in
+//     slice order;
 //  3. top-K: one wavefront per token on s + b, as in step 3 below, plus per-workgroup counts;
+//     with a group limit (moe_route_grouped) the lanes first find the best c of every expert
+//     group and mask the experts of the groups outside the topk_groups best;
 //  4. counts: a fixed-order reduction of the per-workgroup counts into expert_load.
 //
 // Fused VALU path (fp32 tokens, or any other shape).  One workgroup (256 threads) owns
