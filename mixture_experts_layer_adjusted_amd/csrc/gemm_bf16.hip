@@ -284,6 +284,135 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// LDS traffic of this wavefront done (lgkmcnt 0; vmcnt 63 and expcnt 7 are no wait), then a bare
+// barrier: unlike __syncthreads() it leaves global loads, LDS DMA and stores in flight.  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Staged epilogues of the 256 x 256 tile kernels (eight wavefronts; wavefront (wm, wn) holds rows
+// wm * 128 + [0, 128) of the tile in MB = 4 blocks of 32 and 64 output columns (plain) or 32
+// gate + the matching 32 up features (SwiGLU) in NBW = 2 blocks of 32).  The 32 x 32 MFMA result
+// layout gives each lane runs of 4 columns of one row, so direct stores write 32 rows x 16 bytes
+// per instruction; staged through an LDS stage no load is filling, each store instead writes
+// whole 256- or 512-byte row spans (8 full 128-byte lines).  Staged 16-byte chunk c of row r sits
+// at slot c ^ (r mod chunks per row), so neither side piles onto a few banks.  The LDS accesses
+// are typed (64-bit and 4 x 32-bit integers), which keeps the compiler from making them wait for
+// the global loads and stores in flight.  The caller has passed lds_barrier() since the stage was
+// last read.  Every store instruction has an active lane (chunk 0 lies below N; N is a multiple
+// of 8), so the return value, the stores this wavefront issued, is exact for vmcnt accounting.
+constexpr int kStagedRounds = 8;   // row-span stores per wavefront per 64 KB of staged output
+
+// four values rounded to bf16 (nearest even, as f32_to_bf16 for finite values) by the packed
+// conversion instruction, lowest address first
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint64_t pack_bf16x4(float a, float b, float c, float d) {
+  const bf16x2_t lo = {(__bf16)a, (__bf16)b};
+  const bf16x2_t hi = {(__bf16)c, (__bf16)d};
+  return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+}
+
+// plain 256 x 256 tile (rows m0 + [0, tile_rows), tile_rows 128 or 256, columns n0 + [0, 256)
+// below N) in two passes of 512-byte rows: pass p stages accumulator blocks 2p and 2p + 1 of
+// every wavefront (tile rows wm * 128 + p * 64 + [0, 64) as staged rows wm * 64 + [0, 64)), so
+// half of each wavefront's accumulators are dead before any row is read back
+__device__ __forceinline__ int store_tile_staged(const f32x16 (&acc)[4][2], uint16_t* stg, uint16_t* out,
+                                                 int64_t m0, int n0, int N, int tile_rows, int wave, int wm,
+                                                 int wn, int lane) {
+  // the lane index made opaque: the per-lane LDS offsets below are then computed per tile rather
+  // than hoisted out of the caller's tile loop, where they would hold registers across the MFMAs
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, khalf = lane >> 5;
+  // staged rows 64 and up belong to wavefronts wm = 1, absent from a half tile
+  const int rounds = tile_rows > 128 ? kStagedRounds : kStagedRounds / 2;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (p > 0) lds_barrier();   // the first pass has been read back
+    if (wm * 128 < tile_rows) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = wm * 64 + h * 32 + l32;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = wn * 8 + nb * 4 + q;
+            const f32x16& a = acc[2 * p + h][nb];
+            *reinterpret_cast<uint64_t*>(stg + r * 256 + ((c ^ (r & 31)) << 3) + khalf * 4) =
+                pack_bf16x4(a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]);
+          }
+      }
+    }
+    lds_barrier();
+    const int c = lane & 31;
+    const int f = n0 + c * 8;
+#pragma unroll
+    for (int i = 0; i < kStagedRounds; ++i) {
+      if (i < rounds) {
+        const int r = (i * 8 + wave) * 2 + (lane >> 5);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((c ^ (r & 31)) << 3));
+        const int64_t row = m0 + (r >> 6) * 128 + p * 64 + (r & 63);
+        if (f < N) *reinterpret_cast<u32x4*>(out + row * N + f) = v;
+      }
+    }
+  }
+  return 2 * rounds;
+}
+
+// SwiGLU 256 x 128 tile H = silu(gate) * up in one pass of 256-byte rows (rows m0 + [0, tile_rows),
+// features n0 + [0, 128) below N)
+__device__ __forceinline__ int store_tile_staged_swiglu(const f32x16 (&acc)[4][2], uint16_t* stg, uint16_t* out,
+                                                        int64_t m0, int n0, int N, int tile_rows, int wave, int wm,
+                                                        int wn, int lane) {
+  asm volatile("" : "+v"(lane));   // as in store_tile_staged
+  const int l32 = lane & 31, khalf = lane >> 5;
+  if (wm * 128 < tile_rows) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int r = wm * 128 + mb * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * 4 + q;
+        const f32x16& ga = acc[mb][0];
+        const f32x16& ua = acc[mb][1];
+        *reinterpret_cast<uint64_t*>(stg + r * 128 + ((c ^ (r & 15)) << 3) + khalf * 4) =
+            pack_bf16x4(silu(ga[q * 4]) * ua[q * 4], silu(ga[q * 4 + 1]) * ua[q * 4 + 1],
+                        silu(ga[q * 4 + 2]) * ua[q * 4 + 2], silu(ga[q * 4 + 3]) * ua[q * 4 + 3]);
+      }
+    }
+  }
+  lds_barrier();
+  const int c = lane & 15;
+  const int f = n0 + c * 8;
+  const int rounds = tile_rows > 128 ? kStagedRounds : kStagedRounds / 2;
+#pragma unroll
+  for (int i = 0; i < kStagedRounds; ++i) {
+    if (i < rounds) {
+      const int r = (i * 8 + wave) * 4 + (lane >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * 128 + ((c ^ (r & 15)) << 3));
+      if (f < N) *reinterpret_cast<u32x4*>(out + (m0 + r) * N + f) = v;
+    }
+  }
+  return rounds;
+}
+
+// wait until at most n (0, 4, 8 or 16: the stores a staged epilogue issued after the loads
+// being waited for) vector memory operations are outstanding
+__device__ __forceinline__ void wait_loads_behind_stores(int n) {
+  if (n == 16)
+    wait_vmcnt<16>();
+  else if (n == 8)
+    wait_vmcnt<8>();
+  else if (n == 4)
+    wait_vmcnt<4>();
+  else
+    wait_vmcnt<0>();
+}
+
 // wait until at most `ahead` stages of this wave's loads are still in flight
 template <int PER, int MAXAHEAD>
 __device__ __forceinline__ void wait_stages(int ahead) {
@@ -564,8 +693,11 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
 // form), persistent: one workgroup per CU walks logical tiles i * G + 32 x + j (slot j of XCD x,
 // G workgroups: the same tile-to-XCD assignment as the one-tile grid when G = 256) and issues the
 // first K-step of its next tile during the last K-step of the current one, so a tile's pipeline
-// fill and its stores overlap its neighbour's loads.  Tiles past the last 256-row tile end the
-// walk (their slots only grow).
+// fill overlaps its neighbour's MFMAs.  The output goes out through LDS as whole row spans
+// (store_tile_staged*), after those loads, and the next tile's first wait counts the stores
+// (vmcnt retires in issue order): the stores stay in flight through that tile's first K-step.
+// The tile after next is described before the stores, whose table reads would otherwise wait for
+// them.  Tiles past the last 256-row tile end the walk (their slots only grow).
 template <int EPI, bool WKN>
 __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmOperands g, int NT) {
   constexpr bool SWIGLU = EPI == 1;
@@ -582,8 +714,9 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
   const int kn_split = WKN ? g.kn_split : K;
   const size_t wstride = (size_t)N * kn_split;
   const int64_t lda = K, ldw = WKN ? N : K;
-  const int64_t G = gridDim.x;
-  int64_t L = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+  const int G = gridDim.x;
+  const int max_slots = (int)g.max_tiles;
+  int L = (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds);
 
   struct Tile {
     int seg, nt, tile_rows;
@@ -591,23 +724,25 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
   };
   // the 256-row tile of logical index l, in the XCD-aware within-expert order of the streaming
   // kernel; seg < 0 past the last one
-  auto describe = [&](int64_t l) {
+  // (tile indices, walk included, stay below 2^31: the launcher checks)
+  auto describe = [&](int l) {
     Tile t{-1, 0, 0, 0};
-    const int64_t slot = l / NT;
-    if (slot >= g.max_tiles) return t;
-    const int seg = g.pair_seg[slot];
+    const int slot = l / NT;
+    if (slot >= max_slots) return t;
+    // wave-uniform table entries, kept in scalar registers
+    const int seg = __builtin_amdgcn_readfirstlane(g.pair_seg[slot]);
     if (seg < 0) return t;
-    const int seg_first = g.pair_off[seg];
-    const int seg_count = g.pair_off[seg + 1] - seg_first;
-    const int64_t lam = l - (int64_t)seg_first * NT;
-    const int grp = (int)(lam / (kGroupM * NT));
+    const int seg_first = __builtin_amdgcn_readfirstlane(g.pair_off[seg]);
+    const int seg_count = __builtin_amdgcn_readfirstlane(g.pair_off[seg + 1]) - seg_first;
+    const int lam = l - seg_first * NT;
+    const int grp = lam / (kGroupM * NT);
     const int gm = min(kGroupM, seg_count - grp * kGroupM);
-    const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
+    const int rem = lam - grp * kGroupM * NT;
     const int local = grp * kGroupM + rem % gm;
     t.seg = seg;
     t.nt = rem / gm;
-    t.m0 = (int64_t)g.seg_off[seg] + (int64_t)local * TM;
-    t.tile_rows = min(TM, g.seg_off[seg + 1] - (int)t.m0);
+    t.m0 = (int64_t)__builtin_amdgcn_readfirstlane(g.seg_off[seg]) + (int64_t)local * TM;
+    t.tile_rows = min(TM, __builtin_amdgcn_readfirstlane(g.seg_off[seg + 1]) - (int)t.m0);
     return t;
   };
   // per-lane load sources of the tile being loaded (as in the streaming kernel)
@@ -624,13 +759,23 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
     W1 = SWIGLU || (WKN && kn_split < K)
              ? static_cast<const char*>(shared ? g.w_shared[1] : g.w_routed[1]) + e * wstride * 2
              : W0;
+    // rows past a half tile: a valid row; the token gathers are issued together (one branch,
+    // one round trip)
+    int tok[C::kADma];
 #pragma unroll
     for (int i = 0; i < C::kADma; ++i) {
       const int row = wave * (TM / WAVES) + i * C::kRowsPerDma + lrow;
-      const int64_t r = t.m0 + (row < t.tile_rows ? row : 0);  // rows past a half tile: a valid row
-      int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
-      if (tok < 0) tok = 0;  // padding row: any valid row (its outputs are never read)
-      aoff[i] = (uint32_t)(tok * lda * 2) + ((lslot ^ C::swz(row)) << 4);
+      tok[i] = (int)t.m0 + (row < t.tile_rows ? row : 0);
+    }
+    if (g.row_token) {
+#pragma unroll
+      for (int i = 0; i < C::kADma; ++i) tok[i] = g.row_token[tok[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < C::kADma; ++i) {
+      const int row = wave * (TM / WAVES) + i * C::kRowsPerDma + lrow;
+      const int64_t r = tok[i] < 0 ? 0 : tok[i];  // padding row: any valid row (its outputs are never read)
+      aoff[i] = (uint32_t)(r * lda * 2) + ((lslot ^ C::swz(row)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
@@ -680,9 +825,12 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
   if (cur.seg < 0) return;
   prepare(cur);
   issue(0);
+  Tile nxt = describe(L + G);
+  // stores the previous tile issued after this tile's first K-step loads: vmcnt retires in
+  // issue order, so a count of that many means the K-step has landed while the stores may still
+  // be in flight
+  int stores_behind = 0;
   while (true) {
-    const int64_t Ln = L + G;
-    const Tile nxt = describe(Ln);
     const bool active = mrow0 < cur.tile_rows;   // false only for the upper half of a half tile
     // the loads of the step after kt: this tile's next one, or the next tile's first
     auto issue_next = [&](int kt) {
@@ -700,8 +848,9 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
       for (int c = 0; c < NBW; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+    // the first K-step's loads
+    wait_loads_behind_stores(stores_behind);
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<0>();
       // a bare barrier: stage `consumed` has landed and the other buffer is no longer read
       __builtin_amdgcn_s_barrier();
       if (active) {
@@ -744,14 +893,26 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
         issue_next(kt);
       }
       ++consumed;
+      // the next K-step's loads
+      if (kt + 1 < nk) wait_vmcnt<0>();
     }
-    if (active)
-      store_tile<SWIGLU, MB, NBW>(acc, static_cast<uint16_t*>(g.out), cur.m0 + mrow0,
-                                  cur.nt * (SWIGLU ? WROWS / 2 : WROWS) + wn * (SWIGLU ? WRW / 2 : WRW), N, l32,
-                                  khalf);
+    // the tile after next, described now: the wait for its table reads then covers the
+    // prefetched loads only, not this tile's stores
+    const Tile nxt2 = nxt.seg >= 0 ? describe(L + 2 * G) : nxt;
+    // the tile's output through the stage no load is filling (stage `issued` mod 2, the one the
+    // last K-step read)
+    lds_barrier();   // every wavefront is done reading the stage
+    uint16_t* stg = lds + (issued % C::kStages) * C::kStageElems;
+    if constexpr (SWIGLU)
+      stores_behind = store_tile_staged_swiglu(acc, stg, static_cast<uint16_t*>(g.out), cur.m0, cur.nt * (WROWS / 2),
+                                               N, cur.tile_rows, wave, wm, wn, lane);
+    else
+      stores_behind = store_tile_staged(acc, stg, static_cast<uint16_t*>(g.out), cur.m0, cur.nt * WROWS, N,
+                                        cur.tile_rows, wave, wm, wn, lane);
     if (nxt.seg < 0) break;
     cur = nxt;
-    L = Ln;
+    nxt = nxt2;
+    L += G;
   }
 }
 
@@ -777,6 +938,8 @@ hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
   }
   const int NT = (int)ceil_div(g.N, EPI == 1 ? 128 : 256);
   if (g.max_pairs * NT == 0) return hipSuccess;
+  // the walk's tile indices (up to two grid strides past the last tile) and the table slots are int
+  if (g.max_tiles * NT + 2 * (int64_t)n_cu >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   // one workgroup per CU (the LDS stages allow no more), a multiple of the 8 x 32 tile block
   const int64_t span = kXcds * SC::kXcdChunk;
   const int64_t grid = std::max<int64_t>(span, (int64_t)n_cu / span * span);
@@ -789,13 +952,17 @@ hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
 // 256 x 256 output tile has only a handful of K-steps, so a one-tile workgroup spends much of its
 // time filling its pipeline and draining its stores.  Each workgroup instead walks a fixed
 // sequence of tiles (logical tile i * G + 32 x + j for the workgroup in slot j of XCD x, G
-// workgroups, so an XCD keeps a run of one expert's tiles) and issues the first K-step of its next
-// tile during the last K-step of the current one, so those loads overlap the stores.  The stage
-// ring runs on across tiles (the issued and consumed stage counts pick the LDS buffer).
+// workgroups, so an XCD keeps a run of one expert's tiles: blocks of 4 M-tiles x all N-tiles)
+// and issues the first K-step of its next tile during the last K-step of the current one; the
+// output goes out through LDS as whole row spans after those loads and stays in flight through
+// the next tile's first K-step, as in the persistent kernel above.  The segment table is copied
+// to LDS, so describing a tile takes no global load.  The stage ring runs on across tiles (the
+// issued and consumed stage counts pick the LDS buffer).
 __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g, int NT, int64_t n_tiles) {
   constexpr int BK = 64, TM = 256, WROWS = 256, WAVES = 8, WN = 4, RW = 128, MB = 4, WRW = 64, NBW = 2;
   using C = StreamCfg<BK, WAVES, WROWS, 1, TM>;
   static_assert(C::kStages == 2, "two LDS stages");
+  static_assert(C::kStageElems == (TM / 2) * WROWS, "a stage holds half an output tile");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -808,19 +975,33 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
   int64_t L = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
   if (L >= n_tiles) return;
 
+  // The segment table, copied to LDS behind the operand stages: a tile's description then
+  // needs no global load, whose wait would also drain the previous tile's stores.
+  int32_t* seg_off = reinterpret_cast<int32_t*>(lds + C::kStages * C::kStageElems);
+  for (int i = tid; i <= g.n_seg; i += C::kThreads) seg_off[i] = g.seg_off[i];
+  __syncthreads();
+
   struct Tile {
     int seg, nt, tile_rows, nk;
     int64_t m0, k_base;
   };
+  // an expert's tiles in blocks of kGM M-tiles x all N-tiles, M fastest: the 32 workgroups of an
+  // XCD then hold about kGM M-tiles x 32 / kGM N-tiles and share both operands' slices in L2
+  constexpr int kGM = 4;
   auto describe = [&](int64_t l) {
     Tile t;
     t.seg = (int)(l / per);
     const int rem = (int)(l - (int64_t)t.seg * per);
-    t.nt = rem / MT;
-    t.m0 = (int64_t)(rem % MT) * TM;
+    const int blk = rem / (kGM * NT);
+    const int gm = min(kGM, MT - blk * kGM);
+    const int r2 = rem - blk * kGM * NT;
+    t.nt = r2 / gm;
+    t.m0 = (int64_t)(blk * kGM + r2 % gm) * TM;
     t.tile_rows = min(TM, g.wg_m - (int)t.m0);
-    t.k_base = g.seg_off[t.seg];
-    t.nk = (int)((g.seg_off[t.seg + 1] - t.k_base) / BK);
+    const int k0 = __builtin_amdgcn_readfirstlane(seg_off[t.seg]);
+    const int k1 = __builtin_amdgcn_readfirstlane(seg_off[t.seg + 1]);
+    t.k_base = k0;
+    t.nk = (k1 - k0) / BK;
     return t;
   };
   // per-lane load sources of the tile being loaded, as in the streaming kernel
@@ -865,15 +1046,18 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
   Tile cur = describe(L);
   prepare(cur);
   if (cur.nk > 0) issue(0);
+  // stores the previous tile issued after this tile's first K-step loads: vmcnt retires in
+  // issue order, so a count of that many means the K-step has landed while the stores may still
+  // be in flight
+  int stores_behind = 0;
   while (true) {
     const int64_t Ln = L + G;
     const bool has_next = Ln < n_tiles;
+    const Tile nxt = has_next ? describe(Ln) : cur;
     // the next tile's first K-step, issued once this tile's last one is being computed
     auto prefetch_next = [&]() {
-      if (!has_next) return;
-      const Tile t = describe(Ln);
-      if (t.nk > 0) {
-        prepare(t);
+      if (has_next && nxt.nk > 0) {
+        prepare(nxt);
         issue(0);
       }
     };
@@ -885,8 +1069,9 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
       for (int c = 0; c < NBW; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+    // the first K-step's loads
+    wait_loads_behind_stores(stores_behind);
     for (int kt = 0; kt < cur.nk; ++kt) {
-      wait_vmcnt<0>();
       // a bare barrier: stage `consumed` has landed and the other buffer is no longer read
       __builtin_amdgcn_s_barrier();
       if (kt + 1 < cur.nk)
@@ -918,18 +1103,29 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
         }
       }
       ++consumed;
+      // the next K-step's loads (issued before this step's MFMAs)
+      if (kt + 1 < cur.nk) wait_vmcnt<0>();
     }
-    // a tile without K-steps (an empty segment) prefetched nothing for the next one
-    if (cur.nk == 0) prefetch_next();
-    // segment cur.seg's matrix of the routed or shared output (an empty segment writes zeros)
-    if (active) {
+    // a tile without K-steps (an empty segment) prefetched nothing for the next one; its loads
+    // go to the stage the previous tile's rows were read back from, once every wavefront is
+    // done with them
+    if (cur.nk == 0) {
+      lds_barrier();
+      prefetch_next();
+    }
+    // segment cur.seg's matrix of the routed or shared output (an empty segment writes zeros),
+    // staged through the stage no load is filling: stage `issued` mod 2, the one this tile's last
+    // K-step read
+    {
       const bool shared = cur.seg >= g.n_routed;
       const int e = shared ? cur.seg - g.n_routed : cur.seg;
       uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
-      store_tile<false, MB, NBW>(acc, out, cur.m0 + mrow0, cur.nt * WROWS + wn * WRW, N, l32, khalf);
+      lds_barrier();   // every wavefront is done reading the stage
+      stores_behind = store_tile_staged(acc, lds + (issued % C::kStages) * C::kStageElems, out, cur.m0,
+                                        cur.nt * WROWS, N, cur.tile_rows, wave, wm, wn, lane);
     }
     if (!has_next) break;
-    cur = describe(Ln);
+    cur = nxt;
     L = Ln;
   }
 }
@@ -940,12 +1136,16 @@ hipError_t launch_wgrad_bf16(const GemmOperands& g, hipStream_t st) {
   // 32-bit byte offsets address the transposed activation matrices
   if ((int64_t)g.wg_m * g.lda * 2 >= (int64_t(1) << 32) || (int64_t)g.N * g.ldw * 2 >= (int64_t(1) << 32))
     return hipErrorInvalidValue;
-  const size_t lds_bytes = C::kStages * C::kStageElems * sizeof(uint16_t);
+  // operand stages, then the segment table (n_seg + 1 offsets)
+  const size_t stage_bytes = C::kStages * C::kStageElems * sizeof(uint16_t);
+  const size_t max_lds = stage_bytes + (size_t)(kMaxRouted + kMaxShared + 1) * sizeof(int32_t);
+  if (max_lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
+  const size_t lds_bytes = stage_bytes + (size_t)(g.n_seg + 1) * sizeof(int32_t);
   static bool attr_set = false;
   static int n_cu = 0;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_bf16_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
     if (err != hipSuccess) return err;
     int dev = 0;
     if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
