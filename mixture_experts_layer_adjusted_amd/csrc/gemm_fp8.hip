@@ -83,6 +83,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// LDS traffic of this wavefront done (lgkmcnt 0; vmcnt 63 and expcnt 7 are no wait), then a bare
+// barrier that leaves global loads, LDS DMA and stores in flight; the empty asm statements keep
+// the compiler from moving memory accesses across it
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // 32 bytes of row r starting at 16-byte chunk c (c even): two swizzled 16-byte reads
 __device__ __forceinline__ i32x8 frag32(const uint8_t* st, int r, int c) {
   u32x4 a = *reinterpret_cast<const u32x4*>(st + boff(r, c));
@@ -401,65 +411,88 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
 // segment holds a few hundred rows, so a 256 x 256 output tile has only a few K-steps and a
 // one-tile workgroup spends most of its time filling its pipeline and draining its stores.
 // Here each workgroup walks a fixed sequence of tiles (logical tile i * G + 32 x + j for the
-// workgroup in slot j of XCD x, G workgroups, so an XCD keeps a run of one expert's tiles) and
-// the loads of a tile's first K-step go out during the last K-step of the tile before it, so
-// they overlap that tile's stores.  The stage ring runs on across tiles: the consumed and
-// issued stage counts pick the LDS buffer.
+// workgroup in slot j of XCD x, G workgroups, so an XCD keeps a run of one expert's tiles: blocks
+// of 4 M-tiles x all N-tiles) and the loads of a tile's first K-step go out during the last K-step
+// of the tile before it.  The bf16 output goes out through LDS as whole 512-byte row spans (the
+// 16 x 16 MFMA layout gives 16 rows x 32 bytes per store instruction), after those loads, and
+// stays in flight through the next tile's first K-step: that wait counts the stores (vmcnt
+// retires in issue order).  The segment table is copied to LDS, so describing a tile takes no
+// global load, whose wait would drain the stores.  The stage ring runs on across tiles: the
+// consumed and issued stage counts pick the LDS buffer.
 __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperands g, int NT, int64_t n_tiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  static_assert(kDataBytes == 128 * 512, "a stage's operand bytes hold 128 rows of bf16 output");
+  constexpr int kRounds = 8;   // row-span stores per wavefront per staged half
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int N = g.N;
   const int64_t lda = g.lda, ldw = g.ldw;
   const int MT = (g.wg_m + kTM - 1) / kTM;
-  const int64_t per = (int64_t)MT * NT;
-  const int64_t G = gridDim.x;
-  int64_t L = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+  const int per = MT * NT;
+  const int G = gridDim.x;
+  int L = (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds);
   if (L >= n_tiles) return;
 
+  int32_t* seg_off = reinterpret_cast<int32_t*>(lds + kStages * kStageBytes);
+  for (int i = tid; i <= g.n_seg; i += kThreads) seg_off[i] = g.seg_off[i];
+  __syncthreads();
+
   struct Tile {
-    int seg, nt, tile_rows, nk;
-    int64_t m0, k_base;
+    int seg, nt, tile_rows, nk, m0, k_base;
   };
-  auto describe = [&](int64_t l) {
+  // an expert's tiles in blocks of kGM M-tiles x all N-tiles, M fastest (the launcher keeps the
+  // tile indices, walk included, below 2^31; row and column indices fit 32 bits)
+  constexpr int kGM = 4;
+  auto describe = [&](int l) {
     Tile t;
-    t.seg = (int)(l / per);
-    const int rem = (int)(l - (int64_t)t.seg * per);
-    t.nt = rem / MT;
-    t.m0 = (int64_t)(rem % MT) * kTM;
-    t.tile_rows = min(kTM, g.wg_m - (int)t.m0);
-    t.k_base = g.seg_off[t.seg];
-    t.nk = (int)((g.seg_off[t.seg + 1] - t.k_base) / kBK);
+    t.seg = l / per;
+    const int rem = l - t.seg * per;
+    const int blk = rem / (kGM * NT);
+    const int gm = min(kGM, MT - blk * kGM);
+    const int r2 = rem - blk * kGM * NT;
+    t.nt = r2 / gm;
+    t.m0 = (blk * kGM + r2 % gm) * kTM;
+    t.tile_rows = min(kTM, g.wg_m - t.m0);
+    const int k0 = __builtin_amdgcn_readfirstlane(seg_off[t.seg]);
+    const int k1 = __builtin_amdgcn_readfirstlane(seg_off[t.seg + 1]);
+    t.k_base = k0;
+    t.nk = (k1 - k0) / kBK;
     return t;
   };
   // per-lane load sources of the tile being loaded (as in grouped_gemm_fp8_kernel): 32-bit byte
   // offsets from the wave-uniform bases act_base / w_base; lanes 0..31 load activation-row scales,
   // lanes 32..63 weight-row scales, wave w's 64 dwords landing at [64w, 64w + 64)
-  const int lrow = lane >> 3, lslot = lane & 7;
   uint32_t aoff[kADma], woff[kWDma];
   const uint8_t* act_base = nullptr;
   const uint8_t* w_base = nullptr;
   const float* ssrc = nullptr;
+  // (32-bit offset arithmetic: the launcher checks wg_m * lda and N * ldw against 2^32)
+  const uint32_t lda32 = (uint32_t)lda, ldw32 = (uint32_t)ldw;
   auto prepare = [&](const Tile& t) {
+    // the per-lane parts are derived here from an opaque lane index rather than kept live
+    // across the MFMAs, where registers are short
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lrow = ln >> 3, lslot = ln & 7;
     const int n0 = t.nt * kWRows;
 #pragma unroll
     for (int i = 0; i < kADma; ++i) {
       const int row = wave * (kTM / kWaves) + i * kRowsPerDma + lrow;
-      aoff[i] = (uint32_t)((t.m0 + (row < t.tile_rows ? row : 0)) * lda) + ((lslot ^ swz(row)) << 4);
+      aoff[i] = (uint32_t)(t.m0 + (row < t.tile_rows ? row : 0)) * lda32 + ((lslot ^ swz(row)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < kWDma; ++i) {
       const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;
-      woff[i] = (uint32_t)((int64_t)min(n0 + r, N - 1) * ldw) + ((lslot ^ swz(kTM + r)) << 4);
+      woff[i] = (uint32_t)min(n0 + r, N - 1) * ldw32 + ((lslot ^ swz(kTM + r)) << 4);
     }
     act_base = static_cast<const uint8_t*>(g.act) + t.k_base;
     w_base = static_cast<const uint8_t*>(g.w_routed[0]) + t.k_base;
-    if (lane < 32) {
-      const int row = wave * 32 + lane;
-      ssrc = g.act_scale + (t.m0 + (row < t.tile_rows ? row : 0)) * (lda / kBK) + t.k_base / kBK;
+    if (ln < 32) {
+      const int row = wave * 32 + ln;
+      ssrc = g.act_scale + (int64_t)(t.m0 + (row < t.tile_rows ? row : 0)) * (lda / kBK) + t.k_base / kBK;
     } else {
-      ssrc = g.s_routed[0] + (int64_t)min(n0 + wave * 32 + lane - 32, N - 1) * (ldw / kBK) + t.k_base / kBK;
+      ssrc = g.s_routed[0] + (int64_t)min(n0 + wave * 32 + ln - 32, N - 1) * (ldw / kBK) + t.k_base / kBK;
     }
   };
   int issued = 0, consumed = 0;
@@ -490,10 +523,14 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
   Tile cur = describe(L);
   prepare(cur);
   if (cur.nk > 0) issue(0);
+  // stores the previous tile issued after this tile's first K-step loads
+  int stores_behind = 0;
   while (true) {
-    const int64_t Ln = L + G;
+    const int Ln = L + G;
     const bool has_next = Ln < n_tiles;
-    // the next tile's first K-step, issued once this tile's last one is being computed
+    // the next tile's first K-step, issued once this tile's last one is being computed (a
+    // description is two LDS reads, so it is not carried across the K-loop, where scalar
+    // registers are short)
     auto prefetch_next = [&]() {
       if (!has_next) return;
       const Tile t = describe(Ln);
@@ -508,8 +545,14 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
     for (int a = 0; a < kMB; ++a)
 #pragma unroll
       for (int c = 0; c < kNB; ++c) acc[a][c] = zero;
-    for (int kt = 0; kt < cur.nk; ++kt) {
+    // the first K-step's loads
+    if (stores_behind == 2 * kRounds)
+      wait_vmcnt<2 * kRounds>();
+    else if (stores_behind == kRounds)
+      wait_vmcnt<kRounds>();
+    else
       wait_vmcnt<0>();
+    for (int kt = 0; kt < cur.nk; ++kt) {
       // a bare barrier: stage `consumed` has landed and the other buffer is no longer read
       __builtin_amdgcn_s_barrier();
       if (kt + 1 < cur.nk)
@@ -542,28 +585,66 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
         }
       }
       ++consumed;
+      // the next K-step's loads
+      if (kt + 1 < cur.nk) wait_vmcnt<0>();
     }
-    // a tile without K-steps (an empty segment) prefetched nothing for the next one
-    if (cur.nk == 0) prefetch_next();
+    // a tile without K-steps (an empty segment) prefetched nothing for the next one; its loads
+    // go to the stage the previous tile's rows were read back from, once every wavefront is
+    // done with them
+    if (cur.nk == 0) {
+      lds_barrier();
+      prefetch_next();
+    }
     // ---- epilogue: segment cur.seg's matrix of the routed or shared output (an empty segment
-    // writes zeros); lane holds row mrow0 + 16 mb + l16, features 4 kq + (0..3) of each block
-    if (active) {
+    // writes zeros), through the stage no load is filling (stage `issued` mod 2, the one the last
+    // K-step read) in two passes: pass p stages accumulator blocks 4p..4p+3 of every wavefront
+    // (tile rows wm * 128 + 64 p + [0, 64) as staged rows wm * 64 + [0, 64)), 512-byte rows whose
+    // 16-byte chunk c sits at slot c ^ (row mod 32); the lane holds row 16 mb + l16 of its
+    // wavefront, features 4 kq + (0..3) of each 16-feature block.  The typed LDS accesses keep the
+    // compiler from making them wait for the loads and stores in flight; every store has an
+    // active lane (N is a multiple of 128), so the store count is exact.
+    {
       const bool shared = cur.seg >= g.n_routed;
       const int e = shared ? cur.seg - g.n_routed : cur.seg;
       uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
+      uint16_t* stg = reinterpret_cast<uint16_t*>(lds + (issued % kStages) * kStageBytes);
       const int n0 = cur.nt * kWRows;
+      const int rounds = cur.tile_rows > kTM / 2 ? kRounds : kRounds / 2;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));   // per-lane offsets computed here, not hoisted across the MFMAs
+      lds_barrier();                 // every wavefront is done reading the stage
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        uint16_t* orow = out + (cur.m0 + mrow0 + mb * 16 + l16) * N;
+      for (int p = 0; p < 2; ++p) {
+        if (p > 0) lds_barrier();   // the first pass has been read back
+        if (active) {
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const int f = n0 + wrow[nb] + kq * 4;  // N is a multiple of 128, so f < N covers f + 3
-          if (f < N)
-            *reinterpret_cast<uint2*>(orow + f) =
-                make_uint2((uint32_t)f32_to_bf16(acc[mb][nb][0]) | ((uint32_t)f32_to_bf16(acc[mb][nb][1]) << 16),
-                           (uint32_t)f32_to_bf16(acc[mb][nb][2]) | ((uint32_t)f32_to_bf16(acc[mb][nb][3]) << 16));
+          for (int h = 0; h < 4; ++h) {
+            const int r = wm * 64 + h * 16 + (ln & 15);
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb) {
+              const int c = wn * 8 + nb * 2 + ((ln >> 4) >> 1);
+              const f32x4& a = acc[4 * p + h][nb];
+              const uint64_t lo = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+              const uint64_t hi = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+              *reinterpret_cast<uint64_t*>(stg + r * 256 + ((c ^ (r & 31)) << 3) + ((ln >> 4) & 1) * 4) =
+                  lo | (hi << 32);
+            }
+          }
+        }
+        lds_barrier();
+        const int c = ln & 31;
+        const int f = n0 + c * 8;
+#pragma unroll
+        for (int i = 0; i < kRounds; ++i) {
+          if (i < rounds) {
+            const int r = (i * kWaves + wave) * 2 + (ln >> 5);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((c ^ (r & 31)) << 3));
+            const int64_t row = (int64_t)cur.m0 + (r >> 6) * 128 + p * 64 + (r & 63);
+            if (f < N) *reinterpret_cast<u32x4*>(out + row * N + f) = v;
+          }
         }
       }
+      stores_behind = 2 * rounds;
     }
     if (!has_next) break;
     cur = describe(Ln);
@@ -576,12 +657,16 @@ hipError_t launch_wgrad_fp8(const GemmOperands& g, hipStream_t st) {
     return hipErrorInvalidValue;
   if ((int64_t)g.wg_m * g.lda >= (int64_t(1) << 32) || (int64_t)g.N * g.ldw >= (int64_t(1) << 32))
     return hipErrorInvalidValue;
-  const size_t lds_bytes = kStages * kStageBytes;
+  // operand stages, then the segment table (n_seg + 1 offsets)
+  const size_t stage_bytes = (size_t)kStages * kStageBytes;
+  const size_t max_lds = stage_bytes + (size_t)(kMaxRouted + kMaxShared + 1) * sizeof(int32_t);
+  if (max_lds > 163840) return hipErrorInvalidValue;
+  const size_t lds_bytes = stage_bytes + (size_t)(g.n_seg + 1) * sizeof(int32_t);
   static bool attr_set = false;
   static int n_cu = 0;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_fp8_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
     if (err != hipSuccess) return err;
     int dev = 0;
     if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
@@ -593,6 +678,8 @@ hipError_t launch_wgrad_fp8(const GemmOperands& g, hipStream_t st) {
   if (tiles == 0) return hipSuccess;
   // one workgroup per CU (the LDS stages allow no more), a multiple of the XCD count
   const int64_t grid = std::max<int64_t>(kXcds, (int64_t)n_cu / kXcds * kXcds);
+  // tile indices, walk included, are int
+  if (tiles + grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(grouped_wgrad_fp8_kernel, dim3((unsigned)grid), dim3(kThreads), lds_bytes, st, g, NT, tiles);
   return hipGetLastError();
 }
