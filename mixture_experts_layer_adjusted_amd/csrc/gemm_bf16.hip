@@ -724,16 +724,28 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
   };
   // the 256-row tile of logical index l, in the XCD-aware within-expert order of the streaming
   // kernel; seg < 0 past the last one
+  // The per-segment tables, copied to LDS behind the operand stages: describing a tile then
+  // takes one global read, the segment of its 256-row slot (seg_of), which the walk issues a
+  // tile ahead of use.
+  int32_t* s_pair_off = reinterpret_cast<int32_t*>(lds + C::kStages * C::kStageElems);
+  int32_t* s_seg_off = s_pair_off + g.n_seg + 1;
+  for (int i = tid; i <= g.n_seg; i += C::kThreads) {
+    s_pair_off[i] = g.pair_off[i];
+    s_seg_off[i] = g.seg_off[i];
+  }
+  __syncthreads();
   // (tile indices, walk included, stay below 2^31: the launcher checks)
-  auto describe = [&](int l) {
-    Tile t{-1, 0, 0, 0};
+  auto seg_of = [&](int l) {
     const int slot = l / NT;
-    if (slot >= max_slots) return t;
+    return slot < max_slots ? g.pair_seg[slot] : -1;
+  };
+  auto describe = [&](int l, int seg_read) {
+    Tile t{-1, 0, 0, 0};
     // wave-uniform table entries, kept in scalar registers
-    const int seg = __builtin_amdgcn_readfirstlane(g.pair_seg[slot]);
+    const int seg = __builtin_amdgcn_readfirstlane(seg_read);
     if (seg < 0) return t;
-    const int seg_first = __builtin_amdgcn_readfirstlane(g.pair_off[seg]);
-    const int seg_count = __builtin_amdgcn_readfirstlane(g.pair_off[seg + 1]) - seg_first;
+    const int seg_first = __builtin_amdgcn_readfirstlane(s_pair_off[seg]);
+    const int seg_count = __builtin_amdgcn_readfirstlane(s_pair_off[seg + 1]) - seg_first;
     const int lam = l - seg_first * NT;
     const int grp = lam / (kGroupM * NT);
     const int gm = min(kGroupM, seg_count - grp * kGroupM);
@@ -741,8 +753,8 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
     const int local = grp * kGroupM + rem % gm;
     t.seg = seg;
     t.nt = rem / gm;
-    t.m0 = (int64_t)__builtin_amdgcn_readfirstlane(g.seg_off[seg]) + (int64_t)local * TM;
-    t.tile_rows = min(TM, __builtin_amdgcn_readfirstlane(g.seg_off[seg + 1]) - (int)t.m0);
+    t.m0 = (int64_t)__builtin_amdgcn_readfirstlane(s_seg_off[seg]) + (int64_t)local * TM;
+    t.tile_rows = min(TM, __builtin_amdgcn_readfirstlane(s_seg_off[seg + 1]) - (int)t.m0);
     return t;
   };
   // per-lane load sources of the tile being loaded (as in the streaming kernel)
@@ -821,16 +833,20 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
   const int l32 = lane & 31, khalf = lane >> 5;
   const int mrow0 = wm * RW;
 
-  Tile cur = describe(L);
+  Tile cur = describe(L, seg_of(L));
   if (cur.seg < 0) return;
   prepare(cur);
   issue(0);
-  Tile nxt = describe(L + G);
+  Tile nxt = describe(L + G, seg_of(L + G));
   // stores the previous tile issued after this tile's first K-step loads: vmcnt retires in
   // issue order, so a count of that many means the K-step has landed while the stores may still
   // be in flight
   int stores_behind = 0;
   while (true) {
+    // the segment of the tile after next, read here so that its latency passes under this tile's
+    // first K-step (it is issued after the previous tile's stores, which only makes the counted
+    // wait below stricter)
+    const int seg2 = nxt.seg >= 0 ? seg_of(L + 2 * G) : -1;
     const bool active = mrow0 < cur.tile_rows;   // false only for the upper half of a half tile
     // the loads of the step after kt: this tile's next one, or the next tile's first
     auto issue_next = [&](int kt) {
@@ -896,9 +912,8 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
       // the next K-step's loads
       if (kt + 1 < nk) wait_vmcnt<0>();
     }
-    // the tile after next, described now: the wait for its table reads then covers the
-    // prefetched loads only, not this tile's stores
-    const Tile nxt2 = nxt.seg >= 0 ? describe(L + 2 * G) : nxt;
+    // the tile after next, described from LDS before this tile's stores go out
+    const Tile nxt2 = describe(L + 2 * G, seg2);
     // the tile's output through the stage no load is filling (stage `issued` mod 2, the one the
     // last K-step read)
     lds_barrier();   // every wavefront is done reading the stage
@@ -923,13 +938,18 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
 template <int EPI, bool WKN>
 hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
   using SC = StreamCfg<64, 8, 256, 1, 256>;
-  const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
+  // operand stages, then the pair_off and seg_off tables (n_seg + 1 entries each)
+  const size_t stage_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
+  const size_t max_lds = stage_bytes + 2 * (size_t)(kMaxRouted + kMaxShared + 1) * sizeof(int32_t);
+  static_assert(SC::kStages * SC::kStageElems * 2 + 2 * (kMaxRouted + kMaxShared + 1) * 4 <= kLdsBytes, "LDS");
+  if (g.n_seg < 1 || g.n_seg > kMaxRouted + kMaxShared) return hipErrorInvalidValue;
+  const size_t lds_bytes = stage_bytes + 2 * (size_t)(g.n_seg + 1) * sizeof(int32_t);
   auto kern = &grouped_gemm_bf16_persistent_kernel<EPI, WKN>;
   static bool attr_set = false;
   static int n_cu = 0;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
     if (err != hipSuccess) return err;
     int dev = 0;
     if ((err = hipGetDevice(&dev)) != hipSuccess) return err;

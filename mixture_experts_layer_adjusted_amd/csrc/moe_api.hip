@@ -185,6 +185,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
   g1.pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
   g1.n_routed = s.n_routed;
+  g1.n_seg = s.n_routed + s.n_shared;
   g1.K = s.hidden;
   g1.N = s.inter;
   g1.act_rows = s.tokens;
@@ -209,6 +210,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g2.pair_seg = g1.pair_seg;
   g2.pair_off = g1.pair_off;
   g2.n_routed = s.n_routed;
+  g2.n_seg = g1.n_seg;
   g2.K = s.inter;
   g2.N = s.hidden;
   g2.act_rows = p.max_rows;
@@ -374,6 +376,7 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
     g.pair_seg = reinterpret_cast<const int32_t*>(at(p.pair_seg));
     g.pair_off = reinterpret_cast<const int32_t*>(at(p.pair_off));
     g.n_routed = s.n_routed;
+    g.n_seg = (int)(Nr + Ns);
     g.max_tiles = p.max_tiles;
     g.max_pairs = max_pairs;
     // dH (before the gate) = dout[token] W_down, the W_down codes [d][I] and scales read K-major
@@ -549,6 +552,7 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
     g.pair_seg = pair_seg;
     g.pair_off = pair_off;
     g.n_routed = s.n_routed;
+    g.n_seg = (int)(Nr + Ns);
     g.K = K;
     g.N = N;
     g.act_rows = act_rows;

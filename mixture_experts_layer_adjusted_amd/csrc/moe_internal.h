@@ -135,7 +135,8 @@ struct GemmOperands {
   // act[m, k] * w_routed[0][n, k] (transposed activations, row strides lda and ldw), m < wg_m;
   // routed segments write out + e M N, shared ones out2 + (e - N_r) M N
   int64_t lda, ldw;
-  int wg_m, n_seg;
+  int wg_m;
+  int n_seg;                 // segments (N_r + N_s): entries of seg_off / pair_off minus one
   // input-gradient products (bf16, FP8): the weights are read K-major, as stored ([K rows][N features] per
   // expert, the w_*[0] matrix for K rows [0, kn_split), the w_*[1] matrix for the rest)
   int kn_split;
