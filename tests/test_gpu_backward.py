@@ -73,6 +73,12 @@ def _small(name, T, d, N, K, Ns, I, bias="uniform0.01", cid=60):
     _small("bwd-small", 200, 256, 16, 4, 1, 128),
     _small("bwd-two-shared", 512, 512, 16, 4, 2, 256, cid=61),
     _small("bwd-no-shared-ragged", 77, 384, 8, 3, 0, 384, cid=62),
+    # the most segments the library takes (512 routed + 64 shared): the segment tables the
+    # persistent kernels copy to LDS at their largest; at T=512 most routed segments hold a few
+    # rows or none (weight-gradient tiles without K-steps), at T=8192 the input-gradient
+    # products run on full 256-row tiles
+    _small("bwd-max-segments-sparse", 512, 128, 512, 8, 64, 128, cid=66),
+    _small("bwd-max-segments", 8192, 128, 512, 8, 64, 128, cid=67),
 ], ids=lambda c: c.name)
 def test_backward_parity_small(cfg):
     print(f"backward: {cfg.name} T={cfg.tokens} d={cfg.hidden} N={cfg.n_routed} K={cfg.top_k} "

@@ -111,6 +111,9 @@ def _setup(cfg, dev=None):
     _small("fp8-bwd-small", 200, 256, 16, 4, 1, 128, cid=70),
     _small("fp8-bwd-two-shared", 512, 512, 16, 4, 2, 256, cid=71),
     _small("fp8-bwd-no-shared-ragged", 77, 384, 8, 3, 0, 384, cid=72),
+    # 512 routed + 64 shared segments (the largest segment table, copied to LDS by the
+    # weight-gradient kernel), most routed segments with a few rows or none
+    _small("fp8-bwd-max-segments-sparse", 512, 128, 512, 8, 64, 128, cid=77),
 ], ids=lambda c: c.name)
 def test_fp8_backward_parity_small(cfg):
     print(f"fp8 backward: {cfg.name} T={cfg.tokens} d={cfg.hidden} N={cfg.n_routed} K={cfg.top_k} "

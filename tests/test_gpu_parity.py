@@ -129,6 +129,33 @@ def test_edge_shapes(cfg):
     _run_and_check_small(cfg)
 
 
+def test_max_segments_persistent_forward():
+    """512 routed + 64 shared experts at T=8192, K_r=8: T K_r / N_r = 128 rows per routed expert,
+    so the forward takes the persistent 256 x 256 GEMMs with their segment tables in LDS at the
+    largest size the library accepts.  Every 7th token is compared with the oracle."""
+    cfg = _edge("max-segments", 8192, 128, 512, 8, 64, 128, cid=52)
+    print(f"forward: {cfg.name} T={cfg.tokens} d={cfg.hidden} N={cfg.n_routed} K={cfg.top_k} "
+          f"Ns={cfg.n_shared} I={cfg.inter}", flush=True)
+    assert cfg.tokens * cfg.top_k >= 128 * cfg.n_routed   # not the small-segment tiles
+    h, hf = _host_layer(cfg)
+    r = Runner(cfg, host_to_device(h))
+    r.route()
+    r.forward()
+    torch.cuda.synchronize()
+    idx_g = r.idx.cpu().numpy()
+    idx_o, g_o, load_o, s_o, c_o, gap_o = O.route(hf["u"], hf["centroids"], hf["bias"], cfg.top_k)
+    check_routing(idx_g, r.gate.cpu().numpy(), r.load.cpu().numpy(), s_o, c_o, idx_o, gap_o, cfg.n_routed)
+    toks = np.arange(0, cfg.tokens, 7)
+    idx_s = idx_g[toks].astype(np.int64)
+    shared = list(zip(hf["sh_gate"], hf["sh_up"], hf["sh_down"]))
+    y_ref = O.layer_forward(hf["u"][toks], idx_s, O.gates(s_o[toks], idx_s),
+                            O.stacked(hf["w_gate"], hf["w_up"], hf["w_down"]), shared)
+    y = to_host_f32(r.out)[toks]
+    e_all, e_exp = rel_err(y, y_ref, hf["u"][toks])
+    print("relative errors:", round(e_all, 5), round(e_exp, 5), flush=True)
+    assert e_all <= TOL[cfg.dtype] and e_exp <= TOL[cfg.dtype], (e_all, e_exp)
+
+
 def test_expert_with_zero_load_and_spiked_experts():
     cfg = _edge("bias-spike", 256, 256, 32, 4, 1, 128)
     b = host.bias_vector(cfg).copy()
