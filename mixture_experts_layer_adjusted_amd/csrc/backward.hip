@@ -14,7 +14,8 @@
 //              (blocked partial sums in a fixed order), dg_k is the fixed-order sum of the
 //              per-tile partials the gate/up backward GEMM wrote, then dz, and du_t summed in a
 //              fixed order (residual, routed rows, shared rows, centroid terms);
-//  dcentroid:  de_i by a fixed-order loop over the rows of segment i.
+//  dcentroid:  de_i in two fixed-order passes: per 128-row tile of segment i (rows in order), then
+//              over the segment's tiles (in order).
 #include "fp8_codec.h"
 #include "moe_internal.h"
 
@@ -161,31 +162,70 @@ __global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(
   }
 }
 
-// de[i, j] = sum over the real rows r of segment i of row_dz[r] * u[row_token[r], j]
-__global__ void __launch_bounds__(256) dcentroid_kernel(const uint16_t* __restrict__ u,
-                                                        const int32_t* __restrict__ row_token,
-                                                        const float* __restrict__ row_dz,
-                                                        const int32_t* __restrict__ seg_off,
-                                                        const int32_t* __restrict__ seg_rows, int d,
-                                                        float* __restrict__ de) {
-  const int i = blockIdx.x;
-  const int j = blockIdx.y * 256 + threadIdx.x;
-  if (j >= d) return;
-  const int r0 = seg_off[i], r1 = r0 + seg_rows[i];
-  float acc = 0.0f;
-  int r = r0;
-  for (; r + 4 <= r1; r += 4) {
-    float v[4], w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[q] = __uint_as_float((uint32_t)u[(int64_t)row_token[r + q] * d + j] << 16);
-      w[q] = row_dz[r + q];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc = fmaf(w[q], v[q], acc);
+// de in two fixed-order passes, so that a segment with many rows (the Zipf head) does not hold
+// one workgroup while the rest of the chip idles.  Pass 1, one workgroup per (128-row M-tile of a
+// routed segment, 1024 columns): part[t, j] = sum over the real rows r of tile t, in row order,
+// of row_dz[r] * u[row_token[r], j], 8 columns per lane from 16-byte loads.  Pass 2:
+// de[i, j] = sum over the M-tiles t of segment i, in tile order, of part[t, j]; a segment without
+// rows writes zeros.  d is a multiple of 8.
+constexpr int kDcThreads = 128;
+constexpr int kDcCols = kDcThreads * 8;
+
+__global__ void __launch_bounds__(kDcThreads) dcentroid_part_kernel(const uint16_t* __restrict__ u,
+                                                                    const int32_t* __restrict__ row_token,
+                                                                    const float* __restrict__ row_dz,
+                                                                    const int32_t* __restrict__ tile_seg,
+                                                                    int n_routed, int d, float* __restrict__ part) {
+  const int t = blockIdx.x;
+  const int e = tile_seg[t];
+  if (e < 0 || e >= n_routed) return;   // a shared-expert tile or past the last one: never read
+  __shared__ int32_t tok[kTileM];
+  __shared__ float dz[kTileM];
+  for (int i = threadIdx.x; i < kTileM; i += kDcThreads) {
+    const int64_t r = (int64_t)t * kTileM + i;
+    tok[i] = row_token[r];
+    dz[i] = row_dz[r];
   }
-  for (; r < r1; ++r) acc = fmaf(row_dz[r], __uint_as_float((uint32_t)u[(int64_t)row_token[r] * d + j] << 16), acc);
-  de[(int64_t)i * d + j] = acc;
+  __syncthreads();
+  const int j = blockIdx.y * kDcCols + threadIdx.x * 8;
+  if (j >= d) return;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+  for (int i = 0; i < kTileM; ++i) {
+    const int tk = tok[i];
+    if (tk < 0) continue;   // padding row
+    const uint4 q = *reinterpret_cast<const uint4*>(u + (int64_t)tk * d + j);
+    const float w = dz[i];
+    const uint32_t x[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] = fmaf(w, __uint_as_float(x[k] << 16), acc[2 * k]);
+      acc[2 * k + 1] = fmaf(w, __uint_as_float(x[k] & 0xFFFF0000u), acc[2 * k + 1]);
+    }
+  }
+  float* o = part + (int64_t)t * d + j;
+  *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+__global__ void __launch_bounds__(kDcThreads) dcentroid_sum_kernel(const float* __restrict__ part,
+                                                                   const int32_t* __restrict__ seg_off, int d,
+                                                                   float* __restrict__ de) {
+  const int e = blockIdx.x;
+  const int j = blockIdx.y * kDcCols + threadIdx.x * 8;
+  if (j >= d) return;
+  const int t0 = seg_off[e] / kTileM, t1 = seg_off[e + 1] / kTileM;
+  float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), b = a;
+  for (int t = t0; t < t1; ++t) {
+    const float* p = part + (int64_t)t * d + j;
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    const float4 y = *reinterpret_cast<const float4*>(p + 4);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+  }
+  float* o = de + (int64_t)e * d + j;
+  *reinterpret_cast<float4*>(o) = a;
+  *reinterpret_cast<float4*>(o + 4) = b;
 }
 
 // dst[b][c * ldd + off + r] = scale[r] * src[b][gather[r] * lds + c] for r < R, c < C (bf16):
@@ -328,9 +368,18 @@ hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* cen
 }
 
 hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* row_token, const float* row_dz,
-                            const int32_t* seg_off, const int32_t* seg_rows, float* de, hipStream_t st) {
-  hipLaunchKernelGGL(dcentroid_kernel, dim3((unsigned)s.n_routed, (unsigned)ceil_div(s.hidden, 256)), dim3(256), 0,
-                     st, static_cast<const uint16_t*>(u), row_token, row_dz, seg_off, seg_rows, s.hidden, de);
+                            const int32_t* seg_off, const int32_t* tile_seg, int64_t max_tiles, float* part, float* de,
+                            hipStream_t st) {
+  if (s.hidden % 8 != 0) return hipErrorInvalidValue;
+  const unsigned cols = (unsigned)ceil_div(s.hidden, kDcCols);
+  if (max_tiles > 0) {
+    hipLaunchKernelGGL(dcentroid_part_kernel, dim3((unsigned)max_tiles, cols), dim3(kDcThreads), 0, st,
+                       static_cast<const uint16_t*>(u), row_token, row_dz, tile_seg, s.n_routed, s.hidden, part);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(dcentroid_sum_kernel, dim3((unsigned)s.n_routed, cols), dim3(kDcThreads), 0, st, part, seg_off,
+                     s.hidden, de);
   return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   p.bwd_row_gate = take((size_t)p.max_rows * 4);
   p.bwd_row_dz = take((size_t)p.max_rows * 4);
   p.bwd_dg_part = take((size_t)p.max_rows * (I / 128 > 0 ? I / 128 : 1) * 4);
+  p.bwd_dc_part = take((size_t)p.max_tiles * d * 4);
   const size_t eb = fp8 ? 1 : 2;   // bytes per element of the transposed copies
   const int64_t P = p.max_rows, d8 = d / 128, i8 = I / 128, p8 = P / 128;
 
@@ -503,7 +504,8 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
   const int32_t* row_token = reinterpret_cast<const int32_t*>(wsb + p.row_token);
   const int32_t* perm_row = reinterpret_cast<const int32_t*>(wsb + p.perm_row);
   const int32_t* seg_off = reinterpret_cast<const int32_t*>(wsb + p.seg_off);
-  const int32_t* seg_rows = reinterpret_cast<const int32_t*>(wsb + p.seg_rows);
+  const int32_t* tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
+  float* dc_part = reinterpret_cast<float*>(wsb + p.bwd_dc_part);
   float* row_gate = reinterpret_cast<float*>(wsb + p.bwd_row_gate);
   float* row_dz = reinterpret_cast<float*>(wsb + p.bwd_row_dz);
   float* dg_part = reinterpret_cast<float*>(wsb + p.bwd_dg_part);
@@ -524,7 +526,8 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
     return rc;
   if (fp8) {
     if ((rc = fp8_backward(s, p, wsb, u, centroids, w, topk_idx, dout, du, dw, stream)) != MOE_OK) return rc;
-    return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, seg_rows, d_centroids, stream));
+    return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, tile_seg, p.max_tiles, dc_part,
+                                       d_centroids, stream));
   }
   const int64_t Nr = s.n_routed, Ns = s.n_shared, P = p.max_rows;
   uint16_t* dy_t = reinterpret_cast<uint16_t*>(wsb + p.bwd_dy_t);   // [d][P]
@@ -536,7 +539,6 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
     TransposeArgs t{bf(src), lds, src_b, gather, scale, dst, ldd, off, dst_b, (int)R, (int)C};
     return hip_status(launch_transpose(t, (int)batch, stream));
   };
-  const int32_t* tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
   const int32_t* pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
   const int32_t* pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
   const int64_t max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + Nr + Ns) / 2);
@@ -615,7 +617,8 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
   if ((rc = wgrad(dy_t, (int)d, h_t, (int)I, dw->w_down, dw->sh_down)) != MOE_OK) return rc;
   if ((rc = wgrad(dab_t, (int)I, x_t, (int)d, dw->w_gate, dw->sh_gate)) != MOE_OK) return rc;
   if ((rc = wgrad(dab_t + I * P, (int)I, x_t, (int)d, dw->w_up, dw->sh_up)) != MOE_OK) return rc;
-  return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, seg_rows, d_centroids, stream));
+  return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, tile_seg, p.max_tiles, dc_part,
+                                     d_centroids, stream));
 }
 
 moe_status moe_update_bias(int32_t n_routed, int64_t total_assignments, const int32_t* expert_load, float* bias,

@@ -52,6 +52,7 @@ struct WorkspacePlan {
   size_t bwd_row_gate;      // fp32 [max_rows]
   size_t bwd_row_dz;        // fp32 [max_rows]
   size_t bwd_dg_part;       // fp32 [max_rows, I / 128]
+  size_t bwd_dc_part;       // fp32 [max_tiles, d]  centroid-gradient partial sums per M-tile
   // transposed activations: bf16, or E4M3 codes for FP8_B128 (per run of 128 rows, with the
   // scales below)
   size_t bwd_dy_t;          // [d, max_rows]      (gate * dout of each row) transposed
@@ -178,8 +179,10 @@ hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const fl
 hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* centroids, const int32_t* idx,
                              const int32_t* perm_row, const float* dg_part, const int32_t* seg_off, const void* dout,
                              const void* dX, void* du, float* row_dz, hipStream_t st);
+// part: fp32 [max_tiles, d] per-tile partial sums
 hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* row_token, const float* row_dz,
-                            const int32_t* seg_off, const int32_t* seg_rows, float* de, hipStream_t st);
+                            const int32_t* seg_off, const int32_t* tile_seg, int64_t max_tiles, float* part, float* de,
+                            hipStream_t st);
 
 hipError_t launch_gemm_swiglu(int dtype, const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_down(int dtype, const GemmOperands& g, hipStream_t st);
