@@ -400,11 +400,125 @@ __device__ __forceinline__ int store_tile_staged_swiglu(const f32x16 (&acc)[4][2
   return rounds;
 }
 
-// wait until at most n (0, 4, 8 or 16: the stores a staged epilogue issued after the loads
-// being waited for) vector memory operations are outstanding
+// SwiGLU backward epilogue of a 256 x 128 tile (a, b = the gate and up accumulators of features
+// n0 + [0, 128), rows m0 + [0, tile_rows)), through an LDS stage no load is filling:
+//   dH before the gate (g.dh, [rows, N]) comes in by direct loads into the stage (256-byte rows
+//   whose 16-byte chunk c sits at slot c ^ (row mod 16)) and is read into registers in the
+//   accumulator layout;
+//   with dh = row_gate * dH:  dA = dh b sg (1 + a (1 - sg)),  dB = dh a sg,  H = a sg b
+//   (sg = sigmoid(a)), written to g.out ([rows, 2N]: dA then dB) and g.out2 ([rows, N]);
+//   g.dg_part[row, nt] = sum over the 128 features of dH H, the four wavefronts of a row added in
+//   order through red.
+// Four passes, pass p taking accumulator block p of every wavefront (tile rows wm * 128 + 32 p +
+// [0, 32), staged rows 32 wm + [0, 32)): its dA, dB and H (3 x 16 KB) go through the stage and
+// out as whole 256-byte row spans, after which that block's accumulators are dead.  Waits for
+// every load in flight (the prefetched K-step included) before reading dH.  Returns the stores
+// every wavefront issued (some issue one more: the dg_part rows).
+__device__ __forceinline__ int store_tile_staged_swiglu_bwd(const f32x16 (&acc)[4][2], uint16_t* stg,
+                                                            const GemmOperands& g, int64_t m0, int n0, int nt,
+                                                            int tile_rows, int wave, int wm, int wn, int lane,
+                                                            float (*red)[4]) {
+  asm volatile("" : "+v"(lane));   // as in store_tile_staged
+  const int N = g.N;
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const bool full = tile_rows > 128;
+  // dH rows m0 + r (r beyond the tile: its last row), four rows per 1 KB load
+  {
+    const uint16_t* dh = static_cast<const uint16_t*>(g.dh);
+    const int slot = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kStagedRounds; ++i) {
+      const int r = (i * 8 + wave) * 4 + (lane >> 4);
+      const int rr = r < tile_rows ? r : tile_rows - 1;
+      int f = n0 + 8 * (slot ^ (r & 15));
+      if (f + 8 > N) f = N - 8;   // beyond the last feature: any valid chunk (never stored)
+      lds_dma16(dh + (m0 + rr) * N + f, stg + (i * 8 + wave) * 4 * 128);
+    }
+  }
+  float rg[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int r = wm * 128 + mb * 32 + l32;
+    rg[mb] = g.row_gate[m0 + (r < tile_rows ? r : tile_rows - 1)];
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+  const bool active = wm * 128 < tile_rows;
+  uint64_t dq[4][4];
+  if (active) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int r = wm * 128 + mb * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * 4 + q;
+        dq[mb][q] = *reinterpret_cast<const uint64_t*>(stg + r * 128 + ((c ^ (r & 15)) << 3) + khalf * 4);
+      }
+    }
+  }
+  uint16_t* dab = static_cast<uint16_t*>(g.out);
+  uint16_t* hout = static_cast<uint16_t*>(g.out2);
+  const int c = lane & 15;
+  const int f = n0 + c * 8;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    lds_barrier();   // the stage's previous contents (dH, or the last pass) have been read
+    if (active) {
+      const int sr = wm * 32 + l32;   // staged row
+      float part = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float oa[4], ob[4], oh[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float dhu = __uint_as_float(((uint32_t)(dq[p][q] >> (16 * v)) & 0xFFFFu) << 16);
+          const float a = acc[p][0][q * 4 + v], b = acc[p][1][q * 4 + v];
+          const float sg = 1.0f / (1.0f + __expf(-a));
+          const float dhv = rg[p] * dhu;
+          oa[v] = dhv * b * sg * (1.0f + a * (1.0f - sg));
+          ob[v] = dhv * a * sg;
+          oh[v] = a * sg * b;
+          part += dhu * oh[v];
+        }
+        const int off = sr * 128 + (((wn * 4 + q) ^ (sr & 15)) << 3) + khalf * 4;
+        *reinterpret_cast<uint64_t*>(stg + off) = pack_bf16x4(oa[0], oa[1], oa[2], oa[3]);
+        *reinterpret_cast<uint64_t*>(stg + 8192 + off) = pack_bf16x4(ob[0], ob[1], ob[2], ob[3]);
+        *reinterpret_cast<uint64_t*>(stg + 16384 + off) = pack_bf16x4(oh[0], oh[1], oh[2], oh[3]);
+      }
+      part += __shfl_xor(part, 32, 64);
+      if (khalf == 0) red[wm * 128 + p * 32 + l32][wn] = part;
+    }
+    lds_barrier();
+    // 3 outputs x 64 staged rows x 16 chunks: each load/store covers four rows of one output;
+    // staged rows 32 and up (wavefronts wm = 1) are absent from a half tile
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int blk = i * 8 + wave;          // 0..47
+      const int o = blk >> 4;                // dA, dB, H
+      const int sr = (blk & 15) * 4 + (lane >> 4);
+      if (full || (blk & 15) < 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + o * 8192 + sr * 128 + ((c ^ (sr & 15)) << 3));
+        const int64_t row = m0 + (sr >> 5) * 128 + p * 32 + (sr & 31);
+        uint16_t* dst = o == 2 ? hout + row * N + f : dab + row * 2 * (int64_t)N + (o == 1 ? N : 0) + f;
+        if (f < N) *reinterpret_cast<u32x4*>(dst) = v;
+      }
+    }
+  }
+  // red was complete at the last pass's second barrier
+  const int t = wave * 64 + lane;
+  if (t < tile_rows) g.dg_part[(m0 + t) * (N / 128) + nt] = red[t][0] + red[t][1] + red[t][2] + red[t][3];
+  return full ? 24 : 12;
+}
+
+// wait until at most n (0, 4, 8, 12, 16 or 24: the stores a staged epilogue issued after the
+// loads being waited for) vector memory operations are outstanding
 __device__ __forceinline__ void wait_loads_behind_stores(int n) {
-  if (n == 16)
+  if (n == 24)
+    wait_vmcnt<24>();
+  else if (n == 16)
     wait_vmcnt<16>();
+  else if (n == 12)
+    wait_vmcnt<12>();
   else if (n == 8)
     wait_vmcnt<8>();
   else if (n == 4)
@@ -700,8 +814,8 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
 // them.  Tiles past the last 256-row tile end the walk (their slots only grow).
 template <int EPI, bool WKN>
 __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmOperands g, int NT) {
-  constexpr bool SWIGLU = EPI == 1;
-  static_assert(EPI == 0 || EPI == 1, "plain store or SwiGLU");
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
+  static_assert(EPI == 0 || EPI == 1 || EPI == 2, "plain store, SwiGLU or SwiGLU backward");
   static_assert(!WKN || EPI == 0, "K-major weights: plain store");
   constexpr int BK = 64, TM = 256, WROWS = 256, WAVES = 8, WN = 4, RW = 128, MB = 4, WRW = 64, NBW = 2;
   using C = StreamCfg<BK, WAVES, WROWS, 1, TM>;
@@ -729,6 +843,8 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
   // tile ahead of use.
   int32_t* s_pair_off = reinterpret_cast<int32_t*>(lds + C::kStages * C::kStageElems);
   int32_t* s_seg_off = s_pair_off + g.n_seg + 1;
+  // SwiGLU backward: per-row partials of the gate gradient, one per wavefront of the row
+  float(*red)[4] = reinterpret_cast<float(*)[4]>(s_seg_off + g.n_seg + 1);
   for (int i = tid; i <= g.n_seg; i += C::kThreads) {
     s_pair_off[i] = g.pair_off[i];
     s_seg_off[i] = g.seg_off[i];
@@ -918,7 +1034,10 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
     // last K-step read)
     lds_barrier();   // every wavefront is done reading the stage
     uint16_t* stg = lds + (issued % C::kStages) * C::kStageElems;
-    if constexpr (SWIGLU)
+    if constexpr (EPI == 2)
+      stores_behind = store_tile_staged_swiglu_bwd(acc, stg, g, cur.m0, cur.nt * (WROWS / 2), cur.nt, cur.tile_rows,
+                                                   wave, wm, wn, lane, red);
+    else if constexpr (SWIGLU)
       stores_behind = store_tile_staged_swiglu(acc, stg, static_cast<uint16_t*>(g.out), cur.m0, cur.nt * (WROWS / 2),
                                                N, cur.tile_rows, wave, wm, wn, lane);
     else
@@ -938,12 +1057,14 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
 template <int EPI, bool WKN>
 hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
   using SC = StreamCfg<64, 8, 256, 1, 256>;
-  // operand stages, then the pair_off and seg_off tables (n_seg + 1 entries each)
+  // operand stages, then the pair_off and seg_off tables (n_seg + 1 entries each), then (SwiGLU
+  // backward) the per-row gate-gradient partials
+  constexpr size_t red_bytes = EPI == 2 ? 256 * 4 * sizeof(float) : 0;
   const size_t stage_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
-  const size_t max_lds = stage_bytes + 2 * (size_t)(kMaxRouted + kMaxShared + 1) * sizeof(int32_t);
-  static_assert(SC::kStages * SC::kStageElems * 2 + 2 * (kMaxRouted + kMaxShared + 1) * 4 <= kLdsBytes, "LDS");
+  const size_t max_lds = stage_bytes + 2 * (size_t)(kMaxRouted + kMaxShared + 1) * sizeof(int32_t) + red_bytes;
+  static_assert(SC::kStages * SC::kStageElems * 2 + 2 * (kMaxRouted + kMaxShared + 1) * 4 + 4096 <= kLdsBytes, "LDS");
   if (g.n_seg < 1 || g.n_seg > kMaxRouted + kMaxShared) return hipErrorInvalidValue;
-  const size_t lds_bytes = stage_bytes + 2 * (size_t)(g.n_seg + 1) * sizeof(int32_t);
+  const size_t lds_bytes = stage_bytes + 2 * (size_t)(g.n_seg + 1) * sizeof(int32_t) + red_bytes;
   auto kern = &grouped_gemm_bf16_persistent_kernel<EPI, WKN>;
   static bool attr_set = false;
   static int n_cu = 0;
@@ -956,8 +1077,9 @@ hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
     if ((err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
     attr_set = true;
   }
-  const int NT = (int)ceil_div(g.N, EPI == 1 ? 128 : 256);
+  const int NT = (int)ceil_div(g.N, EPI == 0 ? 256 : 128);
   if (g.max_pairs * NT == 0) return hipSuccess;
+  if (EPI == 2 && g.N % 128 != 0) return hipErrorInvalidValue;   // dg_part holds N / 128 tiles per row
   // the walk's tile indices (up to two grid strides past the last tile) and the table slots are int
   if (g.max_tiles * NT + 2 * (int64_t)n_cu >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   // one workgroup per CU (the LDS stages allow no more), a multiple of the 8 x 32 tile block
@@ -1216,6 +1338,7 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
     if constexpr (EPI == 2) {
       // 256 x 256 tiles (the SwiGLU-backward epilogue assumes four wavefronts of one gate and
       // one up block per row)
+      if (MOE_PERSISTENT_GEMM) return launch_persistent<EPI, false>(g, st);
       return launch_stream<EPI, 64, 8, 256, 1, 2, 256>(g, st);
     } else {
       // segments of a few rows (decode-like batches, expected routed rows per expert below one
