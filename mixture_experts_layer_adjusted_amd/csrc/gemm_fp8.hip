@@ -288,11 +288,19 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
         }
         sw[nb] = sc[kTM + wblk[nb]];
       }
+      // token fragments one block ahead, so that each block's LDS reads are in flight while the
+      // previous block's MFMAs run
+      i32x8 xf_next = frag32(st, mrow0 + l16, kq * 2);
+      float sa_next = sc[mrow0 + l16];
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
-        const int r = mrow0 + mb * 16 + l16;
-        const i32x8 xf = frag32(st, r, kq * 2);
-        const float sa = sc[r];
+        const i32x8 xf = xf_next;
+        const float sa = sa_next;
+        if (mb + 1 < kMB) {
+          const int rn = mrow0 + (mb + 1) * 16 + l16;
+          xf_next = frag32(st, rn, kq * 2);
+          sa_next = sc[rn];
+        }
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
           const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb], xf, zero, 0, 0, 0, kE8M0One, 0,
@@ -570,11 +578,18 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
           const int j = wrow[nb] + kq * 4;
           swr[nb] = *reinterpret_cast<const f32x4*>(sc + 64 * (j >> 5) + 32 + (j & 31));
         }
+        // token fragments one block ahead (as in grouped_gemm_fp8_kernel)
+        i32x8 xf_next = frag32(st, mrow0 + l16, kq * 2);
+        float sa_next = sc[64 * ((mrow0 + l16) >> 5) + ((mrow0 + l16) & 31)];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-          const int r = mrow0 + mb * 16 + l16;
-          const i32x8 xf = frag32(st, r, kq * 2);
-          const float sa = sc[64 * (r >> 5) + (r & 31)];
+          const i32x8 xf = xf_next;
+          const float sa = sa_next;
+          if (mb + 1 < kMB) {
+            const int rn = mrow0 + (mb + 1) * 16 + l16;
+            xf_next = frag32(st, rn, kq * 2);
+            sa_next = sc[64 * (rn >> 5) + (rn & 31)];
+          }
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
             const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[nb], xf, zero, 0, 0, 0, kE8M0One,
