@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(
     const int32_t* __restrict__ perm_row, const float* __restrict__ dg_part, int NT,
     const int32_t* __restrict__ seg_off, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ dX, int d,
     int N, int K, int Ns, uint16_t* __restrict__ du, float* __restrict__ row_dz) {
-  __shared__ float red[kMaxTopK][kRouterThreads];
+  __shared__ float wsum[kRouterThreads / 64][kMaxTopK];
   __shared__ float s_k[kMaxTopK], dg_k[kMaxTopK], dz_k[kMaxTopK];
   __shared__ int32_t e_k[kMaxTopK], row_k[kMaxTopK];
   const int64_t t = blockIdx.x;
@@ -78,19 +78,22 @@ __global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(
     row_k[tid] = ok ? r : -1;
   }
   __syncthreads();
-  // logits of the selected experts: per-thread partial sums over 8-element slices, then a
-  // fixed-order sum over the threads
+  // logits of the selected experts, eight at a time: per-thread partial dot products over the
+  // thread's 8-column slices (the u slice loaded once for all eight), then a fixed-order butterfly
+  // within each wavefront and the wavefronts' sums in order
   const uint16_t* urow = u + t * d;
-  for (int k = 0; k < K; ++k) {
-    float acc = 0.0f;
-    const int e = e_k[k];
-    if (e >= 0) {
-      const float* erow = E + (int64_t)e * d;
-      for (int j = tid * 8; j < d; j += kRouterThreads * 8) {
-        float uv[8];
-        load8(urow + j, uv);
-        const float4 e0 = *reinterpret_cast<const float4*>(erow + j);
-        const float4 e1 = *reinterpret_cast<const float4*>(erow + j + 4);
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = tid * 8; j < d; j += kRouterThreads * 8) {
+      float uv[8];
+      load8(urow + j, uv);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int e = k0 + kk < K ? e_k[k0 + kk] : -1;
+        if (e < 0) continue;
+        const float* erow = E + (int64_t)e * d + j;
+        const float4 e0 = *reinterpret_cast<const float4*>(erow);
+        const float4 e1 = *reinterpret_cast<const float4*>(erow + 4);
         float part = 0.0f;
         part = fmaf(uv[0], e0.x, part);
         part = fmaf(uv[1], e0.y, part);
@@ -100,15 +103,21 @@ __global__ void __launch_bounds__(kRouterThreads) router_bwd_kernel(
         part = fmaf(uv[5], e1.y, part);
         part = fmaf(uv[6], e1.z, part);
         part = fmaf(uv[7], e1.w, part);
-        acc += part;
+        acc[kk] += part;
       }
     }
-    red[k][tid] = acc;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      float v = acc[kk];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if ((tid & 63) == 0 && k0 + kk < K) wsum[tid >> 6][k0 + kk] = v;
+    }
   }
   __syncthreads();
   if (tid < K) {
     float z = 0.0f;
-    for (int i = 0; i < kRouterThreads; ++i) z += red[tid][i];
+    for (int w = 0; w < kRouterThreads / 64; ++w) z += wsum[w][tid];
     float dg = 0.0f;
     const int r = row_k[tid];
     if (r >= 0)
