@@ -338,11 +338,9 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(TransposeQuantArgs
   const float scale = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
   uint32_t w[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    w[k] = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[k] |= e4m3_from_f32(__fdiv_rn(v[4 * k + i], scale)) << (8 * i);
-  }
+  for (int k = 0; k < 8; ++k)
+    w[k] = e4m3x4_from_f32(__fdiv_rn(v[4 * k], scale), __fdiv_rn(v[4 * k + 1], scale), __fdiv_rn(v[4 * k + 2], scale),
+                           __fdiv_rn(v[4 * k + 3], scale));
   uint8_t* drow = a.dst + (int64_t)(c0 + c) * a.ldd + j0 + 32 * q;
   *reinterpret_cast<uint4*>(drow) = make_uint4(w[0], w[1], w[2], w[3]);
   *reinterpret_cast<uint4*>(drow + 16) = make_uint4(w[4], w[5], w[6], w[7]);

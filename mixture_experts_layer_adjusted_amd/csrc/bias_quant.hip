@@ -56,9 +56,11 @@ __global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restri
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
     const float scale = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-    uint32_t o[2] = {0u, 0u};
+    uint32_t o[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j >> 2] |= e4m3_from_f32(__fdiv_rn(v[j], scale)) << (8 * (j & 3));
+    for (int h = 0; h < 2; ++h)
+      o[h] = e4m3x4_from_f32(__fdiv_rn(v[4 * h], scale), __fdiv_rn(v[4 * h + 1], scale), __fdiv_rn(v[4 * h + 2], scale),
+                             __fdiv_rn(v[4 * h + 3], scale));
     if (live) {
       *reinterpret_cast<uint2*>(codes + r * cols + c0) = make_uint2(o[0], o[1]);
       if (sub == 0) scales[t] = scale;
@@ -106,8 +108,8 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = 16 * i + 4 * j;
-      o[j] = e4m3_from_f32(__fdiv_rn(v[b], scale)) | (e4m3_from_f32(__fdiv_rn(v[b + 1], scale)) << 8) |
-             (e4m3_from_f32(__fdiv_rn(v[b + 2], scale)) << 16) | (e4m3_from_f32(__fdiv_rn(v[b + 3], scale)) << 24);
+      o[j] = e4m3x4_from_f32(__fdiv_rn(v[b], scale), __fdiv_rn(v[b + 1], scale), __fdiv_rn(v[b + 2], scale),
+                             __fdiv_rn(v[b + 3], scale));
     }
     *reinterpret_cast<uint4*>(dst + (int64_t)r * cols + c + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
   }

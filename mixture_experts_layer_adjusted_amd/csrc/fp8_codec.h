@@ -34,4 +34,13 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
   return sign | code;
 }
 
+// Four values to their E4M3FN codes, packed lowest first, by gfx950's packed conversion
+// instruction (round to nearest even).  For |v| <= 464 it gives exactly e4m3_from_f32's codes
+// (checked on the GPU for every fp32 bit pattern of that range, both signs); every quantiser here
+// divides values by amax / 448, so its inputs stay within 448 (1 + 2^-23).
+__device__ __forceinline__ uint32_t e4m3x4_from_f32(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 }  // namespace moe

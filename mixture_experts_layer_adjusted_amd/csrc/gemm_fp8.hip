@@ -393,9 +393,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const int f = n0 + wn * 32 + nb * 16 + kq * 4;
-          uint32_t w = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) w |= e4m3_from_f32(__fdiv_rn(acc[mb][nb][v], scale)) << (8 * v);
+          const uint32_t w = e4m3x4_from_f32(__fdiv_rn(acc[mb][nb][0], scale), __fdiv_rn(acc[mb][nb][1], scale),
+                                             __fdiv_rn(acc[mb][nb][2], scale), __fdiv_rn(acc[mb][nb][3], scale));
           *reinterpret_cast<uint32_t*>(orow + f) = w;
         }
         if (wn == 0 && kq == 0) g.out_scale[(m0 + r) * IB + n0 / kBK] = scale;
