@@ -93,6 +93,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+
 // 32 bytes of row r starting at 16-byte chunk c (c even): two swizzled 16-byte reads
 __device__ __forceinline__ i32x8 frag32(const uint8_t* st, int r, int c) {
   u32x4 a = *reinterpret_cast<const u32x4*>(st + boff(r, c));
@@ -106,6 +107,56 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// A 256 x 256 bf16 output tile held in the 16 x 16 MFMA layout (wavefront (wm, wn): rows
+// wm * 128 + 16 mb + (lane mod 16), columns wn * 64 + 16 nb + 4 (lane / 16) + 0..3) written to
+// out (row stride N, rows m0 + [0, tile_rows), columns n0 + [0, 256) below N) through an LDS stage
+// of at least 64 KB that no load is filling, as whole 512-byte row spans: pass p stages
+// accumulator blocks 4p..4p+3 of every wavefront (tile rows wm * 128 + 64 p + [0, 64) as staged
+// rows wm * 64 + [0, 64)), 16-byte chunk c of a staged row at slot c ^ (row mod 32).  The LDS
+// accesses are typed so that the compiler does not make them wait for memory traffic in flight.
+// Every store has an active lane (N is a multiple of 128), so the returned count of this
+// wavefront's stores is exact.
+__device__ __forceinline__ int store_tile_staged16(const f32x4 (&acc)[kMB][kNB], uint8_t* stage, uint16_t* out,
+                                                   int64_t m0, int n0, int N, int tile_rows, int wave, int wm,
+                                                   int wn, int lane) {
+  constexpr int kRounds = 8;   // row-span stores per wavefront per staged half
+  asm volatile("" : "+v"(lane));   // per-lane offsets computed here, not hoisted across the MFMAs
+  uint16_t* stg = reinterpret_cast<uint16_t*>(stage);
+  const bool active = wm * (kTM / 2) < tile_rows;
+  const int rounds = tile_rows > kTM / 2 ? kRounds : kRounds / 2;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (p > 0) lds_barrier();   // the first pass has been read back
+    if (active) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int r = wm * 64 + h * 16 + (lane & 15);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const int c = wn * 8 + nb * 2 + ((lane >> 4) >> 1);
+          const f32x4& a = acc[4 * p + h][nb];
+          const uint64_t lo = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+          const uint64_t hi = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+          *reinterpret_cast<uint64_t*>(stg + r * 256 + ((c ^ (r & 31)) << 3) + ((lane >> 4) & 1) * 4) = lo | (hi << 32);
+        }
+      }
+    }
+    lds_barrier();
+    const int c = lane & 31;
+    const int f = n0 + c * 8;
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      if (i < rounds) {
+        const int r = (i * kWaves + wave) * 2 + (lane >> 5);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((c ^ (r & 31)) << 3));
+        const int64_t row = m0 + (r >> 6) * 128 + p * 64 + (r & 63);
+        if (f < N) *reinterpret_cast<u32x4*>(out + row * N + f) = v;
+      }
+    }
+  }
+  return 2 * rounds;
+}
 
 // EPI: 0 plain bf16 store, 1 SwiGLU with H quantised, 2 SwiGLU backward.
 // WKN (with EPI 0): the weight codes are read K-major as stored ([K rows][N features] per
@@ -400,20 +451,11 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
         if (wn == 0 && kq == 0) g.out_scale[(m0 + r) * IB + n0 / kBK] = scale;
       }
     }
-  } else if (active) {
-    uint16_t* out = static_cast<uint16_t*>(g.out);
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      uint16_t* orow = out + (m0 + mrow0 + mb * 16 + l16) * N;
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int f = n0 + wrow[nb] + kq * 4;  // N is a multiple of 128, so f < N covers f + 3
-        if (f < N)
-          *reinterpret_cast<uint2*>(orow + f) =
-              make_uint2((uint32_t)f32_to_bf16(acc[mb][nb][0]) | ((uint32_t)f32_to_bf16(acc[mb][nb][1]) << 16),
-                         (uint32_t)f32_to_bf16(acc[mb][nb][2]) | ((uint32_t)f32_to_bf16(acc[mb][nb][3]) << 16));
-      }
-    }
+  } else {
+    // whole row spans through stage nk mod 2: the last K-step read the other stage, and every
+    // wavefront passed that step's barrier after its reads of this one (nk = 1: never used)
+    store_tile_staged16(acc, lds + (nk % kStages) * kStageBytes, static_cast<uint16_t*>(g.out), m0, n0, N, tile_rows,
+                        wave, wm, wn, lane);
   }
 }
 
@@ -614,55 +656,15 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
       prefetch_next();
     }
     // ---- epilogue: segment cur.seg's matrix of the routed or shared output (an empty segment
-    // writes zeros), through the stage no load is filling (stage `issued` mod 2, the one the last
-    // K-step read) in two passes: pass p stages accumulator blocks 4p..4p+3 of every wavefront
-    // (tile rows wm * 128 + 64 p + [0, 64) as staged rows wm * 64 + [0, 64)), 512-byte rows whose
-    // 16-byte chunk c sits at slot c ^ (row mod 32); the lane holds row 16 mb + l16 of its
-    // wavefront, features 4 kq + (0..3) of each 16-feature block.  The typed LDS accesses keep the
-    // compiler from making them wait for the loads and stores in flight; every store has an
-    // active lane (N is a multiple of 128), so the store count is exact.
+    // writes zeros) as staged row spans, through the stage no load is filling (stage `issued`
+    // mod 2, the one the last K-step read)
     {
       const bool shared = cur.seg >= g.n_routed;
       const int e = shared ? cur.seg - g.n_routed : cur.seg;
       uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
-      uint16_t* stg = reinterpret_cast<uint16_t*>(lds + (issued % kStages) * kStageBytes);
-      const int n0 = cur.nt * kWRows;
-      const int rounds = cur.tile_rows > kTM / 2 ? kRounds : kRounds / 2;
-      int ln = lane;
-      asm volatile("" : "+v"(ln));   // per-lane offsets computed here, not hoisted across the MFMAs
-      lds_barrier();                 // every wavefront is done reading the stage
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        if (p > 0) lds_barrier();   // the first pass has been read back
-        if (active) {
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const int r = wm * 64 + h * 16 + (ln & 15);
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
-              const int c = wn * 8 + nb * 2 + ((ln >> 4) >> 1);
-              const f32x4& a = acc[4 * p + h][nb];
-              const uint64_t lo = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
-              const uint64_t hi = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
-              *reinterpret_cast<uint64_t*>(stg + r * 256 + ((c ^ (r & 31)) << 3) + ((ln >> 4) & 1) * 4) =
-                  lo | (hi << 32);
-            }
-          }
-        }
-        lds_barrier();
-        const int c = ln & 31;
-        const int f = n0 + c * 8;
-#pragma unroll
-        for (int i = 0; i < kRounds; ++i) {
-          if (i < rounds) {
-            const int r = (i * kWaves + wave) * 2 + (ln >> 5);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * 256 + ((c ^ (r & 31)) << 3));
-            const int64_t row = (int64_t)cur.m0 + (r >> 6) * 128 + p * 64 + (r & 63);
-            if (f < N) *reinterpret_cast<u32x4*>(out + row * N + f) = v;
-          }
-        }
-      }
-      stores_behind = 2 * rounds;
+      lds_barrier();   // every wavefront is done reading the stage
+      stores_behind = store_tile_staged16(acc, lds + (issued % kStages) * kStageBytes, out, cur.m0, cur.nt * kWRows, N,
+                                          cur.tile_rows, wave, wm, wn, lane);
     }
     if (!has_next) break;
     cur = describe(Ln);
