@@ -68,6 +68,15 @@ R16 FP8 backward (the page's FP8 paragraph names the forward GEMM and both backw
     Parity of this reading is pinned by its reduction to R14 with every quantiser and
     rounding replaced by the identity, by exact scaling under powers of two, and by the
     distance to R14 that the E4M3 grid allows.
+R17 bf16 backward storage (the page fixes no precision for the bf16 path): R16's steps with
+    no quantiser, the tensors held between steps (dH, H, dA, dB) rounded to bf16 and
+    gate * dout rounded once to bf16 from its fp32 product; the saved-input variant also
+    holds the SwiGLU inputs a and b in bf16 from the forward.  Outputs whose condition
+    number magnifies these roundings past the bf16 tolerance (the centroid gradient of an
+    expert picked by one or two tokens, where the two terms of ds nearly cancel) are checked
+    against this model; every other output against R14 itself.  Pinned by its reduction to
+    R14 when the roundings are the identity, by the saved-input variant equalling the plain
+    one where a and b are bf16 values, and by the distance to R14 that bf16 allows.
 """
 from __future__ import annotations
 
@@ -482,6 +491,10 @@ class ExactPolicy:
     def scaled(g, x):      # gate * dout
         return np.asarray(g, dtype=np.float64)[:, None] * np.asarray(x, dtype=np.float64)
 
+    @staticmethod
+    def saved(x):          # the SwiGLU inputs a, b as the backward reads them
+        return np.asarray(x, dtype=np.float64)
+
 
 class Fp8Policy:
     """The quantisers and storage precisions of R16."""
@@ -497,6 +510,28 @@ class Fp8Policy:
     def scaled(g, x):      # one fp32 product per element
         return (np.asarray(g, dtype=np.float32)[:, None] * np.asarray(x, dtype=np.float32)).astype(np.float64)
 
+    saved = ExactPolicy.saved   # a, b recomputed in the backward
+
+
+class Bf16Policy:
+    """The storage precisions of R17: no quantiser, held tensors in bf16, gate * dout rounded
+    once to bf16 from its fp32 product, a and b recomputed."""
+
+    tiles = ExactPolicy.tiles
+    runs = ExactPolicy.runs
+    held = staticmethod(bf16_round)
+    saved = ExactPolicy.saved
+
+    @staticmethod
+    def scaled(g, x):
+        return bf16_round(np.asarray(g, dtype=np.float32)[:, None] * np.asarray(x, dtype=np.float32))
+
+
+class Bf16SavedPolicy(Bf16Policy):
+    """R17 with a and b held in bf16 from the forward (the saved-input variant)."""
+
+    saved = staticmethod(bf16_round)
+
 
 def expert_backward(x, dy, u_rows, dout_rows, g, wg, wu, wd, q):
     """One expert's part of layer_backward_steps over its rows (token order): x = tiles(u) and
@@ -504,8 +539,8 @@ def expert_backward(x, dy, u_rows, dout_rows, g, wg, wu, wd, q):
     Returns (dx [rows, d], dg [rows], (dWg, dWu, dWd))."""
     wg, wu, wd = (np.asarray(w, dtype=np.float64) for w in (wg, wu, wd))
     g = np.asarray(g, dtype=np.float64)
-    a = x @ wg.T
-    b = x @ wu.T
+    a = q.saved(x @ wg.T)
+    b = q.saved(x @ wu.T)
     dh_pre = q.held(dy @ wd)
     sg = 1.0 / (1.0 + np.exp(-a))
     h = a * sg * b
