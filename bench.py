@@ -306,6 +306,33 @@ def main():
                     "tflops_algorithmic": round(fl_alg / (b_ms * 1e-3) / 1e12, 1),
                     "tflops_executed": round(fl_exec / (b_ms * 1e-3) / 1e12, 1),
                     "mfma_peak_frac_executed": round(fl_exec / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS[cfg.dtype], 4)}
+        if cfg.dtype == "bf16":
+            # the saved-input pair: a forward that keeps the SwiGLU inputs [a b], and the backward
+            # reading them instead of recomputing the gate/up product; timed beside moe_forward
+            saved = torch.empty(moe.moe_saved_inputs_size(shape) // 2, dtype=torch.bfloat16, device="cuda")
+            out_t = torch.empty_like(dev["u"])
+            moe.moe_forward_train(shape, dev["u"], weights, idx, gate, out_t, saved, ws, stream)
+            moe.moe_backward_saved(shape, dev["u"], dev["centroids"], weights, idx, gate, saved, dout, du, dcent, wgr,
+                                   ws_b, stream)
+            ev_t = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev_t[0].record(stream)
+            for _ in range(reps):
+                moe.moe_forward(shape, dev["u"], weights, idx, gate, out_t, ws, stream)
+            ev_t[1].record(stream)
+            for _ in range(reps):
+                moe.moe_forward_train(shape, dev["u"], weights, idx, gate, out_t, saved, ws, stream)
+            ev_t[2].record(stream)
+            for _ in range(reps):
+                moe.moe_backward_saved(shape, dev["u"], dev["centroids"], weights, idx, gate, saved, dout, du, dcent,
+                                       wgr, ws_b, stream)
+            ev_t[3].record(stream)
+            torch.cuda.synchronize()
+            f_ms, ft_ms, bs_ms = (ev_t[i].elapsed_time(ev_t[i + 1]) / reps for i in range(3))
+            backward["saved_inputs"] = {
+                "saved_bytes": saved.numel() * 2, "forward_ms": round(f_ms, 3), "forward_train_ms": round(ft_ms, 3),
+                "backward_saved_ms": round(bs_ms, 3),
+                "train_step_ms": round(ft_ms + bs_ms, 3), "train_step_ms_recompute": round(f_ms + b_ms, 3)}
+            del saved, out_t
         del grads, ws_b, du, dout, dcent
         torch.cuda.empty_cache()
 

@@ -203,6 +203,39 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
                         const void* dout, void* du, float* d_centroids, const moe_weight_grads* dw,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Saved-input training pair (BF16 only).  The backward's gate/up step needs the SwiGLU inputs
+ * a = x W_gate^T and b = x W_up^T of every (token, expert) row (方法 §2, the h'_t equation: the
+ * expert FFN is SwiGLU).  moe_backward recomputes them with a second gate/up product; this pair
+ * keeps them from the forward instead, trading [max_rows, 2I] bf16 of device memory for that
+ * product.  The results equal moe_forward / moe_backward up to the rounding of a and b to bf16
+ * before the backward's SwiGLU derivative.
+ *
+ * moe_saved_inputs_size: bytes of the saved buffer for `shape`.  Errors as for
+ * moe_backward_workspace_size, and MOE_ERR_UNSUPPORTED unless dtype is BF16. */
+moe_status moe_saved_inputs_size(const moe_shape* shape, size_t* bytes);
+
+/* moe_forward (same arguments, same workspace, same out) that also writes the SwiGLU inputs
+ * [a b] of every row of the permuted token->expert layout to `saved` (bf16, row r at
+ * saved + r * 2I: a then b; the layout is private to the library and fixed by topk_idx).  The
+ * caller owns `saved` and passes it, unchanged, with the same topk_idx to moe_backward_saved.
+ * Errors: those of moe_forward and moe_backward_workspace_size; MOE_ERR_UNSUPPORTED unless
+ * dtype is BF16; MOE_ERR_INVALID_ARG for a null `saved` (T > 0) or one aliasing u or out;
+ * MOE_ERR_WORKSPACE if saved_bytes < moe_saved_inputs_size. */
+moe_status moe_forward_train(const moe_shape* shape, const void* u, const moe_weights* weights,
+                             const int32_t* topk_idx, const float* topk_gate, void* out, void* saved,
+                             size_t saved_bytes, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_backward (same arguments and outputs, same workspace) reading the SwiGLU inputs that
+ * moe_forward_train saved for the same shape, weights and topk_idx in place of recomputing
+ * them.  Errors: those of moe_backward; MOE_ERR_UNSUPPORTED unless dtype is BF16;
+ * MOE_ERR_INVALID_ARG for a null `saved` or one aliasing du; MOE_ERR_WORKSPACE if
+ * saved_bytes < moe_saved_inputs_size. */
+moe_status moe_backward_saved(const moe_shape* shape, const void* u, const float* centroids,
+                              const moe_weights* weights, const int32_t* topk_idx, const float* topk_gate,
+                              const void* saved, size_t saved_bytes, const void* dout, void* du,
+                              float* d_centroids, const moe_weight_grads* dw, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Auxiliary-loss-free bias update (方法 §2, last paragraph), in place on bias[N_r] (fp32):
  * expert i is overloaded when load_i * N_r > total_assignments (= T * K_r, i.e. above the
  * step mean), underloaded when below; b_i <- b_i - gamma resp. b_i + gamma as one fp32 add;

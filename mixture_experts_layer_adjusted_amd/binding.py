@@ -68,6 +68,11 @@ _SIG = {
     "moe_backward_workspace_size": [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)],
     "moe_backward": [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(Weights), _P, _P, _P, _P, _P,
                      ctypes.POINTER(WeightGrads), _P, ctypes.c_size_t, _P],
+    "moe_saved_inputs_size": [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)],
+    "moe_forward_train": [ctypes.POINTER(Shape), _P, ctypes.POINTER(Weights), _P, _P, _P, _P, ctypes.c_size_t, _P,
+                          ctypes.c_size_t, _P],
+    "moe_backward_saved": [ctypes.POINTER(Shape), _P, _P, ctypes.POINTER(Weights), _P, _P, _P, ctypes.c_size_t, _P,
+                           _P, _P, ctypes.POINTER(WeightGrads), _P, ctypes.c_size_t, _P],
     "moe_status_string": [ctypes.c_int32],
 }
 for _name, _args in _SIG.items():
@@ -132,6 +137,26 @@ def moe_backward(shape, u, centroids, weights, topk_idx, topk_gate, dout, du, d_
         ctypes.byref(shape), _ptr(u), _ptr(centroids), ctypes.byref(weights), _ptr(topk_idx), _ptr(topk_gate),
         _ptr(dout), _ptr(du), _ptr(d_centroids), ctypes.byref(weight_grads), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+
+
+def moe_saved_inputs_size(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_saved_inputs_size", _lib.moe_saved_inputs_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def moe_forward_train(shape, u, weights: Weights, topk_idx, topk_gate, out, saved, workspace, stream=None):
+    _check("moe_forward_train", _lib.moe_forward_train(
+        ctypes.byref(shape), _ptr(u), ctypes.byref(weights), _ptr(topk_idx), _ptr(topk_gate), _ptr(out),
+        _ptr(saved), _nbytes(saved), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def moe_backward_saved(shape, u, centroids, weights, topk_idx, topk_gate, saved, dout, du, d_centroids,
+                       weight_grads, workspace, stream=None):
+    _check("moe_backward_saved", _lib.moe_backward_saved(
+        ctypes.byref(shape), _ptr(u), _ptr(centroids), ctypes.byref(weights), _ptr(topk_idx), _ptr(topk_gate),
+        _ptr(saved), _nbytes(saved), _ptr(dout), _ptr(du), _ptr(d_centroids), ctypes.byref(weight_grads),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def moe_workspace_size(shape: Shape) -> int:

@@ -347,6 +347,84 @@ __global__ void __launch_bounds__(256) transpose_quant_kernel(TransposeQuantArgs
   if (q == 0) a.dst_scale[(int64_t)(c0 + c) * (a.ldd / 128) + j0 / 128] = scale;
 }
 
+// SwiGLU backward from the saved inputs [a b] of the forward (ab [rows, 2I]: a then b, bf16):
+// with dH before the gate (dhu [rows, I]) and dh = row_gate * dH, for every feature
+//   dA = dh b sg (1 + a (1 - sg)),  dB = dh a sg,  H = a sg b   (sg = sigmoid(a)),
+// written to dab ([rows, 2I]: dA then dB) and h ([rows, I]); dg_part[row, n] = sum over the
+// features 128 n + [0, 128) of dH H (16 lanes of 8 features, added pairwise in a fixed order).
+// Padding rows (row_token < 0) are written as zeros.  Only the rows [0, seg_off[n_seg]) the
+// segments use are touched.  Each lane takes kSavedUnroll runs of 8 features per grid step, all
+// loads issued before any arithmetic.
+constexpr int kSavedThreads = 256, kSavedUnroll = 4;
+
+__global__ void __launch_bounds__(kSavedThreads) swiglu_bwd_saved_kernel(
+    const uint16_t* __restrict__ ab, const uint16_t* __restrict__ dhu, const float* __restrict__ row_gate,
+    const int32_t* __restrict__ row_token, const int32_t* __restrict__ seg_end, int I, uint16_t* __restrict__ dab,
+    uint16_t* __restrict__ h, float* __restrict__ dg_part) {
+  const int runs = I / 8;                        // runs of 8 features per row, a multiple of 16
+  const int total = seg_end[0] * runs;           // < 2^27: rows * 2I * 2 bytes < 2^32
+  const int step = gridDim.x * kSavedThreads * kSavedUnroll;
+  for (int base = blockIdx.x * kSavedThreads * kSavedUnroll + threadIdx.x; base < total; base += step) {
+    uint4 qa[kSavedUnroll], qb[kSavedUnroll], qd[kSavedUnroll];
+    float rg[kSavedUnroll];
+    int tok[kSavedUnroll];
+#pragma unroll
+    for (int k = 0; k < kSavedUnroll; ++k) {
+      const int i = base + k * kSavedThreads;
+      if (i < total) {
+        const int r = i / runs, f = (i - r * runs) * 8;
+        qa[k] = *reinterpret_cast<const uint4*>(ab + (int64_t)r * 2 * I + f);
+        qb[k] = *reinterpret_cast<const uint4*>(ab + (int64_t)r * 2 * I + I + f);
+        qd[k] = *reinterpret_cast<const uint4*>(dhu + (int64_t)r * I + f);
+        rg[k] = row_gate[r];
+        tok[k] = row_token[r];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kSavedUnroll; ++k) {
+      const int i = base + k * kSavedThreads;
+      // i < total holds for all 16 lanes of a run group or for none (total and the groups are
+      // multiples of 16), so the shuffles below read only lanes of the same group
+      if (i < total) {
+        const int r = i / runs, f = (i - r * runs) * 8;
+        const uint32_t wa[4] = {qa[k].x, qa[k].y, qa[k].z, qa[k].w};
+        const uint32_t wb[4] = {qb[k].x, qb[k].y, qb[k].z, qb[k].w};
+        const uint32_t wd[4] = {qd[k].x, qd[k].y, qd[k].z, qd[k].w};
+        const bool pad = tok[k] < 0;
+        uint32_t oa[4], ob[4], oh[4];
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float va[2], vb[2], vh[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float a = __uint_as_float(t ? wa[j] & 0xFFFF0000u : wa[j] << 16);
+            const float b = __uint_as_float(t ? wb[j] & 0xFFFF0000u : wb[j] << 16);
+            const float du = __uint_as_float(t ? wd[j] & 0xFFFF0000u : wd[j] << 16);
+            const float sg = 1.0f / (1.0f + __expf(-a));
+            const float dh = rg[k] * du;
+            va[t] = pad ? 0.0f : dh * b * sg * (1.0f + a * (1.0f - sg));
+            vb[t] = pad ? 0.0f : dh * a * sg;
+            vh[t] = pad ? 0.0f : a * sg * b;
+            part += du * vh[t];
+          }
+          oa[j] = (uint32_t)f32_to_bf16(va[0]) | ((uint32_t)f32_to_bf16(va[1]) << 16);
+          ob[j] = (uint32_t)f32_to_bf16(vb[0]) | ((uint32_t)f32_to_bf16(vb[1]) << 16);
+          oh[j] = (uint32_t)f32_to_bf16(vh[0]) | ((uint32_t)f32_to_bf16(vh[1]) << 16);
+        }
+        *reinterpret_cast<uint4*>(dab + (int64_t)r * 2 * I + f) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+        *reinterpret_cast<uint4*>(dab + (int64_t)r * 2 * I + I + f) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+        *reinterpret_cast<uint4*>(h + (int64_t)r * I + f) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+        part += __shfl_xor(part, 1, 64);
+        part += __shfl_xor(part, 2, 64);
+        part += __shfl_xor(part, 4, 64);
+        part += __shfl_xor(part, 8, 64);
+        if ((threadIdx.x & 15) == 0) dg_part[(int64_t)r * (I / 128) + f / 128] = part;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const float* gate, const int32_t* seg_off,
@@ -360,6 +438,19 @@ hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const fl
   if (n > 0)
     hipLaunchKernelGGL(row_gate_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, perm_row, gate, seg_off,
                        s.tokens, s.top_k, s.n_routed, s.n_shared, row_gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd_saved(const void* ab, const void* dhu, const float* row_gate, const int32_t* row_token,
+                                  const int32_t* seg_end, int64_t max_rows, int I, void* dab, void* h, float* dg_part,
+                                  hipStream_t st) {
+  if (I % 128 != 0 || max_rows * 2 * I * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  const int64_t per_block = (int64_t)kSavedThreads * kSavedUnroll;
+  const int64_t blocks = std::min<int64_t>(ceil_div(max_rows * (I / 8), per_block), 2048);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_saved_kernel, dim3((unsigned)blocks), dim3(kSavedThreads), 0, st,
+                     static_cast<const uint16_t*>(ab), static_cast<const uint16_t*>(dhu), row_gate, row_token, seg_end,
+                     I, static_cast<uint16_t*>(dab), static_cast<uint16_t*>(h), dg_part);
   return hipGetLastError();
 }
 

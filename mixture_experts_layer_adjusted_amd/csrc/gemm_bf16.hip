@@ -400,6 +400,47 @@ __device__ __forceinline__ int store_tile_staged_swiglu(const f32x16 (&acc)[4][2
   return rounds;
 }
 
+// The SwiGLU inputs of a 256 x 128 tile, a (gate accumulators) to columns n0 + [0, 128) and b (up)
+// to columns N + n0 + [0, 128) of out (row stride 2N, rows m0 + [0, tile_rows)): two staged passes
+// of 256-byte row spans as in store_tile_staged_swiglu.  The caller has passed lds_barrier() since
+// the stage was last read (the SwiGLU pass before it ends with its row reads).
+__device__ __forceinline__ int store_tile_staged_ab(const f32x16 (&acc)[4][2], uint16_t* stg, uint16_t* out,
+                                                    int64_t m0, int n0, int N, int tile_rows, int wave, int wm,
+                                                    int wn, int lane) {
+  asm volatile("" : "+v"(lane));   // as in store_tile_staged
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int rounds = tile_rows > 128 ? kStagedRounds : kStagedRounds / 2;
+  const int c = lane & 15;
+  const int f = n0 + c * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    lds_barrier();   // the stage's previous rows have been read
+    if (wm * 128 < tile_rows) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int r = wm * 128 + mb * 32 + l32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cc = wn * 4 + q;
+          const f32x16& a = acc[mb][h];
+          *reinterpret_cast<uint64_t*>(stg + r * 128 + ((cc ^ (r & 15)) << 3) + khalf * 4) =
+              pack_bf16x4(a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]);
+        }
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kStagedRounds; ++i) {
+      if (i < rounds) {
+        const int r = (i * 8 + wave) * 4 + (lane >> 4);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * 128 + ((c ^ (r & 15)) << 3));
+        if (f < N) *reinterpret_cast<u32x4*>(out + (m0 + r) * 2 * (int64_t)N + h * N + f) = v;
+      }
+    }
+  }
+  return 2 * rounds;
+}
+
 // SwiGLU backward epilogue of a 256 x 128 tile (a, b = the gate and up accumulators of features
 // n0 + [0, 128), rows m0 + [0, tile_rows)), through an LDS stage no load is filling:
 //   dH before the gate (g.dh, [rows, N]) comes in by direct loads into the stage (256-byte rows
@@ -814,8 +855,8 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
 // them.  Tiles past the last 256-row tile end the walk (their slots only grow).
 template <int EPI, bool WKN>
 __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmOperands g, int NT) {
-  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
-  static_assert(EPI == 0 || EPI == 1 || EPI == 2, "plain store, SwiGLU or SwiGLU backward");
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2 || EPI == 3;
+  static_assert(EPI >= 0 && EPI <= 3, "plain store, SwiGLU, SwiGLU backward or SwiGLU saving its inputs");
   static_assert(!WKN || EPI == 0, "K-major weights: plain store");
   constexpr int BK = 64, TM = 256, WROWS = 256, WAVES = 8, WN = 4, RW = 128, MB = 4, WRW = 64, NBW = 2;
   using C = StreamCfg<BK, WAVES, WROWS, 1, TM>;
@@ -1037,9 +1078,13 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
     if constexpr (EPI == 2)
       stores_behind = store_tile_staged_swiglu_bwd(acc, stg, g, cur.m0, cur.nt * (WROWS / 2), cur.nt, cur.tile_rows,
                                                    wave, wm, wn, lane, red);
-    else if constexpr (SWIGLU)
+    else if constexpr (SWIGLU) {
       stores_behind = store_tile_staged_swiglu(acc, stg, static_cast<uint16_t*>(g.out), cur.m0, cur.nt * (WROWS / 2),
                                                N, cur.tile_rows, wave, wm, wn, lane);
+      if constexpr (EPI == 3)   // and the SwiGLU inputs a, b to out2 ([rows, 2N])
+        stores_behind += store_tile_staged_ab(acc, stg, static_cast<uint16_t*>(g.out2), cur.m0, cur.nt * (WROWS / 2),
+                                              N, cur.tile_rows, wave, wm, wn, lane);
+    }
     else
       stores_behind = store_tile_staged(acc, stg, static_cast<uint16_t*>(g.out), cur.m0, cur.nt * WROWS, N,
                                         cur.tile_rows, wave, wm, wn, lane);
@@ -1368,6 +1413,14 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st) { return launch_bf16<1>(g, st); }
+// SwiGLU that also writes its inputs [a b] of every row to g.out2 ([rows, 2N]); always the
+// persistent 256 x 256 form
+hipError_t launch_gemm_bf16_swiglu_save(const GemmOperands& g, hipStream_t st) {
+  if (g.K % 64 != 0 || g.N % 8 != 0 || !g.out2) return hipErrorInvalidValue;
+  if (g.act_rows * g.K * 2 >= (int64_t(1) << 32) || (int64_t)g.N * g.K * 2 >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
+  return launch_persistent<3, false>(g, st);
+}
 hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st) { return launch_bf16<0>(g, st); }
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_bf16<2>(g, st); }
 hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st) { return launch_wgrad_bf16(g, st); }

@@ -7,6 +7,7 @@
 namespace moe {
 
 hipError_t launch_gemm_bf16_swiglu(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_bf16_swiglu_save(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_f32_swiglu(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_f32_down(const GemmOperands& g, hipStream_t st);
@@ -130,9 +131,10 @@ static moe_status check_shape(const moe_shape* s) {
 
 static moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// saved: null, or (BF16) [max_rows, 2I] bf16 for the gate/up GEMM's SwiGLU inputs [a b]
 static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_weights* w, const int32_t* idx,
                                const float* gate, void* out, void* ws, size_t ws_bytes, hipStream_t st,
-                               hipEvent_t* ev, int32_t n_ev) {
+                               hipEvent_t* ev, int32_t n_ev, void* saved = nullptr) {
   moe_status rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
   const moe_shape& s = *shape;
@@ -195,7 +197,12 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.small_segments = (int64_t)s.tokens * s.top_k < (int64_t)kTileM * s.n_routed;
   g1.out = wsb + p.h;
   g1.out_scale = fp8 ? reinterpret_cast<float*>(wsb + p.h_scale) : nullptr;
-  if ((rc = hip_status(launch_gemm_swiglu(s.dtype, g1, st))) != MOE_OK) return rc;
+  if (saved) {
+    g1.out2 = saved;
+    if ((rc = hip_status(launch_gemm_bf16_swiglu_save(g1, st))) != MOE_OK) return rc;
+  } else if ((rc = hip_status(launch_gemm_swiglu(s.dtype, g1, st))) != MOE_OK) {
+    return rc;
+  }
   if (mark(3) != hipSuccess) return MOE_ERR_HIP;
 
   GemmOperands g2{};
@@ -480,10 +487,38 @@ moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes) {
   return MOE_OK;
 }
 
-moe_status moe_backward(const moe_shape* shape, const void* u, const float* centroids, const moe_weights* w,
-                        const int32_t* topk_idx, const float* topk_gate, const void* dout, void* du,
-                        float* d_centroids, const moe_weight_grads* dw, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+// bytes of the saved SwiGLU inputs [a b] of every permuted row: [max_rows, 2I] bf16
+static size_t saved_bytes_for(const moe_shape& s) {
+  return (size_t)plan_workspace(s).max_rows * 2 * (size_t)s.inter * 2;
+}
+
+moe_status moe_saved_inputs_size(const moe_shape* shape, size_t* bytes) {
+  moe_status rc = check_backward_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = saved_bytes_for(*shape);
+  return MOE_OK;
+}
+
+moe_status moe_forward_train(const moe_shape* shape, const void* u, const moe_weights* weights,
+                             const int32_t* topk_idx, const float* topk_gate, void* out, void* saved,
+                             size_t saved_bytes, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status rc = check_backward_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (shape->tokens == 0) return MOE_OK;
+  if (!saved) return MOE_ERR_INVALID_ARG;
+  if (saved_bytes < saved_bytes_for(*shape)) return MOE_ERR_WORKSPACE;
+  if (saved == u || saved == out) return MOE_ERR_INVALID_ARG;
+  return forward_impl(shape, u, weights, topk_idx, topk_gate, out, workspace, workspace_bytes, stream, nullptr, 0,
+                      saved);
+}
+
+static moe_status backward_impl(const moe_shape* shape, const void* u, const float* centroids, const moe_weights* w,
+                                const int32_t* topk_idx, const float* topk_gate, const void* dout, void* du,
+                                float* d_centroids, const moe_weight_grads* dw, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, const void* saved) {
   moe_status rc = check_backward_shape(shape);
   if (rc != MOE_OK) return rc;
   const moe_shape& s = *shape;
@@ -584,17 +619,24 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
     GemmOperands g1 = grouped(dout, row_token, T, bf(w->w_down), bf(w->sh_down), (int)d, (int)I, dhu);
     g1.kn_split = (int)d;
     if ((rc = hip_status(launch_gemm_bf16_dgrad(g1, stream))) != MOE_OK) return rc;
-    // gate/up recomputed: [dA dB], H and the gate-gradient partials
-    GemmOperands g2 = grouped(u, row_token, T, nullptr, nullptr, (int)d, (int)I, dab);
-    g2.w_routed[0] = w->w_gate;
-    g2.w_routed[1] = w->w_up;
-    g2.w_shared[0] = w->sh_gate;
-    g2.w_shared[1] = w->sh_up;
-    g2.dh = dhu;
-    g2.row_gate = row_gate;
-    g2.out2 = hb;
-    g2.dg_part = dg_part;
-    if ((rc = hip_status(launch_gemm_bf16_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
+    if (saved) {
+      // [dA dB], H and the gate-gradient partials from the forward's saved [a b]
+      if ((rc = hip_status(launch_swiglu_bwd_saved(saved, dhu, row_gate, row_token, seg_off + Nr + Ns, P, (int)I, dab,
+                                                   hb, dg_part, stream))) != MOE_OK)
+        return rc;
+    } else {
+      // gate/up recomputed: [dA dB], H and the gate-gradient partials
+      GemmOperands g2 = grouped(u, row_token, T, nullptr, nullptr, (int)d, (int)I, dab);
+      g2.w_routed[0] = w->w_gate;
+      g2.w_routed[1] = w->w_up;
+      g2.w_shared[0] = w->sh_gate;
+      g2.w_shared[1] = w->sh_up;
+      g2.dh = dhu;
+      g2.row_gate = row_gate;
+      g2.out2 = hb;
+      g2.dg_part = dg_part;
+      if ((rc = hip_status(launch_gemm_bf16_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
+    }
     // dX = [dA dB] [W_gate; W_up]: K rows [0, I) from W_gate [I][d], [I, 2I) from W_up, as stored
     GemmOperands g3 = grouped(dab, nullptr, P, bf(w->w_gate), bf(w->sh_gate), (int)(2 * I), (int)d, dx);
     g3.w_routed[1] = w->w_up;
@@ -619,6 +661,28 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
   if ((rc = wgrad(dab_t + I * P, (int)I, x_t, (int)d, dw->w_up, dw->sh_up)) != MOE_OK) return rc;
   return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, tile_seg, p.max_tiles, dc_part,
                                      d_centroids, stream));
+}
+
+moe_status moe_backward(const moe_shape* shape, const void* u, const float* centroids, const moe_weights* w,
+                        const int32_t* topk_idx, const float* topk_gate, const void* dout, void* du,
+                        float* d_centroids, const moe_weight_grads* dw, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return backward_impl(shape, u, centroids, w, topk_idx, topk_gate, dout, du, d_centroids, dw, workspace,
+                       workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_backward_saved(const moe_shape* shape, const void* u, const float* centroids, const moe_weights* w,
+                              const int32_t* topk_idx, const float* topk_gate, const void* saved, size_t saved_bytes,
+                              const void* dout, void* du, float* d_centroids, const moe_weight_grads* dw,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status rc = check_backward_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!saved) return MOE_ERR_INVALID_ARG;
+  if (saved_bytes < saved_bytes_for(*shape)) return MOE_ERR_WORKSPACE;
+  if (saved == du) return MOE_ERR_INVALID_ARG;
+  return backward_impl(shape, u, centroids, w, topk_idx, topk_gate, dout, du, d_centroids, dw, workspace,
+                       workspace_bytes, stream, saved);
 }
 
 moe_status moe_update_bias(int32_t n_routed, int64_t total_assignments, const int32_t* expert_load, float* bias,

@@ -179,6 +179,11 @@ hipError_t launch_row_gate(const moe_shape& s, const int32_t* perm_row, const fl
 hipError_t launch_router_bwd(const moe_shape& s, const void* u, const float* centroids, const int32_t* idx,
                              const int32_t* perm_row, const float* dg_part, const int32_t* seg_off, const void* dout,
                              const void* dX, void* du, float* row_dz, hipStream_t st);
+// SwiGLU backward from saved inputs: ab [rows, 2I] (a then b), dhu [rows, I] -> dab [rows, 2I],
+// h [rows, I], dg_part [rows, I / 128], for the rows [0, *seg_end) (padding rows: zeros)
+hipError_t launch_swiglu_bwd_saved(const void* ab, const void* dhu, const float* row_gate, const int32_t* row_token,
+                                  const int32_t* seg_end, int64_t max_rows, int I, void* dab, void* h, float* dg_part,
+                                  hipStream_t st);
 // part: fp32 [max_tiles, d] per-tile partial sums
 hipError_t launch_dcentroid(const moe_shape& s, const void* u, const int32_t* row_token, const float* row_dz,
                             const int32_t* seg_off, const int32_t* tile_seg, int64_t max_tiles, float* part, float* de,

@@ -146,3 +146,46 @@ def test_single_hip_runtime_in_process():
     hip = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     hsa = {ln.split()[-1] for ln in maps if "libhsa-runtime64" in ln}
     assert len(hip) == 1 and len(hsa) <= 1, (hip, hsa)
+
+
+def test_saved_input_pair_errors_before_launch():
+    """moe_saved_inputs_size / moe_forward_train / moe_backward_saved: BF16 only, the saved buffer's
+    size, null and aliasing checks come before any launch."""
+    lib = binding.raw_lib()
+    fake = ctypes.c_void_p(0x1000)
+    big = ctypes.c_size_t(1 << 40)
+    n = ctypes.c_size_t(0)
+    sb = moe.make_shape(300, 256, 16, 4, 1, 128, moe.MOE_DTYPE_BF16)
+    assert lib.moe_saved_inputs_size(ctypes.byref(sb), ctypes.byref(n)) == 0
+    # [max_rows, 2I] bf16, max_rows = 128 * ((T K + N (128 - 1)) / 128 + N_s ceil(T / 128))
+    max_rows = 128 * ((300 * 4 + 16 * 127) // 128 + 1 * ((300 + 127) // 128))
+    assert n.value == max_rows * 2 * 128 * 2
+    for dt in (moe.MOE_DTYPE_F32, moe.MOE_DTYPE_FP8_B128):
+        s = moe.make_shape(300, 256, 16, 4, 1, 128, dt)
+        assert lib.moe_saved_inputs_size(ctypes.byref(s), ctypes.byref(n)) == 2, dt
+    assert lib.moe_saved_inputs_size(ctypes.byref(moe.make_shape(300, 256, 16, 4, 1, 192, moe.MOE_DTYPE_BF16)),
+                                     ctypes.byref(n)) == 2                                   # I % 128
+    assert lib.moe_saved_inputs_size(ctypes.byref(sb), None) == 1
+    w = moe.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    out = ctypes.c_void_p(0x2000)
+    saved = ctypes.c_void_p(0x3000)
+    fwd = lambda shape, sv, sbytes, ws_bytes: lib.moe_forward_train(  # noqa: E731
+        ctypes.byref(shape), fake, ctypes.byref(w), fake, fake, out, sv, sbytes, fake, ws_bytes, None)
+    assert fwd(sb, None, big, big) == 1                                                     # null saved
+    assert fwd(sb, saved, 16, big) == 3                                                     # saved too small
+    assert fwd(sb, fake, big, big) == 1                                                     # saved == u
+    assert fwd(sb, saved, big, 16) == 3                                                     # workspace too small
+    s8 = moe.make_shape(300, 256, 16, 4, 1, 128, moe.MOE_DTYPE_FP8_B128)
+    assert fwd(s8, saved, big, big) == 2
+    assert fwd(moe.make_shape(0, 256, 16, 4, 1, 128, moe.MOE_DTYPE_BF16), None, 0, 0) == 0   # no tokens: no-op
+    wg = moe.WeightGrads(0x4000, 0x4000, 0x4000, 0x4000, 0x4000, 0x4000)
+    du = ctypes.c_void_p(0x5000)
+    bwd = lambda shape, sv, sbytes, du_, ws_bytes: lib.moe_backward_saved(  # noqa: E731
+        ctypes.byref(shape), fake, fake, ctypes.byref(w), fake, fake, sv, sbytes, out, du_, fake, ctypes.byref(wg),
+        fake, ws_bytes, None)
+    assert bwd(sb, None, big, du, big) == 1                                                  # null saved
+    assert bwd(sb, saved, 16, du, big) == 3                                                  # saved too small
+    assert bwd(sb, saved, big, saved, big) == 1                                              # du == saved
+    assert bwd(sb, saved, big, du, 16) == 3                                                  # workspace too small
+    assert bwd(sb, saved, big, fake, big) == 1                                               # du == u
+    assert bwd(s8, saved, big, du, big) == 2
