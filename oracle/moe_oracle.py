@@ -71,7 +71,8 @@ R16 FP8 backward (the page's FP8 paragraph names the forward GEMM and both backw
 R17 bf16 backward storage (the page fixes no precision for the bf16 path): R16's steps with
     no quantiser, the tensors held between steps (dH, H, dA, dB) rounded to bf16 and
     gate * dout rounded once to bf16 from its fp32 product; the saved-input variant also
-    holds the SwiGLU inputs a and b in bf16 from the forward.  Outputs whose condition
+    holds the SwiGLU inputs a and b in bf16 from the forward (for the FP8 backward of R16
+    too: a and b then come from the FP8 forward product and are rounded to bf16).  Outputs whose condition
     number magnifies these roundings past the bf16 tolerance (the centroid gradient of an
     expert picked by one or two tokens, where the two terms of ds nearly cancel) are checked
     against this model; every other output against R14 itself.  Pinned by its reduction to
@@ -533,6 +534,12 @@ class Bf16SavedPolicy(Bf16Policy):
     saved = staticmethod(bf16_round)
 
 
+class Fp8SavedPolicy(Fp8Policy):
+    """R16 with a and b held in bf16 from the forward (the saved-input variant of R17)."""
+
+    saved = staticmethod(bf16_round)
+
+
 def expert_backward(x, dy, u_rows, dout_rows, g, wg, wu, wd, q):
     """One expert's part of layer_backward_steps over its rows (token order): x = tiles(u) and
     dy = tiles(dout) of those rows, their held u and dout, and their gates g.
@@ -604,9 +611,10 @@ def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
     return du, de, d_routed, d_shared
 
 
-def layer_backward_fp8(u, centroids, idx, routed_q, shared_q, dout):
+def layer_backward_fp8(u, centroids, idx, routed_q, shared_q, dout, saved=False):
     """FP8 backward of R16.  routed_q(e) / shared_q entries are ((codes, scale) x 3) from
-    quantize_weight_128x128 of (w_gate, w_up, w_down); u and dout as held (bf16 values)."""
+    quantize_weight_128x128 of (w_gate, w_up, w_down); u and dout as held (bf16 values).
+    saved: a and b held in bf16 from the forward (R17's saved-input variant)."""
     deq = lambda ws: tuple(dequant_weight(*w) for w in ws)  # noqa: E731
     return layer_backward_steps(u, centroids, idx, lambda ex: deq(routed_q(ex)), [deq(w) for w in shared_q], dout,
-                                Fp8Policy)
+                                Fp8SavedPolicy if saved else Fp8Policy)

@@ -6,7 +6,9 @@ variant, a and b held in bf16 from the forward.  Pinned by
 * its rounding functions: bf16 storage and the once-rounded gate * dout against torch;
 * the saved-input variant equalling the plain one bit for bit where a and b are bf16 values
   (small integers), and differing from it where they are not;
-* the distance to the exact R14 backward that bf16 allows, on the well-conditioned outputs.
+* the distance to the exact R14 backward that bf16 allows, on the well-conditioned outputs;
+* the FP8 saved-input variant: R16's quantisers with a and b rounded to bf16, differing from the
+  plain FP8 backward by no more than that rounding moves the E4M3 codes.
 """
 import numpy as np
 import torch
@@ -97,3 +99,25 @@ def test_bf16_storage_within_bf16_of_the_exact_backward():
             # a few bf16 roundings (relative 2^-9 each) on the path to every output
             assert err < 1.5e-2, (policy.__name__, k, err)
             assert err > 0, (policy.__name__, k)
+
+
+def test_fp8_saved_variant_is_r16_with_bf16_a_and_b():
+    assert O.Fp8SavedPolicy.tiles is O.Fp8Policy.tiles and O.Fp8SavedPolicy.runs is O.Fp8Policy.runs
+    assert O.Fp8SavedPolicy.held is O.Fp8Policy.held and O.Fp8SavedPolicy.scaled is O.Fp8Policy.scaled
+    x = np.random.default_rng(4).standard_normal((7, 19)) * 30.0
+    assert np.array_equal(O.Fp8SavedPolicy.saved(x), O.bf16_round(x))
+    assert np.array_equal(O.Fp8Policy.saved(x), x)
+    L = _layer(np.random.default_rng(5), T=160, d=256, N=4, K=2, I=128, Ns=1, integer=False)
+    q = lambda w: tuple(O.quantize_weight_128x128(m) for m in w)  # noqa: E731
+    rq = lambda ex: q((L["wg"][ex], L["wu"][ex], L["wd"][ex]))  # noqa: E731
+    shq = [q(w) for w in L["sh"]]
+    plain = _flat(O.layer_backward_fp8(L["u"], L["e"], L["idx"], rq, shq, L["dout"]))
+    saved = _flat(O.layer_backward_fp8(L["u"], L["e"], L["idx"], rq, shq, L["dout"], saved=True))
+    assert not np.array_equal(plain["wg0"], saved["wg0"])
+    for k in plain:
+        if k == "de":
+            continue
+        ref = plain[k] - (L["dout"] if k == "du" else 0)
+        got = saved[k] - (L["dout"] if k == "du" else 0)
+        # bf16 a, b move some E4M3 codes of dA, dB by one step (1/16 at most): Frobenius small
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 2e-2, k
