@@ -306,7 +306,7 @@ def main():
                     "tflops_algorithmic": round(fl_alg / (b_ms * 1e-3) / 1e12, 1),
                     "tflops_executed": round(fl_exec / (b_ms * 1e-3) / 1e12, 1),
                     "mfma_peak_frac_executed": round(fl_exec / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS[cfg.dtype], 4)}
-        if cfg.dtype == "bf16":
+        if cfg.dtype in ("bf16", "fp8"):
             # the saved-input pair: a forward that keeps the SwiGLU inputs [a b], and the backward
             # reading them instead of recomputing the gate/up product; timed beside moe_forward
             saved = torch.empty(moe.moe_saved_inputs_size(shape) // 2, dtype=torch.bfloat16, device="cuda")

@@ -203,23 +203,24 @@ moe_status moe_backward(const moe_shape* shape, const void* u, const float* cent
                         const void* dout, void* du, float* d_centroids, const moe_weight_grads* dw,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Saved-input training pair (BF16 only).  The backward's gate/up step needs the SwiGLU inputs
+/* Saved-input training pair (BF16 and FP8_B128).  The backward's gate/up step needs the SwiGLU inputs
  * a = x W_gate^T and b = x W_up^T of every (token, expert) row (方法 §2, the h'_t equation: the
  * expert FFN is SwiGLU).  moe_backward recomputes them with a second gate/up product; this pair
  * keeps them from the forward instead, trading [max_rows, 2I] bf16 of device memory for that
  * product.  The results equal moe_forward / moe_backward up to the rounding of a and b to bf16
- * before the backward's SwiGLU derivative.
+ * before the backward's SwiGLU derivative (FP8_B128: a and b of the FP8 forward product, kept
+ * in bf16; the backward's other FP8 products are unchanged).
  *
- * moe_saved_inputs_size: bytes of the saved buffer for `shape`.  Errors as for
- * moe_backward_workspace_size, and MOE_ERR_UNSUPPORTED unless dtype is BF16. */
+ * moe_saved_inputs_size: bytes of the saved buffer for `shape` (bf16 [max_rows, 2I] for both
+ * dtypes).  Errors as for moe_backward_workspace_size. */
 moe_status moe_saved_inputs_size(const moe_shape* shape, size_t* bytes);
 
 /* moe_forward (same arguments, same workspace, same out) that also writes the SwiGLU inputs
  * [a b] of every row of the permuted token->expert layout to `saved` (bf16, row r at
  * saved + r * 2I: a then b; the layout is private to the library and fixed by topk_idx).  The
  * caller owns `saved` and passes it, unchanged, with the same topk_idx to moe_backward_saved.
- * Errors: those of moe_forward and moe_backward_workspace_size; MOE_ERR_UNSUPPORTED unless
- * dtype is BF16; MOE_ERR_INVALID_ARG for a null `saved` (T > 0) or one aliasing u or out;
+ * Errors: those of moe_forward and moe_backward_workspace_size (so MOE_ERR_UNSUPPORTED for
+ * F32); MOE_ERR_INVALID_ARG for a null `saved` (T > 0) or one aliasing u or out;
  * MOE_ERR_WORKSPACE if saved_bytes < moe_saved_inputs_size. */
 moe_status moe_forward_train(const moe_shape* shape, const void* u, const moe_weights* weights,
                              const int32_t* topk_idx, const float* topk_gate, void* out, void* saved,
@@ -227,8 +228,7 @@ moe_status moe_forward_train(const moe_shape* shape, const void* u, const moe_we
 
 /* moe_backward (same arguments and outputs, same workspace) reading the SwiGLU inputs that
  * moe_forward_train saved for the same shape, weights and topk_idx in place of recomputing
- * them.  Errors: those of moe_backward; MOE_ERR_UNSUPPORTED unless dtype is BF16;
- * MOE_ERR_INVALID_ARG for a null `saved` or one aliasing du; MOE_ERR_WORKSPACE if
+ * them.  Errors: those of moe_backward; MOE_ERR_INVALID_ARG for a null `saved` or one aliasing du; MOE_ERR_WORKSPACE if
  * saved_bytes < moe_saved_inputs_size. */
 moe_status moe_backward_saved(const moe_shape* shape, const void* u, const float* centroids,
                               const moe_weights* weights, const int32_t* topk_idx, const float* topk_gate,

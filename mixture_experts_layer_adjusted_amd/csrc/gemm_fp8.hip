@@ -164,7 +164,7 @@ __device__ __forceinline__ int store_tile_staged16(const f32x4 (&acc)[kMB][kNB],
 // through transposing LDS reads, for the input-gradient products of the backward
 template <int EPI, bool WKN = false>
 __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands g, int NT) {
-  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2 || EPI == 3;
   static_assert(!WKN || EPI == 0, "K-major weights: plain store");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ float row_red[kTM][4];   // per-row reductions across the four wavefronts of a row
@@ -416,11 +416,28 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     __syncthreads();
     for (int row = tid; row < tile_rows; row += kThreads)
       g.dg_part[(m0 + row) * (N / kBK) + nt] = row_red[row][0] + row_red[row][1] + row_red[row][2] + row_red[row][3];
-  } else if constexpr (EPI == 1) {
+  } else if constexpr (EPI == 1 || EPI == 3) {
     uint8_t* out = static_cast<uint8_t*>(g.out);
     const int IB = N / kBK;
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
+      if constexpr (EPI == 3) {
+        // the SwiGLU inputs a (gate) and b (up) of the row, bf16, to out2 ([rows, 2N]: a then b)
+        if (active) {
+          uint16_t* ab = static_cast<uint16_t*>(g.out2) + (m0 + mrow0 + mb * 16 + l16) * 2 * N;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int f = n0 + wn * 32 + nb * 16 + kq * 4;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const f32x4& v = acc[mb][nb + 2 * h];
+              *reinterpret_cast<uint2*>(ab + h * N + f) =
+                  make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                             (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+            }
+          }
+        }
+      }
       float amax = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
@@ -706,7 +723,8 @@ hipError_t launch_wgrad_fp8(const GemmOperands& g, hipStream_t st) {
 
 template <int EPI, bool WKN = false>
 hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
-  constexpr bool SWIGLU = EPI == 1 || EPI == 2;
+  constexpr bool SWIGLU = EPI == 1 || EPI == 2 || EPI == 3;
+  if (EPI == 3 && !g.out2) return hipErrorInvalidValue;
   if (WKN && (g.kn_split % kBK != 0 || g.kn_split <= 0 || g.kn_split > g.K)) return hipErrorInvalidValue;
   if (g.K % kBK != 0 || g.N % kBK != 0) return hipErrorInvalidValue;
   // 32-bit byte offsets address the activation matrix and one expert's weight matrix
@@ -731,6 +749,8 @@ hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st) { return launch_fp8<1>(g, st); }
+// SwiGLU with H quantised, also writing the inputs [a b] of every row to g.out2 ([rows, 2N] bf16)
+hipError_t launch_gemm_fp8_swiglu_save(const GemmOperands& g, hipStream_t st) { return launch_fp8<3>(g, st); }
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st) { return launch_fp8<0>(g, st); }
 hipError_t launch_gemm_fp8_swiglu_bwd(const GemmOperands& g, hipStream_t st) { return launch_fp8<2>(g, st); }
 hipError_t launch_gemm_fp8_wgrad(const GemmOperands& g, hipStream_t st) { return launch_wgrad_fp8(g, st); }

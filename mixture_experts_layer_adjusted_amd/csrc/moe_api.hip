@@ -12,6 +12,7 @@ hipError_t launch_gemm_bf16_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_f32_swiglu(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_f32_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_swiglu(const GemmOperands& g, hipStream_t st);
+hipError_t launch_gemm_fp8_swiglu_save(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_fp8_down(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_swiglu_bwd(const GemmOperands& g, hipStream_t st);
 hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st);
@@ -131,7 +132,7 @@ static moe_status check_shape(const moe_shape* s) {
 
 static moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// saved: null, or (BF16) [max_rows, 2I] bf16 for the gate/up GEMM's SwiGLU inputs [a b]
+// saved: null, or (BF16, FP8_B128) [max_rows, 2I] bf16 for the gate/up GEMM's SwiGLU inputs [a b]
 static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_weights* w, const int32_t* idx,
                                const float* gate, void* out, void* ws, size_t ws_bytes, hipStream_t st,
                                hipEvent_t* ev, int32_t n_ev, void* saved = nullptr) {
@@ -199,7 +200,8 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.out_scale = fp8 ? reinterpret_cast<float*>(wsb + p.h_scale) : nullptr;
   if (saved) {
     g1.out2 = saved;
-    if ((rc = hip_status(launch_gemm_bf16_swiglu_save(g1, st))) != MOE_OK) return rc;
+    if ((rc = hip_status(fp8 ? launch_gemm_fp8_swiglu_save(g1, st) : launch_gemm_bf16_swiglu_save(g1, st))) != MOE_OK)
+      return rc;
   } else if ((rc = hip_status(launch_gemm_swiglu(s.dtype, g1, st))) != MOE_OK) {
     return rc;
   }
@@ -324,7 +326,8 @@ moe_status moe_forward_profiled(const moe_shape* shape, const void* u, const moe
 // of each segment.  Runs after the permutation and the row gates; ends with du (router_bwd).
 static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char* wsb, const void* u,
                                const float* centroids, const moe_weights* w, const int32_t* topk_idx,
-                               const void* dout, void* du, const moe_weight_grads* dw, hipStream_t stream) {
+                               const void* dout, void* du, const moe_weight_grads* dw, hipStream_t stream,
+                               const void* saved) {
   moe_status rc;
   const int64_t T = s.tokens, d = s.hidden, I = s.inter, Nr = s.n_routed, Ns = s.n_shared, P = p.max_rows;
   const int64_t p8 = P / 128;
@@ -376,7 +379,7 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
   };
   if (T > 0) {
     // E4M3 copies of u and dout (1 x 128 tiles along d)
-    if ((rc = hip_status(launch_quantize_act(T, (int)d, u, u_q, u_s, stream))) != MOE_OK) return rc;
+    if (!saved && (rc = hip_status(launch_quantize_act(T, (int)d, u, u_q, u_s, stream))) != MOE_OK) return rc;
     if ((rc = hip_status(launch_quantize_act(T, (int)d, dout, dout_q, dout_s, stream))) != MOE_OK) return rc;
     GemmOperands g{};
     g.tile_seg = reinterpret_cast<const int32_t*>(at(p.tile_seg));
@@ -402,28 +405,35 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
     g1.kn_split = (int)d;
     g1.out = dhu;
     if ((rc = hip_status(launch_gemm_fp8_dgrad(g1, stream))) != MOE_OK) return rc;
-    // gate/up recomputed from the quantised u: [dA dB], H and the gate-gradient partials
-    GemmOperands g2 = g;
-    g2.act = u_q;
-    g2.act_scale = u_s;
-    g2.row_token = row_token;
-    g2.act_rows = T;
-    g2.w_routed[0] = w->w_gate;
-    g2.w_routed[1] = w->w_up;
-    g2.w_shared[0] = w->sh_gate;
-    g2.w_shared[1] = w->sh_up;
-    g2.s_routed[0] = w->w_gate_scale;
-    g2.s_routed[1] = w->w_up_scale;
-    g2.s_shared[0] = w->sh_gate_scale;
-    g2.s_shared[1] = w->sh_up_scale;
-    g2.K = (int)d;
-    g2.N = (int)I;
-    g2.dh = dhu;
-    g2.row_gate = row_gate;
-    g2.out = dab;
-    g2.out2 = hb;
-    g2.dg_part = dg_part;
-    if ((rc = hip_status(launch_gemm_fp8_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
+    if (saved) {
+      // [dA dB], H and the gate-gradient partials from the forward's saved [a b]
+      if ((rc = hip_status(launch_swiglu_bwd_saved(saved, dhu, row_gate, row_token, seg_off + Nr + Ns, P, (int)I, dab,
+                                                   hb, dg_part, stream))) != MOE_OK)
+        return rc;
+    } else {
+      // gate/up recomputed from the quantised u: [dA dB], H and the gate-gradient partials
+      GemmOperands g2 = g;
+      g2.act = u_q;
+      g2.act_scale = u_s;
+      g2.row_token = row_token;
+      g2.act_rows = T;
+      g2.w_routed[0] = w->w_gate;
+      g2.w_routed[1] = w->w_up;
+      g2.w_shared[0] = w->sh_gate;
+      g2.w_shared[1] = w->sh_up;
+      g2.s_routed[0] = w->w_gate_scale;
+      g2.s_routed[1] = w->w_up_scale;
+      g2.s_shared[0] = w->sh_gate_scale;
+      g2.s_shared[1] = w->sh_up_scale;
+      g2.K = (int)d;
+      g2.N = (int)I;
+      g2.dh = dhu;
+      g2.row_gate = row_gate;
+      g2.out = dab;
+      g2.out2 = hb;
+      g2.dg_part = dg_part;
+      if ((rc = hip_status(launch_gemm_fp8_swiglu_bwd(g2, stream))) != MOE_OK) return rc;
+    }
     // dX = [dA dB] [W_gate; W_up], [dA dB] in 1 x 128 tiles along 2I
     if ((rc = hip_status(launch_quantize_act(P, (int)(2 * I), dab, dab_q, dab_s, stream))) != MOE_OK) return rc;
     // K rows [0, I) from the W_gate codes [I][d], [I, 2I) from W_up, as stored
@@ -495,7 +505,6 @@ static size_t saved_bytes_for(const moe_shape& s) {
 moe_status moe_saved_inputs_size(const moe_shape* shape, size_t* bytes) {
   moe_status rc = check_backward_shape(shape);
   if (rc != MOE_OK) return rc;
-  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!bytes) return MOE_ERR_INVALID_ARG;
   *bytes = saved_bytes_for(*shape);
   return MOE_OK;
@@ -506,7 +515,6 @@ moe_status moe_forward_train(const moe_shape* shape, const void* u, const moe_we
                              size_t saved_bytes, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status rc = check_backward_shape(shape);
   if (rc != MOE_OK) return rc;
-  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (shape->tokens == 0) return MOE_OK;
   if (!saved) return MOE_ERR_INVALID_ARG;
   if (saved_bytes < saved_bytes_for(*shape)) return MOE_ERR_WORKSPACE;
@@ -560,7 +568,7 @@ static moe_status backward_impl(const moe_shape* shape, const void* u, const flo
       MOE_OK)
     return rc;
   if (fp8) {
-    if ((rc = fp8_backward(s, p, wsb, u, centroids, w, topk_idx, dout, du, dw, stream)) != MOE_OK) return rc;
+    if ((rc = fp8_backward(s, p, wsb, u, centroids, w, topk_idx, dout, du, dw, stream, saved)) != MOE_OK) return rc;
     return hip_status(launch_dcentroid(s, u, row_token, row_dz, seg_off, tile_seg, p.max_tiles, dc_part,
                                        d_centroids, stream));
   }
@@ -677,7 +685,6 @@ moe_status moe_backward_saved(const moe_shape* shape, const void* u, const float
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   moe_status rc = check_backward_shape(shape);
   if (rc != MOE_OK) return rc;
-  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!saved) return MOE_ERR_INVALID_ARG;
   if (saved_bytes < saved_bytes_for(*shape)) return MOE_ERR_WORKSPACE;
   if (saved == du) return MOE_ERR_INVALID_ARG;

@@ -149,8 +149,8 @@ def test_single_hip_runtime_in_process():
 
 
 def test_saved_input_pair_errors_before_launch():
-    """moe_saved_inputs_size / moe_forward_train / moe_backward_saved: BF16 only, the saved buffer's
-    size, null and aliasing checks come before any launch."""
+    """moe_saved_inputs_size / moe_forward_train / moe_backward_saved: BF16 and FP8_B128, the saved
+    buffer's size, null and aliasing checks come before any launch."""
     lib = binding.raw_lib()
     fake = ctypes.c_void_p(0x1000)
     big = ctypes.c_size_t(1 << 40)
@@ -160,9 +160,11 @@ def test_saved_input_pair_errors_before_launch():
     # [max_rows, 2I] bf16, max_rows = 128 * ((T K + N (128 - 1)) / 128 + N_s ceil(T / 128))
     max_rows = 128 * ((300 * 4 + 16 * 127) // 128 + 1 * ((300 + 127) // 128))
     assert n.value == max_rows * 2 * 128 * 2
-    for dt in (moe.MOE_DTYPE_F32, moe.MOE_DTYPE_FP8_B128):
-        s = moe.make_shape(300, 256, 16, 4, 1, 128, dt)
-        assert lib.moe_saved_inputs_size(ctypes.byref(s), ctypes.byref(n)) == 2, dt
+    s32 = moe.make_shape(300, 256, 16, 4, 1, 128, moe.MOE_DTYPE_F32)
+    assert lib.moe_saved_inputs_size(ctypes.byref(s32), ctypes.byref(n)) == 2
+    n8 = ctypes.c_size_t(0)
+    s8 = moe.make_shape(300, 256, 16, 4, 1, 128, moe.MOE_DTYPE_FP8_B128)
+    assert lib.moe_saved_inputs_size(ctypes.byref(s8), ctypes.byref(n8)) == 0 and n8.value == max_rows * 2 * 128 * 2
     assert lib.moe_saved_inputs_size(ctypes.byref(moe.make_shape(300, 256, 16, 4, 1, 192, moe.MOE_DTYPE_BF16)),
                                      ctypes.byref(n)) == 2                                   # I % 128
     assert lib.moe_saved_inputs_size(ctypes.byref(sb), None) == 1
@@ -175,8 +177,8 @@ def test_saved_input_pair_errors_before_launch():
     assert fwd(sb, saved, 16, big) == 3                                                     # saved too small
     assert fwd(sb, fake, big, big) == 1                                                     # saved == u
     assert fwd(sb, saved, big, 16) == 3                                                     # workspace too small
-    s8 = moe.make_shape(300, 256, 16, 4, 1, 128, moe.MOE_DTYPE_FP8_B128)
-    assert fwd(s8, saved, big, big) == 2
+    assert fwd(s32, saved, big, big) == 2
+    assert fwd(s8, saved, big, big) == 1                                                     # no weight scales
     assert fwd(moe.make_shape(0, 256, 16, 4, 1, 128, moe.MOE_DTYPE_BF16), None, 0, 0) == 0   # no tokens: no-op
     wg = moe.WeightGrads(0x4000, 0x4000, 0x4000, 0x4000, 0x4000, 0x4000)
     du = ctypes.c_void_p(0x5000)
@@ -188,4 +190,5 @@ def test_saved_input_pair_errors_before_launch():
     assert bwd(sb, saved, big, saved, big) == 1                                              # du == saved
     assert bwd(sb, saved, big, du, 16) == 3                                                  # workspace too small
     assert bwd(sb, saved, big, fake, big) == 1                                               # du == u
-    assert bwd(s8, saved, big, du, big) == 2
+    assert bwd(s32, saved, big, du, big) == 2
+    assert bwd(s8, saved, big, du, big) == 1                                                 # no weight scales

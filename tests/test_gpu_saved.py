@@ -10,7 +10,9 @@ the backward reads them in place of a second gate/up product.  Checked here:
   segment starting on a multiple of 128 rows);
 * the gradients against the oracle's float64 backward, to the bf16 backward tolerance, and close
   to moe_backward's (the two differ only in rounding a and b to bf16);
-* padding and unused rows of the saved buffer and the workspace never reach a gradient.
+* padding and unused rows of the saved buffer and the workspace never reach a gradient;
+* FP8_B128: the same pair on E4M3 weights, against the oracle's FP8 backward with a and b held
+  in bf16 (reading R17 on R16), to the FP8 backward's Frobenius / max-abs bar.
 """
 from __future__ import annotations
 
@@ -29,10 +31,11 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from helpers import Runner, to_host_f32
     from test_gpu_backward import BWD_TOL, _dout, _f, _grads_like, _rel, _row_rel
+    from test_gpu_backward_fp8 import _check, _fro, _setup, _weights_q
 
 
-def _small(name, T, d, N, K, Ns, I, cid):
-    return LayerConfig(cid, name, T, d, N, K, Ns, I, "bf16", "uniform0.01")
+def _small(name, T, d, N, K, Ns, I, cid, dtype="bf16"):
+    return LayerConfig(cid, name, T, d, N, K, Ns, I, dtype, "uniform0.01")
 
 
 def _saved_buffer(shape, fill=None):
@@ -173,15 +176,19 @@ def test_backward_saved_parity(cfg):
         assert v <= BWD_TOL, (k, v)
 
 
-def test_backward_saved_ignores_poisoned_padding():
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_backward_saved_ignores_poisoned_padding(dtype):
     """Saved buffer and workspace filled with NaN / arbitrary bytes before the calls give the
     same, finite gradients as zero-filled ones: padding rows and rows past the last segment are
     never read into a gradient."""
-    cfg = _small("saved-poison", 77, 384, 8, 3, 1, 384, cid=84)
+    cfg = _small("saved-poison", 77, 384, 8, 3, 1, 384, cid=84, dtype=dtype)
     h = host.make_host_inputs(cfg)
     dev = host_to_device(h)
-    r = Runner(cfg, dev)
-    r.route()
+    if dtype == "fp8":
+        dev, r = _setup(cfg, dev)
+    else:
+        r = Runner(cfg, dev)
+        r.route()
     dout_d, _ = _dout(cfg, cfg.tokens)
     ws = torch.empty(moe.moe_backward_workspace_size(r.shape), dtype=torch.uint8, device="cuda")
     outs = []
@@ -265,3 +272,89 @@ def test_backward_saved_prefill_shape_matches_recompute():
     print("relative differences:", {k: round(v, 5) for k, v in worst.items()}, flush=True)
     for k, v in worst.items():
         assert v <= BWD_TOL, (k, v)
+
+
+FP8_CASES = [
+    _small("saved-fp8-small", 200, 256, 16, 4, 1, 128, cid=85, dtype="fp8"),
+    _small("saved-fp8-two-shared", 512, 512, 16, 4, 2, 256, cid=86, dtype="fp8"),
+    _small("saved-fp8-max-segments-sparse", 512, 128, 512, 8, 64, 128, cid=87, dtype="fp8"),
+]
+
+
+@pytest.mark.parametrize("cfg", FP8_CASES, ids=lambda c: c.name)
+def test_fp8_saved_pair_parity(cfg):
+    print(f"fp8 saved pair: {cfg.name} T={cfg.tokens} d={cfg.hidden} N={cfg.n_routed} K={cfg.top_k} "
+          f"Ns={cfg.n_shared} I={cfg.inter}", flush=True)
+    h = host.make_host_inputs(cfg)
+    hf = {k: _f(v) for k, v in h.items()}
+    dev, r = _setup(cfg, host_to_device(h))
+    r.forward()
+    ref_out = r.out.clone()
+    saved = _saved_buffer(r.shape, fill=0xFF)
+    out = torch.empty_like(ref_out)
+    moe.moe_forward_train(r.shape, dev["u"], r.weights, r.idx, r.gate, out, saved, r.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    dout_d, dout_h = _dout(cfg, cfg.tokens)
+    du, de, g = _backward_saved(cfg, r, dev, dout_d, saved)
+    idx = r.idx.cpu().numpy().astype(np.int64)
+    shq = _weights_q(dev, "sh_")
+    du_o, de_o, dr_o, dsh_o = O.layer_backward_fp8(hf["u"], hf["centroids"], idx, _weights_q(dev, "w_"),
+                                                   [shq(s) for s in range(cfg.n_shared)], dout_h, saved=True)
+    du_g = to_host_f32(du)
+    errs = {"du": (_fro(du_g - dout_h, du_o - dout_h), _row_rel(du_g, du_o))}
+    de_g = de.cpu().numpy()
+    used = sorted(dr_o)
+    errs["de"] = (_fro(de_g[used], de_o[used]), _row_rel(de_g[used], de_o[used]))
+    assert np.all(de_g[[e for e in range(cfg.n_routed) if e not in dr_o]] == 0)
+    w = (0.0, 0.0)
+    for name, j in (("w_gate", 0), ("w_up", 1), ("w_down", 2)):
+        got = to_host_f32(g[name])
+        for e in range(cfg.n_routed):
+            if e in dr_o:
+                w = (max(w[0], _fro(got[e], dr_o[e][j])), max(w[1], _rel(got[e], dr_o[e][j])))
+            else:
+                assert np.all(got[e] == 0), (name, e)
+    errs["dW_routed"] = w
+    w = (0.0, 0.0)
+    for s_i, grads in enumerate(dsh_o):
+        for name, j in (("sh_gate", 0), ("sh_up", 1), ("sh_down", 2)):
+            got = to_host_f32(g[name])[s_i]
+            w = (max(w[0], _fro(got, grads[j])), max(w[1], _rel(got, grads[j])))
+    errs["dW_shared"] = w
+    _check(errs)
+
+
+# Two FP8 models apart: a, b rounded to bf16 move some E4M3 codes of dA and dB by one step.  The
+# oracle bounds that distance between its own two FP8 variants by 2e-2 (Frobenius,
+# tests/test_oracle_backward_bf16.py); one E4M3 step moves an element by at most 1/8 of itself.
+FP8_SAVED_VS_RECOMPUTE_FRO = 2e-2
+FP8_SAVED_VS_RECOMPUTE_MAX = 0.125
+
+
+def test_fp8_saved_prefill_shape_matches_recompute():
+    """T = 8192 at the V3 shape: the FP8 saved path against the FP8 recomputing backward, per
+    expert matrix and on du - dout, within the distance the two FP8 models allow each other (the
+    oracle's parity of each is checked on the small cases)."""
+    cfg = CONFIGS[4]
+    print("fp8 backward_saved vs moe_backward: V3 prefill shape, T=8192", flush=True)
+    dev, r = _setup(cfg, make_device_inputs(cfg))
+    saved = _saved_buffer(r.shape)
+    moe.moe_forward_train(r.shape, dev["u"], r.weights, r.idx, r.gate, r.out, saved, r.ws)
+    dout_d, _ = _dout(cfg, cfg.tokens)
+    a = _backward_saved(cfg, r, dev, dout_d, saved)
+    del saved
+    b = _backward(cfg, r, dev, dout_d)
+    x, y = a[0].float() - dout_d.float(), b[0].float() - dout_d.float()
+    worst = {"du": ((x - y).norm() / y.norm()).item()}
+    for k in ("w_gate", "w_up", "w_down"):
+        x, y = a[2][k].float(), b[2][k].float()
+        used = y.flatten(1).abs().amax(1) > 0
+        fro = ((x - y)[used].flatten(1).norm(dim=1) / y[used].flatten(1).norm(dim=1)).max().item()
+        mx = ((x - y)[used].flatten(1).abs().amax(1) / y[used].flatten(1).abs().amax(1)).max().item()
+        worst[k] = (fro, mx)
+        del x, y
+    print("relative differences (frobenius[, max-abs]):", worst, flush=True)
+    assert worst["du"] <= FP8_SAVED_VS_RECOMPUTE_FRO
+    for k in ("w_gate", "w_up", "w_down"):
+        assert worst[k][0] <= FP8_SAVED_VS_RECOMPUTE_FRO and worst[k][1] <= FP8_SAVED_VS_RECOMPUTE_MAX, (k, worst[k])
