@@ -125,7 +125,12 @@ def test_forward_train_output_and_saved_rows(cfg):
     assert worst <= 1e-2
 
 
-@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+# the largest segment count with full 256-row tiles in the input-gradient products (backward
+# only: the saved-row walk above would take minutes at 590 K rows)
+BWD_CASES = CASES + [_small("saved-max-segments", 8192, 128, 512, 8, 64, 128, cid=89)]
+
+
+@pytest.mark.parametrize("cfg", BWD_CASES, ids=lambda c: c.name)
 def test_backward_saved_parity(cfg):
     print(f"backward_saved: {cfg.name} T={cfg.tokens} d={cfg.hidden} N={cfg.n_routed} K={cfg.top_k} "
           f"Ns={cfg.n_shared} I={cfg.inter}", flush=True)
