@@ -363,3 +363,26 @@ def test_fp8_saved_prefill_shape_matches_recompute():
     assert worst["du"] <= FP8_SAVED_VS_RECOMPUTE_FRO
     for k in ("w_gate", "w_up", "w_down"):
         assert worst[k][0] <= FP8_SAVED_VS_RECOMPUTE_FRO and worst[k][1] <= FP8_SAVED_VS_RECOMPUTE_MAX, (k, worst[k])
+
+
+def test_saved_pair_zero_tokens():
+    """T = 0: moe_forward_train is a no-op (a null saved buffer is allowed) and moe_backward_saved
+    writes zero weight and centroid gradients, as moe_backward does."""
+    cfg = _small("saved-empty", 64, 256, 8, 2, 1, 128, cid=64)
+    dev = host_to_device(host.make_host_inputs(cfg))
+    r = Runner(cfg, dev, tokens=0)
+    moe.moe_forward_train(r.shape, dev["u"], r.weights, r.idx, r.gate, r.out, None, r.ws)
+    g = _grads_like(dev, 1)
+    for t in g.values():
+        t.fill_(1.0)
+    de = torch.full((cfg.n_routed, cfg.hidden), 1.0, dtype=torch.float32, device="cuda")
+    du = torch.empty((1, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    dout = torch.zeros((1, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_backward_workspace_size(r.shape), dtype=torch.uint8, device="cuda")
+    saved = _saved_buffer(r.shape, fill=0xFF)
+    wg = moe.make_weight_grads(g["w_gate"], g["w_up"], g["w_down"], g["sh_gate"], g["sh_up"], g["sh_down"])
+    moe.moe_backward_saved(r.shape, dev["u"], dev["centroids"], r.weights, r.idx, r.gate, saved, dout, du, de, wg, ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(de) == 0
+    for k, t in g.items():
+        assert torch.count_nonzero(t) == 0, k
