@@ -1052,6 +1052,7 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
         load_frags(0, 0);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
+          __builtin_amdgcn_iglp_opt(1);   // the compiler interleaves LDS reads with the MFMAs
           const int cb = kk & 1;
           if (kk + 1 < BK / 16) load_frags(cb ^ 1, kk + 1);
 #pragma unroll
@@ -1280,6 +1281,7 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
         load_frags(0, 0);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
+          __builtin_amdgcn_iglp_opt(1);   // the compiler interleaves LDS reads with the MFMAs
           const int cb = kk & 1;
           if (kk + 1 < BK / 16) load_frags(cb ^ 1, kk + 1);
 #pragma unroll
