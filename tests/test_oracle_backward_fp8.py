@@ -111,3 +111,21 @@ def test_bf16_round_matches_torch():
                         np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0, -0.0])])
     want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(O.bf16_round(x), want)
+
+
+def test_fp8_input_gradient_quantises_each_token_on_its_own():
+    # R16 quantises [dA dB] per 1x128 tile along 2I, i.e. within one token's row, and every
+    # other step before du is per row as well.  So scaling one token's dout by a power of two
+    # leaves every other token's du bit-identical and scales that token's du exactly; a
+    # quantiser whose tiles ran down the rows (several tokens sharing a scale) would move
+    # the neighbours' du through the shared scale.
+    L = _layer(seed=5)
+    t0 = 37
+    d2 = L["dout"].copy()
+    d2[t0] *= 8.0
+    du1 = O.layer_backward_fp8(L["u"], L["e"], L["idx"], L["rq"], L["shq"], L["dout"])[0]
+    du2 = O.layer_backward_fp8(L["u"], L["e"], L["idx"], L["rq"], L["shq"], d2)[0]
+    others = np.arange(du1.shape[0]) != t0
+    assert np.array_equal(du2[others], du1[others])
+    assert np.array_equal(du2[t0] - d2[t0], 8.0 * (du1[t0] - L["dout"][t0]))
+    assert np.any(du1[t0] != L["dout"][t0])

@@ -249,3 +249,90 @@ def test_fp8_forward_is_exact_for_grid_inputs_up_to_h():
     hq = (h.reshape(T, 1, 128) / sc[..., None]).to(torch.float8_e4m3fn).to(torch.float64) * sc[..., None].double()
     want = x + hq.reshape(T, I).numpy() @ wd.astype(np.float64).T
     np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- FP8 forward, step by step
+
+def _torch_tiles(x):
+    """1x128 tiles along the last axis, each cast with torch's float8_e4m3fn (R8 scale rule)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    r, k = t.shape
+    t = t.reshape(r, k // 128, 128)
+    amax = t.abs().amax(-1, keepdim=True)
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    return ((t / sc).to(torch.float8_e4m3fn).to(torch.float64) * sc.double()).reshape(r, k)
+
+
+def _torch_blocks(w):
+    """128x128 blocks of a stored [out, in] matrix, each cast with torch's float8_e4m3fn."""
+    t = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32))
+    n, k = t.shape
+    t = t.reshape(n // 128, 128, k // 128, 128)
+    amax = t.abs().amax(dim=(1, 3), keepdim=True)
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    return ((t / sc).to(torch.float8_e4m3fn).to(torch.float64) * sc.double()).reshape(n, k)
+
+
+def _unequal_blocks(rng, n, k, spread):
+    """Off-grid values whose 128x128 blocks differ in magnitude by the given factors."""
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    f = rng.choice(spread, size=(n // 128, k // 128)).astype(np.float32)
+    return (w.reshape(n // 128, 128, k // 128, 128) * f[:, None, :, None]).reshape(n, k)
+
+
+def test_weight_dequant_per_block_against_torch():
+    # every 128x128 block keeps its own scale: blocks that differ by factors up to 1e5
+    # dequantise to torch's per-block cast exactly (a shared scale would move the small
+    # blocks to zero and saturate the large ones)
+    rng = np.random.default_rng(23)
+    w = _unequal_blocks(rng, 384, 256, [1e-3, 0.37, 1.0, 7.5, 90.0])
+    codes, scale = O.quantize_weight_128x128(w)
+    assert len(np.unique(scale)) == scale.size
+    got = O.dequant_weight(codes, scale)
+    np.testing.assert_array_equal(got, _torch_blocks(w).numpy())
+    # and each block alone quantises to the same values (no block sees another's amax)
+    for bi in range(3):
+        for bj in range(2):
+            blk = w[128 * bi:128 * (bi + 1), 128 * bj:128 * (bj + 1)]
+            c1, s1 = O.quantize_weight_128x128(blk)
+            np.testing.assert_array_equal(O.dequant_weight(c1, s1),
+                                          got[128 * bi:128 * (bi + 1), 128 * bj:128 * (bj + 1)])
+
+
+def test_fp8_forward_against_torch_casts():
+    # the whole quantisation-faithful layer on off-grid data: u tiles with unequal amax,
+    # weights with unequal block scales, two routed experts per token and a shared expert.
+    # The reference re-derives every quantisation with torch's float8_e4m3fn cast and the
+    # float64 products with torch, so a tile or block scale applied to the wrong elements,
+    # or a skipped quantisation of u or H, separates the two.
+    rng = np.random.default_rng(24)
+    T, d, I, N, K = 6, 256, 256, 3, 2
+    u = rng.standard_normal((T, d)).astype(np.float32)
+    u *= rng.choice([0.01, 0.3, 1.0, 40.0], size=(T, d // 128)).repeat(128, axis=1).astype(np.float32)
+    ws = {n: [_unequal_blocks(rng, *shape, [0.002, 0.05, 0.4]) for shape in ((I, d), (I, d), (d, I))]
+          for n in range(N + 1)}
+    idx = np.array([[0, 1], [2, 0], [1, 2], [0, 2], [2, 1], [1, 0]])
+    gate = rng.uniform(0.2, 0.8, (T, K))
+    gate /= gate.sum(axis=1, keepdims=True)
+    q = {n: tuple(O.quantize_weight_128x128(w) for w in ws[n]) for n in ws}
+    got = O.layer_forward_fp8(u, idx, gate, lambda e: q[e], [q[N]])
+
+    x = _torch_tiles(u)
+
+    def ffn(xr, n):
+        wg, wu, wd = (_torch_blocks(w) for w in ws[n])
+        a = xr @ wg.T
+        b = xr @ wu.T
+        h = (torch.nn.functional.silu(a) * b).to(torch.float32)
+        return _torch_tiles(h.numpy()) @ wd.T
+
+    want = torch.from_numpy(u.astype(np.float64)) + ffn(x, N)
+    for t in range(T):
+        for k in range(K):
+            want[t] += gate[t, k] * ffn(x[t:t + 1], int(idx[t, k]))[0]
+    np.testing.assert_allclose(got, want.numpy(), rtol=0, atol=1e-12 * float(want.abs().max()))
+    # the test separates an unquantised u from the quantised one by far more than its bar
+    x_plain = torch.from_numpy(u.astype(np.float64))
+    alt = x_plain + ffn(x_plain, N)
+    shared_only = torch.from_numpy(u.astype(np.float64)) + ffn(x, N)
+    assert float((alt - shared_only).abs().max()) > 1e-3 * float(shared_only.abs().max())
