@@ -216,13 +216,15 @@ def swiglu_ffn(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.n
     return (silu(a) * b) @ np.asarray(w_down, dtype=np.float64).T
 
 
-def layer_forward(u, idx, gate, routed, shared, ffn=swiglu_ffn, x=None) -> np.ndarray:
+def layer_forward(u, idx, gate, routed, shared, ffn=swiglu_ffn, x=None, map=map) -> np.ndarray:
     """h'_t = u_t + sum_s FFN^(s)_s(u_t) + sum_k gate[t,k] FFN^(r)_{idx[t,k]}(u_t) (方法 §2, h' equation).
 
     routed: callable e -> (w_gate, w_up, w_down) of routed expert e;
     shared: sequence of (w_gate, w_up, w_down), one per shared expert.
     x: what the expert FFNs read (defaults to u; the FP8 variant passes the
     fake-quantised u here while the residual stays u).
+    map: how the routed experts' FFN terms are evaluated (an executor's map runs them
+    concurrently; the terms are added in increasing expert order either way).
     Rows of u, idx and gate correspond; pass a subset of rows to evaluate
     only those tokens (every term is per token).
     """
@@ -233,10 +235,14 @@ def layer_forward(u, idx, gate, routed, shared, ffn=swiglu_ffn, x=None) -> np.nd
         out += ffn(x, wg, wu, wd)
     idx = np.asarray(idx)
     gate = np.asarray(gate, dtype=np.float64)
-    for e in np.unique(idx):
+
+    def term(e):
         rows, slots = np.nonzero(idx == e)
         wg, wu, wd = routed(int(e))
-        out[rows] += gate[rows, slots][:, None] * ffn(x[rows], wg, wu, wd)
+        return rows, gate[rows, slots][:, None] * ffn(x[rows], wg, wu, wd)
+
+    for rows, y in map(term, np.unique(idx)):
+        out[rows] += y
     return out
 
 
@@ -282,12 +288,14 @@ def swiglu_ffn_backward(x, w_gate, w_up, w_down, dy):
     return da @ wg + db @ wu, da.T @ x, db.T @ x, dy.T @ h
 
 
-def layer_backward(u, centroids, idx, routed, shared, dout):
+def layer_backward(u, centroids, idx, routed, shared, dout, map=map):
     """Backward of the layer (R14): gradients of <dout, h'> for a fixed selection idx.
 
     routed: e -> (w_gate, w_up, w_down); shared: sequence of (w_gate, w_up, w_down).
     Returns (du [T, d], d_centroids [N_r, d], d_routed {e: (dWg, dWu, dWd)} for the experts
     that appear in idx, d_shared [(dWg, dWu, dWd)] per shared expert), all float64.
+    map: how the routed experts' terms are evaluated (as in layer_forward; they are added in
+    increasing expert order either way).
 
     With g_k = s_k / S (S = sum of the selected s) and dg_k = <dout_t, FFN_k(u_t)>:
     ds_j = dg_j / S - (sum_k dg_k s_k) / S^2 for selected j (0 elsewhere),
@@ -310,14 +318,19 @@ def layer_backward(u, centroids, idx, routed, shared, dout):
         d_shared.append((dwg, dwu, dwd))
     dg = np.zeros((t_n, k_n))
     d_routed = {}
-    for ex in np.unique(idx):
+
+    def term(ex):
         rows, slots = np.nonzero(idx == ex)
         wg, wu, wd = routed(int(ex))
         y = swiglu_ffn(u[rows], wg, wu, wd)
-        dg[rows, slots] = np.sum(dout[rows] * y, axis=1)
-        dx, dwg, dwu, dwd = swiglu_ffn_backward(u[rows], wg, wu, wd, gate[rows, slots][:, None] * dout[rows])
+        dg_e = np.sum(dout[rows] * y, axis=1)
+        return (int(ex), rows, slots, dg_e,
+                *swiglu_ffn_backward(u[rows], wg, wu, wd, gate[rows, slots][:, None] * dout[rows]))
+
+    for ex, rows, slots, dg_e, dx, dwg, dwu, dwd in map(term, np.unique(idx)):
+        dg[rows, slots] = dg_e
         du[rows] += dx
-        d_routed[int(ex)] = (dwg, dwu, dwd)
+        d_routed[ex] = (dwg, dwu, dwd)
     ds = dg / ssum - np.sum(dg * ssel, axis=1, keepdims=True) / ssum ** 2
     dz = ds * ssel * (1.0 - ssel)
     de = np.zeros_like(e)
@@ -442,13 +455,13 @@ def swiglu_ffn_fp8(x_deq: np.ndarray, wq_gate, wq_up, wq_down) -> np.ndarray:
     return hq @ dequant_weight(*wq_down).T
 
 
-def layer_forward_fp8(u, idx, gate, routed_q, shared_q) -> np.ndarray:
+def layer_forward_fp8(u, idx, gate, routed_q, shared_q, map=map) -> np.ndarray:
     """Quantisation-faithful FP8 layer: u quantised per 1x128 tile, weights per 128x128 block
     (routed_q(e) / shared_q entries are ((codes, scale) x 3) from quantize_weight_128x128),
     H quantised per 1x128 tile; float64 arithmetic on the dequantised values (R8)."""
     u32 = np.asarray(u, dtype=np.float32)
     x = dequant_act(*quantize_act_1x128(u32))
-    return layer_forward(u32, idx, gate, routed_q, shared_q, ffn=swiglu_ffn_fp8, x=x)
+    return layer_forward(u32, idx, gate, routed_q, shared_q, ffn=swiglu_ffn_fp8, x=x, map=map)
 
 
 # ----------------------------------------------------------------------------- FP8 backward (R16)
@@ -561,7 +574,7 @@ def expert_backward(x, dy, u_rows, dout_rows, g, wg, wu, wd, q):
     return dx, dg, (q.runs(da).T @ uo, q.runs(db).T @ uo, dwd)
 
 
-def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
+def layer_backward_steps(u, centroids, idx, routed, shared, dout, q, map=map):
     """The R14 backward taken step by step, each GEMM operand passed through policy q (R16).
 
     routed(e) / shared[i] give float64 (w_gate [I, d], w_up [I, d], w_down [d, I]); for the FP8
@@ -570,7 +583,8 @@ def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
       a = x Wg^T, b = x Wu^T, dH = held(dy Wd), h = SiLU(a) b, dg = sum dH h,
       dA = held(g dH b SiLU'(a)), dB = held(g dH SiLU(a)), dx = tiles([dA dB]) [Wg; Wu],
       dWd = runs(scaled(g, dout))^T runs(held(h)), dWg = runs(dA)^T runs(u), dWu = runs(dB)^T runs(u).
-    The router part and the residual follow layer_backward.  Returns the same tuple.
+    The router part and the residual follow layer_backward.  Returns the same tuple; map as
+    in layer_backward.
     """
     u = np.asarray(u, dtype=np.float64)
     e = np.asarray(centroids, dtype=np.float64)
@@ -596,12 +610,15 @@ def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
         d_shared.append(grads)
     dg = np.zeros((t_n, k_n))
     d_routed = {}
-    for ex in np.unique(idx):
+
+    def term(ex):
         rows, slots = np.nonzero(idx == ex)          # rows ascend: token order
-        dx, dg_e, grads = expert(rows, gate[rows, slots], *routed(int(ex)))
+        return (int(ex), rows, slots, *expert(rows, gate[rows, slots], *routed(int(ex))))
+
+    for ex, rows, slots, dx, dg_e, grads in map(term, np.unique(idx)):
         dg[rows, slots] = dg_e
         du[rows] += dx
-        d_routed[int(ex)] = grads
+        d_routed[ex] = grads
     ds = dg / ssum - np.sum(dg * ssel, axis=1, keepdims=True) / ssum ** 2
     dz = ds * ssel * (1.0 - ssel)
     de = np.zeros_like(e)
@@ -611,10 +628,10 @@ def layer_backward_steps(u, centroids, idx, routed, shared, dout, q):
     return du, de, d_routed, d_shared
 
 
-def layer_backward_fp8(u, centroids, idx, routed_q, shared_q, dout, saved=False):
+def layer_backward_fp8(u, centroids, idx, routed_q, shared_q, dout, saved=False, map=map):
     """FP8 backward of R16.  routed_q(e) / shared_q entries are ((codes, scale) x 3) from
     quantize_weight_128x128 of (w_gate, w_up, w_down); u and dout as held (bf16 values).
     saved: a and b held in bf16 from the forward (R17's saved-input variant)."""
     deq = lambda ws: tuple(dequant_weight(*w) for w in ws)  # noqa: E731
     return layer_backward_steps(u, centroids, idx, lambda ex: deq(routed_q(ex)), [deq(w) for w in shared_q], dout,
-                                Fp8SavedPolicy if saved else Fp8Policy)
+                                Fp8SavedPolicy if saved else Fp8Policy, map=map)

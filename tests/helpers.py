@@ -17,12 +17,16 @@ Matching rules (the layer of 方法 §2, "DeepSeek-V3 技術報告"):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+import threading
+
 import numpy as np
 import torch
 
 import mixture_experts_layer_adjusted_amd as moe
 from oracle import moe_oracle as O
-from synth import bf16_bits_to_f32
+from synth import bf16_bits_to_f32, host
 from synth.device import bf16_to_numpy_bits
 
 GAP_EXEMPT = 1e-6
@@ -171,3 +175,73 @@ def rel_err(y_gpu, y_ref, u=None):
     d_ref = y_ref - ue
     e2 = np.max(np.abs((y_gpu - ue) - d_ref), 1) / np.maximum(np.max(np.abs(d_ref), 1), 1e-30)
     return float(e.max()), float(e2.max())
+
+
+# ----------------------------------------------------------------------------- sampling at the V3 shapes
+
+def tile_covering_tokens(idx, n_routed, n_shared=1, seed=0, tile=128):
+    """Tokens whose rows reach every 128-row M-tile of the padded permuted layout.
+
+    Routed expert e's segment holds the tokens that picked e in increasing token order, and
+    each shared segment holds every token in order; both start on a 128-row boundary, and
+    the grouped GEMMs walk them in 256-row tiles (a segment's odd last M-tile is a half tile).
+    Every M-tile of every segment gets at least one sampled row at a random position in the
+    tile, so every 256-row tile, every half tile and every tile of the most loaded expert is
+    compared.  Greedy: a tile that already holds a sampled token is skipped."""
+    idx = np.asarray(idx)
+    T = idx.shape[0]
+    rng = np.random.default_rng(seed)
+    mark = np.zeros(T, dtype=bool)
+    segments = [np.nonzero((idx == e).any(axis=1))[0] for e in rng.permutation(n_routed)]
+    if n_shared:
+        segments.append(np.arange(T))
+    for toks in segments:
+        for m in range(0, len(toks), tile):
+            rows = toks[m:m + tile]
+            if not mark[rows].any():
+                mark[rng.choice(rows)] = True
+    return np.nonzero(mark)[0]
+
+
+def oracle_pool():
+    """Threads for the oracle's per-expert terms (numpy releases the GIL in its kernels)."""
+    return cf.ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1)))
+
+
+def _f32(a):
+    return bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, np.float32)
+
+
+class HostExperts:
+    """Oracle-side expert weights regenerated from the seeded streams on the host; with fp8=True
+    each matrix is quantised by the oracle's 128x128 block quantiser.  Nothing is copied from
+    the device."""
+
+    def __init__(self, cfg, fp8=False, report_every=32):
+        self.cfg = cfg
+        self.fp8 = fp8
+        self._lock = threading.Lock()
+        self._done = 0
+        self._every = report_every
+
+    @staticmethod
+    def _quantize(w):
+        # one 128-row strip of blocks at a time: blocks are independent, and the strips keep the
+        # oracle's temporaries small enough for several threads to quantise at once
+        parts = [O.quantize_weight_128x128(w[r:r + 128]) for r in range(0, w.shape[0], 128)]
+        return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+    def _prep(self, ws):
+        ws = tuple(_f32(w) for w in ws)
+        return tuple(self._quantize(w) for w in ws) if self.fp8 else ws
+
+    def routed(self, e):
+        w = self._prep(host.expert_weights(self.cfg, int(e)))
+        with self._lock:
+            self._done += 1
+            if self._done % self._every == 0:
+                print(f"  oracle: {self._done} routed experts prepared ({'fp8' if self.fp8 else 'bf16'})", flush=True)
+        return w
+
+    def shared(self):
+        return [self._prep(host.expert_weights(self.cfg, s, shared=True)) for s in range(self.cfg.n_shared)]

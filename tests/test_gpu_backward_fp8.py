@@ -29,7 +29,7 @@ from synth.device import fill_normal_, host_to_device, make_device_inputs
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from helpers import Runner, quantize_fp8_weights, to_host_f32
+    from helpers import HostExperts, Runner, oracle_pool, quantize_fp8_weights, to_host_f32
 
 FP8_BWD_FRO = 1e-2
 FP8_BWD_MAX = 5e-2
@@ -72,14 +72,14 @@ def _small(name, T, d, N, K, Ns, I, cid):
     return LayerConfig(cid, name, T, d, N, K, Ns, I, "fp8", "uniform0.01")
 
 
-def _weights_q(dev, prefix):
-    """Accessor e -> ((codes, scale) x 3) of the device FP8 weights, copied to the host lazily."""
+def _weights_q(hf, prefix):
+    """Accessor e -> ((codes, scale) x 3): the oracle's 128x128 block quantiser applied to the host
+    copies of the bf16 weights (nothing is read back from the device)."""
     cache = {}
 
     def get(e):
         if e not in cache:
-            cache[e] = tuple((dev[f"{prefix}{n}_q"][e].cpu().numpy(), dev[f"{prefix}{n}_scale"][e].cpu().numpy())
-                             for n in ("gate", "up", "down"))
+            cache[e] = tuple(O.quantize_weight_128x128(hf[f"{prefix}{n}"][e]) for n in ("gate", "up", "down"))
         return cache[e]
     return get
 
@@ -124,8 +124,8 @@ def test_fp8_backward_parity_small(cfg):
     dout_d, dout_h = _dout(cfg, cfg.tokens)
     du, de, g = _run_backward(cfg, r, dev, dout_d)
     idx = r.idx.cpu().numpy().astype(np.int64)
-    shq = _weights_q(dev, "sh_")
-    du_o, de_o, dr_o, dsh_o = O.layer_backward_fp8(hf["u"], hf["centroids"], idx, _weights_q(dev, "w_"),
+    shq = _weights_q(hf, "sh_")
+    du_o, de_o, dr_o, dsh_o = O.layer_backward_fp8(hf["u"], hf["centroids"], idx, _weights_q(hf, "w_"),
                                                    [shq(s) for s in range(cfg.n_shared)], dout_h)
     du_g = to_host_f32(du)
     errs = {"du": (_fro(du_g - dout_h, du_o - dout_h), _row_rel(du_g, du_o))}
@@ -176,13 +176,14 @@ def test_fp8_backward_v3_prefill_sampled():
     idx = r.idx.cpu().numpy().astype(np.int64)
     u_h = _f(host.token_rows(cfg))
     c_h = host.centroids(cfg)
-    routed = _weights_q(dev, "w_")
-    shq = _weights_q(dev, "sh_")
+    ex_q = HostExperts(cfg, fp8=True)
     deq = lambda ws: tuple(O.dequant_weight(*w) for w in ws)  # noqa: E731
     # du of a few tokens depends on those tokens' rows only
     toks = np.array([0, 4097, cfg.tokens - 1])
-    du_o, _, _, _ = O.layer_backward_steps(u_h[toks], c_h, idx[toks], lambda e: deq(routed(e)),
-                                           [deq(shq(s)) for s in range(cfg.n_shared)], dout_h[toks], O.Fp8Policy)
+    with oracle_pool() as pool:
+        du_o, _, _, _ = O.layer_backward_steps(u_h[toks], c_h, idx[toks], lambda e: deq(ex_q.routed(e)),
+                                               [deq(w) for w in ex_q.shared()], dout_h[toks], O.Fp8Policy,
+                                               map=pool.map)
     du_g = to_host_f32(du)[toks]
     errs = {"du": (_fro(du_g - dout_h[toks], du_o - dout_h[toks]), _row_rel(du_g, du_o))}
     # one routed expert's weight gradients depend on its rows (in token order) only
@@ -195,7 +196,7 @@ def test_fp8_backward_v3_prefill_sampled():
     gate = ssel[np.arange(len(rows)), slots] / ssel.sum(axis=1)
     P = O.Fp8Policy
     _, _, dw_o = O.expert_backward(P.tiles(u_h[rows]), P.tiles(dout_h[rows]), u_h[rows], dout_h[rows], gate,
-                                   *deq(routed(ex)), P)
+                                   *deq(ex_q.routed(ex)), P)
     for name, j in (("w_gate", 0), ("w_up", 1), ("w_down", 2)):
         got = to_host_f32(g[name][ex])
         errs[f"d{name}"] = (_fro(got, dw_o[j]), _rel(got, dw_o[j]))

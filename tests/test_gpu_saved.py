@@ -29,7 +29,7 @@ from synth.device import host_to_device, make_device_inputs
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from helpers import Runner, to_host_f32
+    from helpers import HostExperts, Runner, oracle_pool, to_host_f32
     from test_gpu_backward import BWD_TOL, _dout, _f, _grads_like, _rel, _row_rel
     from test_gpu_backward_fp8 import _check, _fro, _setup, _weights_q
 
@@ -252,31 +252,67 @@ def test_backward_saved_v3_decode_shape_sampled():
     assert e_du <= BWD_TOL and e_de <= BWD_TOL and e_w <= BWD_TOL
 
 
-def test_backward_saved_prefill_shape_matches_recompute():
-    """At the V3 prefill shape the oracle is out of reach for the weight gradients, so the saved
-    path is held to the recomputing one (itself checked against the oracle at the decode shape
-    and on small cases): per token / per expert matrix within the bf16 backward tolerance."""
+def _pick_experts(load):
+    """The most loaded expert, and one whose segment has at least one full 256-row tile and
+    ends in a half tile (an odd count of 128-row M-tiles)."""
+    top = int(np.argmax(load))
+    mt = -(-load // 128)
+    half = np.nonzero((mt % 2 == 1) & (load > 256))[0]
+    return top, int(half[np.argsort(load[half])[len(half) // 2]])
+
+
+def test_backward_prefill_shape_against_oracle():
+    """T = 16384 at the V3 shape (Zipf routing): moe_backward and moe_backward_saved against the
+    float64 oracle (R14).  du on sampled tokens, each from the oracle over that token's own rows,
+    and every weight gradient of two experts from the oracle's steps over exactly that expert's
+    rows: the most loaded one (its segment spans some 18 256-row tiles) and one whose segment ends
+    in a half tile."""
     cfg = CONFIGS[3]   # T=16384, d=7168, N_r=256, K_r=8, N_s=1, I=2048
-    print("backward_saved vs moe_backward: V3 prefill shape", flush=True)
+    print("backward and backward_saved vs the oracle: V3 prefill shape", flush=True)
     dev = make_device_inputs(cfg)
     r = Runner(cfg, dev)
     r.route()
-    saved = _saved_buffer(r.shape)
-    moe.moe_forward_train(r.shape, dev["u"], r.weights, r.idx, r.gate, r.out, saved, r.ws)
-    dout_d, _ = _dout(cfg, cfg.tokens)
-    a = _backward_saved(cfg, r, dev, dout_d, saved)
-    del saved
-    b = _backward(cfg, r, dev, dout_d)
-    tok = ((a[0].float() - b[0].float()).abs().amax(1) / b[0].float().abs().amax(1).clamp_min(1e-30)).max().item()
-    worst = {"du": tok}
-    for k in ("w_gate", "w_up", "w_down"):
-        x, y = a[2][k].float(), b[2][k].float()
-        den = y.abs().flatten(1).amax(1).clamp_min(1e-30)
-        worst[k] = ((x - y).abs().flatten(1).amax(1) / den).max().item()
-        del x, y
-    print("relative differences:", {k: round(v, 5) for k, v in worst.items()}, flush=True)
-    for k, v in worst.items():
-        assert v <= BWD_TOL, (k, v)
+    dout_d, dout_h = _dout(cfg, cfg.tokens)
+    idx = r.idx.cpu().numpy().astype(np.int64)
+    load = np.bincount(idx.ravel(), minlength=cfg.n_routed)
+    experts = _pick_experts(load)
+    toks = np.random.default_rng(16).choice(cfg.tokens, 16, replace=False)
+    got = {}
+    for kind in ("recompute", "saved"):
+        if kind == "saved":
+            saved = _saved_buffer(r.shape)
+            moe.moe_forward_train(r.shape, dev["u"], r.weights, r.idx, r.gate, r.out, saved, r.ws)
+            du, de, g = _backward_saved(cfg, r, dev, dout_d, saved)
+            del saved
+        else:
+            du, de, g = _backward(cfg, r, dev, dout_d)
+        got[kind] = (to_host_f32(du)[toks],
+                     {e: tuple(to_host_f32(g[n][e]) for n in ("w_gate", "w_up", "w_down")) for e in experts})
+        del du, de, g
+        torch.cuda.empty_cache()
+    u_h = _f(host.token_rows(cfg))
+    c_h = host.centroids(cfg)
+    ex = HostExperts(cfg)
+    with oracle_pool() as pool:
+        du_o, _, _, _ = O.layer_backward(u_h[toks], c_h, idx[toks], ex.routed, ex.shared(), dout_h[toks],
+                                         map=pool.map)
+    s_all = O.affinity64(u_h, c_h)
+    dw_o = {}
+    for e in experts:
+        rows, slots = np.nonzero(idx == e)
+        ssel = np.take_along_axis(s_all[rows], idx[rows], axis=1)
+        gate = ssel[np.arange(len(rows)), slots] / ssel.sum(axis=1)
+        P = O.ExactPolicy
+        _, _, dw_o[e] = O.expert_backward(u_h[rows], dout_h[rows], u_h[rows], dout_h[rows], gate, *ex.routed(e), P)
+    print(f"tokens {sorted(toks.tolist())}; experts {experts} with {[int(load[e]) for e in experts]} rows", flush=True)
+    for kind, (du_g, dw_g) in got.items():
+        errs = {"du": _row_rel(du_g, du_o)}
+        for e in experts:
+            for j, name in enumerate(("dWg", "dWu", "dWd")):
+                errs[f"{name}[{e}]"] = _rel(dw_g[e][j], dw_o[e][j])
+        print(kind, "relative errors:", {k: round(v, 5) for k, v in errs.items()}, flush=True)
+        for k, v in errs.items():
+            assert v <= BWD_TOL, (kind, k, v)
 
 
 FP8_CASES = [
@@ -303,8 +339,8 @@ def test_fp8_saved_pair_parity(cfg):
     dout_d, dout_h = _dout(cfg, cfg.tokens)
     du, de, g = _backward_saved(cfg, r, dev, dout_d, saved)
     idx = r.idx.cpu().numpy().astype(np.int64)
-    shq = _weights_q(dev, "sh_")
-    du_o, de_o, dr_o, dsh_o = O.layer_backward_fp8(hf["u"], hf["centroids"], idx, _weights_q(dev, "w_"),
+    shq = _weights_q(hf, "sh_")
+    du_o, de_o, dr_o, dsh_o = O.layer_backward_fp8(hf["u"], hf["centroids"], idx, _weights_q(hf, "w_"),
                                                    [shq(s) for s in range(cfg.n_shared)], dout_h, saved=True)
     du_g = to_host_f32(du)
     errs = {"du": (_fro(du_g - dout_h, du_o - dout_h), _row_rel(du_g, du_o))}

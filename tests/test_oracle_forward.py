@@ -336,3 +336,26 @@ def test_fp8_forward_against_torch_casts():
     alt = x_plain + ffn(x_plain, N)
     shared_only = torch.from_numpy(u.astype(np.float64)) + ffn(x, N)
     assert float((alt - shared_only).abs().max()) > 1e-3 * float(shared_only.abs().max())
+
+
+def test_concurrent_expert_terms_change_nothing():
+    # the map option only changes how the per-expert terms are evaluated: the output is
+    # bit-identical to the plain loop, forward and backward
+    import concurrent.futures as cf
+    rng = np.random.default_rng(25)
+    L = _rand_layer(rng, T=40, N=9, K=3, Ns=2)
+    idx, g, *_ = O.route(L["u"], L["e"], L["b"], L["K"])
+    routed = O.stacked(L["wg"], L["wu"], L["wd"])
+    shared = list(zip(L["sg"], L["su"], L["sd"]))
+    dout = rng.standard_normal(L["u"].shape)
+    with cf.ThreadPoolExecutor(4) as pool:
+        a = O.layer_forward(L["u"], idx, g, routed, shared, map=pool.map)
+        b1 = O.layer_backward(L["u"], L["e"], idx, routed, shared, dout, map=pool.map)
+        b2 = O.layer_backward_steps(L["u"], L["e"], idx, routed, shared, dout, O.Bf16Policy, map=pool.map)
+    assert np.array_equal(a, O.layer_forward(L["u"], idx, g, routed, shared))
+    for x, y in ((b1, O.layer_backward(L["u"], L["e"], idx, routed, shared, dout)),
+                 (b2, O.layer_backward_steps(L["u"], L["e"], idx, routed, shared, dout, O.Bf16Policy))):
+        assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+        assert x[2].keys() == y[2].keys()
+        for e in x[2]:
+            assert all(np.array_equal(p, q) for p, q in zip(x[2][e], y[2][e]))
