@@ -16,9 +16,12 @@
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is DEVICE memory owned by the caller.  The library
- *    keeps no hidden state, never allocates device memory, and never
- *    synchronises: work is enqueued on `stream` and results are valid once the
- *    stream has completed it.  Scratch memory is the caller's workspace.
+ *    never allocates device memory and never synchronises: work is enqueued on
+ *    `stream` (which must belong to the calling thread's current device) and
+ *    results are valid once the stream has completed it.  Scratch memory is the
+ *    caller's workspace.  Between calls the library keeps only per-device facts
+ *    set up once per device (its CU count and the kernels' LDS limits), under
+ *    std::call_once / a mutex, so host threads may call it concurrently.
  *  - Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and the outputs are untouched.  A failed launch
  *    returns MOE_ERR_HIP.  No C++ exception crosses the ABI.

@@ -1112,17 +1112,9 @@ hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
   if (g.n_seg < 1 || g.n_seg > kMaxRouted + kMaxShared) return hipErrorInvalidValue;
   const size_t lds_bytes = stage_bytes + 2 * (size_t)(g.n_seg + 1) * sizeof(int32_t) + red_bytes;
   auto kern = &grouped_gemm_bf16_persistent_kernel<EPI, WKN>;
-  static bool attr_set = false;
-  static int n_cu = 0;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
-    if (err != hipSuccess) return err;
-    int dev = 0;
-    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
-    if ((err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
-    attr_set = true;
-  }
+  int n_cu = 0;
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)max_lds);
+  if (err != hipSuccess || (err = device_cu_count(&n_cu)) != hipSuccess) return err;
   const int NT = (int)ceil_div(g.N, EPI == 0 ? 256 : 128);
   if (g.max_pairs * NT == 0) return hipSuccess;
   if (EPI == 2 && g.N % 128 != 0) return hipErrorInvalidValue;   // dg_part holds N / 128 tiles per row
@@ -1330,17 +1322,9 @@ hipError_t launch_wgrad_bf16(const GemmOperands& g, hipStream_t st) {
   const size_t max_lds = stage_bytes + (size_t)(kMaxRouted + kMaxShared + 1) * sizeof(int32_t);
   if (max_lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
   const size_t lds_bytes = stage_bytes + (size_t)(g.n_seg + 1) * sizeof(int32_t);
-  static bool attr_set = false;
-  static int n_cu = 0;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_bf16_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
-    if (err != hipSuccess) return err;
-    int dev = 0;
-    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
-    if ((err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
-    attr_set = true;
-  }
+  int n_cu = 0;
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(&grouped_wgrad_bf16_kernel), (int)max_lds);
+  if (err != hipSuccess || (err = device_cu_count(&n_cu)) != hipSuccess) return err;
   const int NT = (int)ceil_div(g.N, 256);
   const int64_t tiles = (int64_t)g.n_seg * ceil_div(g.wg_m, 256) * NT;
   if (tiles == 0) return hipSuccess;
@@ -1357,13 +1341,8 @@ hipError_t launch_stream(const GemmOperands& g, hipStream_t st) {
   const int NT = (int)ceil_div(g.N, SWIGLU ? SR / 2 : SR);
   const size_t lds_bytes = SC::kStages * SC::kStageElems * sizeof(uint16_t);
   auto kern = &grouped_gemm_bf16_stream_kernel<EPI, SBK, SW, SR, SG, SM, STM, WKN>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds_bytes);
+  if (err != hipSuccess) return err;
   const int64_t tiles = (STM == kTileM ? g.max_tiles : g.max_pairs) * NT;
   const int64_t span = kXcds * SC::kXcdChunk;
   const int64_t grid = ceil_div(tiles, span) * span;
@@ -1400,13 +1379,8 @@ hipError_t launch_bf16(const GemmOperands& g, hipStream_t st) {
   }
   if (EPI == 2) return hipErrorInvalidValue;   // the backward mode exists in the streaming kernel only
   const size_t lds_bytes = 2 * kStageElems * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_kernel<SWIGLU>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm_bf16_kernel<SWIGLU>), (int)lds_bytes);
+  if (err != hipSuccess) return err;
   dim3 grid((unsigned)g.max_tiles, (unsigned)ceil_div(g.N, SWIGLU ? kWRows / 2 : kWRows));
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<SWIGLU>, grid, dim3(kThreads), lds_bytes, st, g);
   return hipGetLastError();

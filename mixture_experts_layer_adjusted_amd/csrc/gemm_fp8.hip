@@ -699,17 +699,9 @@ hipError_t launch_wgrad_fp8(const GemmOperands& g, hipStream_t st) {
   const size_t max_lds = stage_bytes + (size_t)(kMaxRouted + kMaxShared + 1) * sizeof(int32_t);
   if (max_lds > 163840) return hipErrorInvalidValue;
   const size_t lds_bytes = stage_bytes + (size_t)(g.n_seg + 1) * sizeof(int32_t);
-  static bool attr_set = false;
-  static int n_cu = 0;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_fp8_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
-    if (err != hipSuccess) return err;
-    int dev = 0;
-    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
-    if ((err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
-    attr_set = true;
-  }
+  int n_cu = 0;
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(&grouped_wgrad_fp8_kernel), (int)max_lds);
+  if (err != hipSuccess || (err = device_cu_count(&n_cu)) != hipSuccess) return err;
   const int NT = (int)ceil_div(g.N, kWRows);
   const int64_t tiles = (int64_t)g.n_seg * ceil_div(g.wg_m, kTM) * NT;
   if (tiles == 0) return hipSuccess;
@@ -730,13 +722,8 @@ hipError_t launch_fp8(const GemmOperands& g, hipStream_t st) {
   // 32-bit byte offsets address the activation matrix and one expert's weight matrix
   if (g.act_rows * g.K >= (int64_t(1) << 32) || (int64_t)g.N * g.K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const size_t lds_bytes = kStages * kStageBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_fp8_kernel<EPI, WKN>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(&grouped_gemm_fp8_kernel<EPI, WKN>), (int)lds_bytes);
+  if (err != hipSuccess) return err;
   const int NT = (int)ceil_div(g.N, SWIGLU ? kWRows / 2 : kWRows);
   const int64_t tiles = g.max_pairs * NT;
   const int64_t grid = ceil_div(tiles, kXcds * kXcdChunk) * (kXcds * kXcdChunk);

@@ -82,6 +82,13 @@ struct RouteWorkspace {
   float* zpart;
 };
 
+// ---- per-device state (device_state.hip): set up once per device, thread-safe ----
+hipError_t current_device(int* dev);
+// CU count of the current device
+hipError_t device_cu_count(int* n_cu);
+// raise `kernel`'s dynamic LDS limit to `bytes` on the current device (once per device)
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+
 // ---- launchers (return hipSuccess or the launch error) ----
 bool route_uses_mfma(const moe_shape& s);
 int64_t route_mfma_blocks(const moe_shape& s);

@@ -545,13 +545,8 @@ hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float*
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t lds_bytes = 2 * kLStageElems * sizeof(uint16_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  if ((err = ensure_dynamic_lds(reinterpret_cast<const void*>(&router_logits_kernel), (int)lds_bytes)) != hipSuccess)
+    return err;
   const int splits = route_logit_splits(s);
   const int nk = d / kLBK, nk_per = (int)ceil_div(nk, splits);
   hipLaunchKernelGGL(router_logits_kernel, dim3((unsigned)ceil_div(T, kLT), (unsigned)(npad / kLE), (unsigned)splits),
@@ -737,13 +732,8 @@ hipError_t launch_seq_balance(const moe_shape& s, int seq_len, float alpha, cons
     return hipGetLastError();
   }
   const size_t lds = (size_t)seq_len * 4 + (size_t)s.n_routed * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&seq_balance_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 65536 + 4 * kMaxRouted);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(&seq_balance_kernel), 65536 + 4 * kMaxRouted);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(seq_balance_kernel, dim3((unsigned)n_seq), dim3(256), lds, st, scores, idx, s.n_routed, s.top_k,
                      seq_len, alpha, loss);
   return hipGetLastError();
