@@ -246,6 +246,24 @@ moe_status moe_backward_saved(const moe_shape* shape, const void* u, const float
 moe_status moe_update_bias(int32_t n_routed, int64_t total_assignments, const int32_t* expert_load,
                            float* bias, float gamma, hipStream_t stream);
 
+/* One-time weight preparation for moe_forward and moe_backward (untimed, outside the hot path).
+ *   logical       the layer's weights as stored: bf16 for BF16 and FP8_B128, fp32 for F32
+ *                 (scale pointers ignored; shared pointers may be NULL when n_shared == 0)
+ *   packed        device buffer of *packed_bytes bytes owned by the caller (FP8_B128 only)
+ *   prepared      out: the moe_weights to pass to moe_forward / moe_backward
+ * With prepared == NULL the call only writes to *packed_bytes the size `packed` needs (0 for BF16
+ * and F32) and touches nothing else.  BF16 and F32: the kernels read the weights as stored, so
+ * `prepared` receives the logical pointers and nothing is launched.  FP8_B128 (核心概念, FP8 item:
+ * E4M3 weights with one fp32 scale per 128x128 block): every stack is quantised as by
+ * moe_quantize_weights into `packed` (the six code stacks, then the six scale stacks, each
+ * 256-byte aligned), and `prepared` points into it.  `packed` must stay allocated while
+ * `prepared` is in use and may not overlap the logical weights.
+ * Errors: check_shape's; MOE_ERR_INVALID_ARG for a null logical, packed_bytes, needed weight
+ * pointer or (FP8_B128) packed; MOE_ERR_WORKSPACE if *packed_bytes is too small.  Nothing is
+ * launched on an error. */
+moe_status moe_prepare_weights(const moe_shape* shape, const moe_weights* logical, void* packed,
+                               size_t* packed_bytes, moe_weights* prepared, hipStream_t stream);
+
 /* FP8 weight preparation (核心概念, FP8 item: 128x128 block scaling): quantises a stack of
  * n_mats bf16 matrices [rows, cols] into E4M3FN codes [n_mats, rows, cols] and fp32 scales
  * [n_mats, rows/128, cols/128]: scale = amax/448 (1 for an all-zero block), code =

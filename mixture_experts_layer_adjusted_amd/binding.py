@@ -61,6 +61,8 @@ _SIG = {
     "moe_forward_profiled": [ctypes.POINTER(Shape), _P, ctypes.POINTER(Weights), _P, _P, _P, _P, ctypes.c_size_t,
                              _P, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32],
     "moe_update_bias": [ctypes.c_int32, ctypes.c_int64, _P, _P, ctypes.c_float, _P],
+    "moe_prepare_weights": [ctypes.POINTER(Shape), ctypes.POINTER(Weights), _P, ctypes.POINTER(ctypes.c_size_t),
+                            ctypes.POINTER(Weights), _P],
     "moe_quantize_weights": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
     "moe_quantize_act": [ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
     "moe_route_balance": [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -204,6 +206,20 @@ def moe_forward_profiled(shape, u, weights: Weights, topk_idx, topk_gate, out, w
 def moe_update_bias(n_routed, total_assignments, expert_load, bias, gamma, stream=None):
     _check("moe_update_bias", _lib.moe_update_bias(n_routed, total_assignments, _ptr(expert_load), _ptr(bias),
                                                    gamma, _stream(stream)))
+
+
+def moe_prepare_weights(shape, logical, packed=None, stream=None, size_only=False):
+    """size_only: returns the bytes `packed` needs.  Otherwise returns the prepared Weights (for
+    FP8_B128 they point into `packed`, which must outlive them)."""
+    n = ctypes.c_size_t(0 if packed is None else _nbytes(packed))
+    if size_only:
+        _check("moe_prepare_weights", _lib.moe_prepare_weights(ctypes.byref(shape), ctypes.byref(logical), None,
+                                                               ctypes.byref(n), None, None))
+        return n.value
+    prepared = Weights()
+    _check("moe_prepare_weights", _lib.moe_prepare_weights(ctypes.byref(shape), ctypes.byref(logical), _ptr(packed),
+                                                           ctypes.byref(n), ctypes.byref(prepared), _stream(stream)))
+    return prepared
 
 
 def moe_quantize_weights(n_mats, rows, cols, w_bf16, codes, scales, stream=None):

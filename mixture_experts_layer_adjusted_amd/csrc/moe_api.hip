@@ -707,6 +707,64 @@ moe_status moe_quantize_weights(int32_t n_mats, int32_t rows, int32_t cols, cons
   return hip_status(launch_quantize_weights(n_mats, rows, cols, w_bf16, codes, scales, stream));
 }
 
+moe_status moe_prepare_weights(const moe_shape* shape, const moe_weights* logical, void* packed, size_t* packed_bytes,
+                               moe_weights* prepared, hipStream_t stream) {
+  moe_status rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!logical || !packed_bytes) return MOE_ERR_INVALID_ARG;
+  const moe_shape& s = *shape;
+  const int64_t N = s.n_routed, Ns = s.n_shared, d = s.hidden, I = s.inter;
+  const bool fp8 = s.dtype == MOE_DTYPE_FP8_B128;
+  // the six stacks in moe_weights order: routed gate, up, down, then shared gate, up, down
+  const void* src[6] = {logical->w_gate, logical->w_up, logical->w_down, logical->sh_gate, logical->sh_up,
+                        logical->sh_down};
+  const int64_t n[6] = {N, N, N, Ns, Ns, Ns};
+  const int64_t rows[6] = {I, I, d, I, I, d}, cols[6] = {d, d, I, d, d, I};
+  // FP8 packing: the six E4M3 code stacks, then the six fp32 scale stacks, each 256-byte aligned
+  size_t code_off[6], scale_off[6], o = 0;
+  for (int i = 0; i < 6; ++i) {
+    code_off[i] = o;
+    o = align_up(o + (fp8 ? (size_t)(n[i] * rows[i] * cols[i]) : 0), 256);
+  }
+  for (int i = 0; i < 6; ++i) {
+    scale_off[i] = o;
+    o = align_up(o + (fp8 ? (size_t)(n[i] * (rows[i] / 128) * (cols[i] / 128)) * 4 : 0), 256);
+  }
+  if (!prepared) {   // size query
+    *packed_bytes = o;
+    return MOE_OK;
+  }
+  for (int i = 0; i < 6; ++i)
+    if (n[i] > 0 && !src[i]) return MOE_ERR_INVALID_ARG;
+  if (!fp8) {        // bf16 and fp32 weights are used as stored
+    *prepared = moe_weights{};
+    prepared->w_gate = logical->w_gate;
+    prepared->w_up = logical->w_up;
+    prepared->w_down = logical->w_down;
+    prepared->sh_gate = Ns > 0 ? logical->sh_gate : nullptr;
+    prepared->sh_up = Ns > 0 ? logical->sh_up : nullptr;
+    prepared->sh_down = Ns > 0 ? logical->sh_down : nullptr;
+    return MOE_OK;
+  }
+  if (*packed_bytes < o) return MOE_ERR_WORKSPACE;
+  if (!packed) return MOE_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(packed);
+  const void* codes[6];
+  const float* scales[6];
+  for (int i = 0; i < 6; ++i) {
+    codes[i] = n[i] > 0 ? base + code_off[i] : nullptr;
+    scales[i] = n[i] > 0 ? reinterpret_cast<const float*>(base + scale_off[i]) : nullptr;
+    if (n[i] == 0) continue;
+    hipError_t e = launch_quantize_weights((int32_t)n[i], (int32_t)rows[i], (int32_t)cols[i], src[i],
+                                           reinterpret_cast<uint8_t*>(base + code_off[i]),
+                                           reinterpret_cast<float*>(base + scale_off[i]), stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  *prepared = moe_weights{codes[0], codes[1], codes[2], codes[3], codes[4], codes[5],
+                          scales[0], scales[1], scales[2], scales[3], scales[4], scales[5]};
+  return MOE_OK;
+}
+
 moe_status moe_quantize_act(int32_t rows, int32_t cols, const void* x_bf16, uint8_t* codes, float* scales,
                             hipStream_t stream) {
   if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;

@@ -192,3 +192,40 @@ def test_saved_input_pair_errors_before_launch():
     assert bwd(sb, saved, big, fake, big) == 1                                               # du == u
     assert bwd(s32, saved, big, du, big) == 2
     assert bwd(s8, saved, big, du, big) == 1                                                 # no weight scales
+
+
+def test_prepare_weights_sizes_and_errors_before_launch():
+    """moe_prepare_weights: a size query (prepared = NULL) touches nothing; BF16 needs no packed
+    buffer; FP8_B128 packs the six code stacks then the six scale stacks, each 256-byte aligned."""
+    lib = binding.raw_lib()
+    fake = ctypes.c_void_p(0x1000)
+    w = moe.Weights(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)
+    n = ctypes.c_size_t(12345)
+    T, d, N, K, Ns, I = 256, 7168, 256, 8, 1, 2048
+    s8 = moe.make_shape(T, d, N, K, Ns, I, moe.MOE_DTYPE_FP8_B128)
+    assert lib.moe_prepare_weights(ctypes.byref(s8), ctypes.byref(w), None, ctypes.byref(n), None, None) == 0
+    al = lambda x: -(-x // 256) * 256  # noqa: E731
+    codes = 3 * al(N * I * d) + 3 * al(Ns * I * d)
+    scales = 3 * al(N * (I // 128) * (d // 128) * 4) + 3 * al(Ns * (I // 128) * (d // 128) * 4)
+    assert n.value == codes + scales
+    assert moe.moe_prepare_weights(s8, w, size_only=True) == codes + scales
+    sb = moe.make_shape(T, d, N, K, Ns, I, moe.MOE_DTYPE_BF16)
+    assert moe.moe_prepare_weights(sb, w, size_only=True) == 0
+    # bf16: the prepared weights are the logical ones, nothing launched
+    out = moe.Weights()
+    n0 = ctypes.c_size_t(0)
+    assert lib.moe_prepare_weights(ctypes.byref(sb), ctypes.byref(w), None, ctypes.byref(n0), ctypes.byref(out),
+                                   None) == 0
+    assert (out.w_gate, out.w_up, out.w_down, out.sh_gate, out.sh_up, out.sh_down) == \
+        (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)
+    # fp8 errors: too small a packed buffer, null packed, a missing weight stack
+    small = ctypes.c_size_t(n.value - 1)
+    assert lib.moe_prepare_weights(ctypes.byref(s8), ctypes.byref(w), fake, ctypes.byref(small), ctypes.byref(out),
+                                   None) == 3
+    assert lib.moe_prepare_weights(ctypes.byref(s8), ctypes.byref(w), None, ctypes.byref(n), ctypes.byref(out),
+                                   None) == 1
+    w_missing = moe.Weights(0x1000, None, 0x3000, 0x4000, 0x5000, 0x6000)
+    assert lib.moe_prepare_weights(ctypes.byref(s8), ctypes.byref(w_missing), fake, ctypes.byref(n),
+                                   ctypes.byref(out), None) == 1
+    assert lib.moe_prepare_weights(ctypes.byref(s8), None, fake, ctypes.byref(n), ctypes.byref(out), None) == 1
+    assert lib.moe_prepare_weights(ctypes.byref(s8), ctypes.byref(w), fake, None, ctypes.byref(out), None) == 1
