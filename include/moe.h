@@ -114,6 +114,25 @@ moe_status moe_route(const moe_shape* shape, const void* u, const float* centroi
                      int32_t* expert_load, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* Size of the fixed device array that holds moe_route_noalloc's scratch (one per GPU). */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_route without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * outputs, errors and results as moe_route, bit for bit.  The routing's scratch lives in a
+ * file-scope device array of MOE_ROUTE_NOALLOC_SCRATCH_BYTES (64 MiB): each GPU the library
+ * runs on holds its own copy from the library's load until the process ends, and its address is
+ * looked up once per device on the first call there.  The call allocates nothing.
+ *   - A shape whose routing scratch exceeds the array (at d=7168, N_r=256 that is T > 52330)
+ *     returns MOE_ERR_WORKSPACE before anything touches the GPU.
+ *   - `stream` must belong to the calling thread's current device (else MOE_ERR_INVALID_ARG).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two streams,
+ *     two host threads, or a call overlapping a graph replay that contains one) race on it and
+ *     must be ordered by the caller.  Nothing in the array needs clearing between calls. */
+moe_status moe_route_noalloc(const moe_shape* shape, const void* u, const float* centroids,
+                             const float* bias, int32_t* topk_idx, float* topk_gate,
+                             int32_t* expert_load, hipStream_t stream);
+
 /* moe_route with a per-token group limit.  The page's cross-node all-to-all section limits
  * every token to experts on at most 4 nodes and prints no rule for choosing them; the reading
  * here: the N_r experts form n_groups equal contiguous groups (expert i is in group

@@ -55,6 +55,7 @@ _P = ctypes.c_void_p
 _SIG = {
     "moe_workspace_size": [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)],
     "moe_route": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_route_noalloc": [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P],
     "moe_route_grouped": [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                           ctypes.c_size_t, _P],
     "moe_forward": [ctypes.POINTER(Shape), _P, ctypes.POINTER(Weights), _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -175,6 +176,12 @@ def moe_route(shape, u, centroids, bias, topk_idx, topk_gate, expert_load, works
     _check("moe_route", _lib.moe_route(ctypes.byref(shape), _ptr(u), _ptr(centroids), _ptr(bias), _ptr(topk_idx),
                                        _ptr(topk_gate), _ptr(expert_load), _ptr(workspace), _nbytes(workspace),
                                        _stream(stream)))
+
+
+def moe_route_noalloc(shape, u, centroids, bias, topk_idx, topk_gate, expert_load, stream=None):
+    _check("moe_route_noalloc", _lib.moe_route_noalloc(ctypes.byref(shape), _ptr(u), _ptr(centroids), _ptr(bias),
+                                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(expert_load),
+                                                       _stream(stream)))
 
 
 def moe_route_grouped(shape, n_groups, topk_groups, u, centroids, bias, topk_idx, topk_gate, expert_load, workspace,

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/moe.h: argument validation,
 // workspace layout, and the ordered launch of the kernels of each call.
+#include <mutex>
 #include <new>
 
 #include "moe_internal.h"
@@ -250,16 +251,19 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
   return MOE_OK;
 }
 
+// route_only: the workspace holds the routing's scratch only (moe_route_noalloc), not the
+// forward's as well
 static moe_status route_impl(const moe_shape* shape, GroupLimit gl, const void* u, const float* centroids,
                              const float* bias, int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream, bool keep_scores = false) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream, bool keep_scores = false,
+                             bool route_only = false) {
   moe_status rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!expert_load) return MOE_ERR_INVALID_ARG;
   if (shape->tokens > 0 && (!u || !centroids || !bias || !topk_idx || !topk_gate || !workspace))
     return MOE_ERR_INVALID_ARG;
   const WorkspacePlan p = plan_workspace(*shape);
-  if (shape->tokens > 0 && workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  if (shape->tokens > 0 && workspace_bytes < (route_only ? p.route_bytes : p.total)) return MOE_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
   RouteWorkspace rw{reinterpret_cast<int32_t*>(wsb + p.route_partial), reinterpret_cast<uint16_t*>(wsb + p.route_e_hi),
                     reinterpret_cast<uint16_t*>(wsb + p.route_e_mid), reinterpret_cast<uint16_t*>(wsb + p.route_e_lo),
@@ -274,6 +278,60 @@ moe_status moe_route(const moe_shape* shape, const void* u, const float* centroi
                      size_t workspace_bytes, hipStream_t stream) {
   return route_impl(shape, GroupLimit{1, 1}, u, centroids, bias, topk_idx, topk_gate, expert_load, workspace,
                     workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- moe_route_noalloc: the routing scratch in a fixed device array ----
+//
+// One copy of `scratch` exists on every GPU the library runs on, from module load until the
+// process ends.  In host code its name is only a host-side stand-in: the device address of the
+// current GPU's copy comes from hipGetSymbolAddress, looked up once per device and kept in
+// g_scratch_ptr; only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MOE_ROUTE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+
+// The current device's copy of `scratch`; `stream` must belong to that device.
+moe_status scratch_for(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  if (current_device(&dev) != hipSuccess || dev >= kScratchDevices) return MOE_ERR_HIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_ERR_HIP;
+    if (sdev != dev) return MOE_ERR_INVALID_ARG;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return MOE_ERR_HIP;
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route_noalloc(const moe_shape* shape, const void* u, const float* centroids, const float* bias,
+                             int32_t* topk_idx, float* topk_gate, int32_t* expert_load, hipStream_t stream) {
+  moe_status rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!expert_load) return MOE_ERR_INVALID_ARG;
+  if (shape->tokens > 0 && (!u || !centroids || !bias || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+  // size check first, on the host: a shape beyond the array is refused before the GPU is touched
+  if (plan_workspace(*shape).route_bytes > (size_t)MOE_ROUTE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ptr = nullptr;
+  if ((rc = scratch_for(stream, &ptr)) != MOE_OK) return rc;
+  // the routing kernels write every scratch element they later read (partial counts, split
+  // centroids, affinities, split-K partial logits), so nothing has to be cleared between calls
+  return route_impl(shape, GroupLimit{1, 1}, u, centroids, bias, topk_idx, topk_gate, expert_load, ptr,
+                    MOE_ROUTE_NOALLOC_SCRATCH_BYTES, stream, false, true);
 }
 
 moe_status moe_route_grouped(const moe_shape* shape, int32_t n_groups, int32_t topk_groups, const void* u,

@@ -229,3 +229,14 @@ def test_prepare_weights_sizes_and_errors_before_launch():
                                    ctypes.byref(out), None) == 1
     assert lib.moe_prepare_weights(ctypes.byref(s8), None, fake, ctypes.byref(n), ctypes.byref(out), None) == 1
     assert lib.moe_prepare_weights(ctypes.byref(s8), ctypes.byref(w), fake, None, ctypes.byref(out), None) == 1
+
+
+def test_noalloc_route_refuses_oversized_shapes_on_the_host():
+    """moe_route_noalloc checks the shape against its fixed 64 MiB scratch before it touches the
+    GPU: at d=7168, N_r=256 the routing scratch outgrows the array above T = 52330."""
+    lib = binding.raw_lib()
+    fake = ctypes.c_void_p(0x1000)
+    s = moe.make_shape(52331, 7168, 256, 8, 1, 2048, moe.MOE_DTYPE_BF16)
+    assert lib.moe_route_noalloc(ctypes.byref(s), fake, fake, fake, fake, fake, fake, None) == 3
+    s = moe.make_shape(64, 128, 16, 4, 1, 64, moe.MOE_DTYPE_BF16)
+    assert lib.moe_route_noalloc(ctypes.byref(s), fake, fake, fake, fake, fake, None, None) == 1   # no expert_load
