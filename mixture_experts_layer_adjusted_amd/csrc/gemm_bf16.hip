@@ -277,6 +277,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint16_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_base), 16, 0, 0);
 }
 
+// The same 16-byte-per-lane load into LDS in buffer form: address = base + voff + soff, with soff
+// wave-uniform (the K-step's byte offset).  A raw buffer of 2^32 - 1 bytes covers every 32-bit
+// offset the kernels form (the launchers check that their operands stay below 4 GiB).  Measured
+// 2-4% faster than the global form on the same tiles.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ void lds_buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_base), 16, voff, soff, 0, 0);
+}
+
+#ifndef MOE_BUFFER_LOADS
+#define MOE_BUFFER_LOADS 1
+#endif
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   // s_waitcnt with vmcnt = N (split field on gfx9: bits 3:0 and 15:14), expcnt and lgkmcnt not waited
@@ -962,20 +977,33 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
     }
   };
   int issued = 0, consumed = 0;
+  const __amdgpu_buffer_rsrc_t act_buf = raw_buffer(act);
   auto issue = [&](int kt) {
     uint16_t* st = lds + (issued % C::kStages) * C::kStageElems;
     const int k0 = kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < C::kADma; ++i)
-      lds_dma16(act + k0 + aoff[i], st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
+    for (int i = 0; i < C::kADma; ++i) {
+      uint16_t* dst = st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK;
+      if (MOE_BUFFER_LOADS)
+        lds_buf16(act_buf, aoff[i], (uint32_t)k0, dst);
+      else
+        lds_dma16(act + k0 + aoff[i], dst);
+    }
     const int kr0 = kt * BK;
     // gate rows come from W0, up rows from W1 (the split falls on a wave boundary); K-major
     // weights advance by BK rows per step, switching matrix at kn_split
-    const char* wb = WKN ? (kr0 < kn_split ? W0 + (int64_t)kr0 * ldw * 2 : W1 + (int64_t)(kr0 - kn_split) * ldw * 2)
-                         : ((SWIGLU && wave * (WROWS / WAVES) >= WROWS / 2) ? W1 : W0) + k0;
+    const char* wm_base = WKN ? (kr0 < kn_split ? W0 : W1)
+                              : ((SWIGLU && wave * (WROWS / WAVES) >= WROWS / 2) ? W1 : W0);
+    const uint32_t wk = WKN ? (uint32_t)((int64_t)(kr0 < kn_split ? kr0 : kr0 - kn_split) * ldw * 2) : (uint32_t)k0;
+    const __amdgpu_buffer_rsrc_t w_buf = raw_buffer(wm_base);
 #pragma unroll
-    for (int i = 0; i < C::kWDma; ++i)
-      lds_dma16(wb + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
+    for (int i = 0; i < C::kWDma; ++i) {
+      uint16_t* dst = st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK;
+      if (MOE_BUFFER_LOADS)
+        lds_buf16(w_buf, woff[i], wk, dst);
+      else
+        lds_dma16(wm_base + wk + woff[i], dst);
+    }
     ++issued;
   };
 
