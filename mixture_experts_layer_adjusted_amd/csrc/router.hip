@@ -65,15 +65,32 @@ __device__ __forceinline__ uint64_t score_key(float c, int e) {
   return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
 }
 
+// one step of a wave-wide 64-bit maximum: v = max(v, v moved by the DPP control `ctrl` over the
+// rows in row_mask); lanes without a source keep their own value, which leaves the maximum as is
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t mlo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t mhi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)mhi << 32) | mlo;
+  return o > v ? o : v;
+}
+
+// maximum of v over the 64 lanes, returned to every lane: running maxima within each row of 16
+// lanes by row shifts of 1, 2, 4 and 8 (lane 15 of a row then holds the row's maximum), row 1
+// and 3 take in the row before through row_bcast:15, rows 2 and 3 take in lane 31 through
+// row_bcast:31, so lane 63 ends with the maximum, read out as a scalar.  DPP moves stay in the
+// VALU; the xor-shuffle form went through the LDS crossbar (ds_bpermute) twice per step.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_max_step<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_max_step<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_max_step<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_max_step<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Group limit (the per-token node limit of the page's cross-node all-to-all section, with the
@@ -272,6 +289,9 @@ constexpr int kLE = 128;           // experts per logits tile
 constexpr int kLBK = 64;           // contraction per K-step
 constexpr int kLStageElems = (kLT + 3 * kLE) * kLBK;  // 64 KB
 constexpr int kTopkTokens = 64;    // tokens per top-K workgroup
+constexpr int kTopkThreads = 1024; // 16 wavefronts, four tokens each: latency of the K rounds of
+                                   // wave-wide maxima hidden across the wavefronts
+static_assert(kTopkTokens * kMaxTopK % 4 == 0 && kTopkTokens % 4 == 0, "picks counted four at a time");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -440,15 +460,16 @@ __global__ void logit_reduce_kernel(const float* __restrict__ z_part, int splits
 
 // top-K over precomputed affinities: one wavefront per token, kTopkTokens tokens per workgroup
 template <int CPL>
-__global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict__ s_in, const float* __restrict__ bias,
-                                                        int T, int N, int K, GroupLimit gl,
-                                                        int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
-                                                        int32_t* __restrict__ partial) {
-  __shared__ int32_t picks[kTopkTokens * kMaxTopK];
-  __shared__ uint32_t gmax[kThreads / 64][64];
+__global__ void __launch_bounds__(kTopkThreads) topk_kernel(const float* __restrict__ s_in,
+                                                            const float* __restrict__ bias, int T, int N, int K,
+                                                            GroupLimit gl, int32_t* __restrict__ idx_out,
+                                                            float* __restrict__ gate_out,
+                                                            int32_t* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) int32_t picks[kTopkTokens * kMaxTopK];
+  __shared__ uint32_t gmax[kTopkThreads / 64][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kTopkTokens;
-  for (int q = tid; q < kTopkTokens * kMaxTopK; q += kThreads) picks[q] = -1;
+  for (int q = tid; q < kTopkTokens * kMaxTopK; q += kTopkThreads) picks[q] = -1;
   float bl[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
@@ -456,7 +477,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
     bl[j] = e < N ? bias[e] : 0.0f;
   }
   __syncthreads();
-  for (int tt = wave; tt < kTopkTokens; tt += kThreads / 64) {
+  for (int tt = wave; tt < kTopkTokens; tt += kTopkThreads / 64) {
     const int t = t0 + tt;
     if (t >= T) break;
     const float* srow = s_in + (int64_t)t * N;
@@ -508,9 +529,13 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
     }
   }
   __syncthreads();
-  for (int e = tid; e < N; e += kThreads) {
+  // the workgroup's picks of each expert, four LDS entries per read (64 K entries, unused ones -1)
+  for (int e = tid; e < N; e += kTopkThreads) {
     int c = 0;
-    for (int q = 0; q < kTopkTokens * K; ++q) c += (picks[q] == e);
+    for (int q = 0; q < kTopkTokens * K; q += 4) {
+      const int4 p = *reinterpret_cast<const int4*>(&picks[q]);
+      c += (p.x == e) + (p.y == e) + (p.z == e) + (p.w == e);
+    }
     partial[(int64_t)blockIdx.x * N + e] = c;
   }
 }
@@ -560,7 +585,7 @@ hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float*
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t blocks = ceil_div(T, kTopkTokens);
-  dim3 grid((unsigned)blocks), block(kThreads);
+  dim3 grid((unsigned)blocks), block(kTopkThreads);
 #define MOE_TOPK_CASE(C) \
   hipLaunchKernelGGL((topk_kernel<C>), grid, block, 0, st, w.scores, bias, T, N, s.top_k, gl, idx, gate, w.partial)
   if (N <= 64) MOE_TOPK_CASE(1);
