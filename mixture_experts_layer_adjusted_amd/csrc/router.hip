@@ -12,7 +12,8 @@
 //     holding consecutive 8-bit slices of its 24-bit significand, so u . e = u . hi + u . mid +
 //     u . lo with every bf16 x bf16 product exact in fp32;
 //  2. logits: one bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16) over tokens x experts with the three
-//     parts as three B operands, 128 x 128 tiles, LDS stages filled by direct global->LDS loads;
+//     parts as three B operands, 128 x 128 tiles on 8 wavefronts (two per SIMD, each 64 tokens x
+//     32 experts of every part), LDS stages filled by direct global->LDS loads;
 //     each 64-wide K-step starts a fresh accumulator that is then added to an fp32 running sum
 //     (blocked summation keeps the logit error near 1e-7 of the sum of |terms|); s = sigmoid(z)
 //     is written to the workspace; with fewer than 128 output tiles (decode-sized batches) the
@@ -288,6 +289,7 @@ constexpr int kLT = 128;           // tokens per logits tile
 constexpr int kLE = 128;           // experts per logits tile
 constexpr int kLBK = 64;           // contraction per K-step
 constexpr int kLStageElems = (kLT + 3 * kLE) * kLBK;  // 64 KB
+constexpr int kLWaves = 8;         // two wavefronts per SIMD
 constexpr int kTopkTokens = 64;    // tokens per top-K workgroup
 constexpr int kTopkThreads = 1024; // 16 wavefronts, four tokens each: latency of the K rounds of
                                    // wave-wide maxima hidden across the wavefronts
@@ -324,22 +326,23 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // logits tile: 256 threads, waves (wm, wn) in 2 x 2 own 64 tokens x 64 experts; two LDS stages
-__global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __restrict__ u,
-                                                            const uint16_t* __restrict__ ehi,
-                                                            const uint16_t* __restrict__ emid,
-                                                            const uint16_t* __restrict__ elo, int T, int d, int N,
-                                                            float* __restrict__ s_out, int nk_per,
-                                                            float* __restrict__ z_part) {
+__global__ void __launch_bounds__(kLWaves * 64) router_logits_kernel(const uint16_t* __restrict__ u,
+                                                                     const uint16_t* __restrict__ ehi,
+                                                                     const uint16_t* __restrict__ emid,
+                                                                     const uint16_t* __restrict__ elo, int T, int d,
+                                                                     int N, float* __restrict__ s_out, int nk_per,
+                                                                     float* __restrict__ z_part) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 grid: 64 tokens x 32 experts (of each part) per wave
   const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
   const int lrow = lane >> 3, lslot = lane & 7;
-  // DMA sources: wave w fills token rows [32w, 32w+32) and, for each part, expert rows [32w, 32w+32)
-  const uint16_t* src[16];
+  // DMA sources: wave w fills token rows [16w, 16w+16) and, for each part, expert rows [16w, 16w+16)
+  const uint16_t* src[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wave * 32 + i * 8 + lrow;
+  for (int i = 0; i < 2; ++i) {
+    const int row = wave * 16 + i * 8 + lrow;
     const int t = min(t0 + row, T - 1);  // rows past T: any valid row (outputs discarded)
     src[i] = u + (int64_t)t * d + ((lslot ^ rswz(row)) << 3);
   }
@@ -347,32 +350,30 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
   for (int p = 0; p < 3; ++p) {
     const uint16_t* base = p == 0 ? ehi : (p == 1 ? emid : elo);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wave * 32 + i * 8 + lrow;         // expert row within the part
+    for (int i = 0; i < 2; ++i) {
+      const int row = wave * 16 + i * 8 + lrow;         // expert row within the part
       const int lrow_lds = kLT + p * kLE + row;          // LDS row
-      src[4 + p * 4 + i] = base + (int64_t)(e0 + row) * d + ((lslot ^ rswz(lrow_lds)) << 3);
+      src[2 + p * 2 + i] = base + (int64_t)(e0 + row) * d + ((lslot ^ rswz(lrow_lds)) << 3);
     }
   }
   auto issue = [&](int kt) {
     uint16_t* st = lds + (kt & 1) * kLStageElems;
     const int k0 = kt * kLBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + k0, (lds_void_t*)(st + (wave * 32 + i * 8) * kLBK), 16, 0, 0);
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(src[i] + k0, (lds_void_t*)(st + (wave * 16 + i * 8) * kLBK), 16, 0, 0);
 #pragma unroll
     for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds(src[4 + p * 4 + i] + k0,
-                                         (lds_void_t*)(st + (kLT + p * kLE + wave * 32 + i * 8) * kLBK), 16, 0, 0);
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(src[2 + p * 2 + i] + k0,
+                                         (lds_void_t*)(st + (kLT + p * kLE + wave * 16 + i * 8) * kLBK), 16, 0, 0);
   };
-  float zsum[2][2][16];
+  float zsum[2][16];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) zsum[a][b][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) zsum[a][v] = 0.0f;
   const int l32 = lane & 31, khalf = lane >> 5;
   // K-steps [kt0, kt1) of the contraction: all of it, or slice blockIdx.z when it is split
   const int kt0 = blockIdx.z * nk_per, kt1 = min(d / kLBK, kt0 + nk_per);
@@ -382,70 +383,60 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
     __builtin_amdgcn_s_barrier();  // stage kt landed for every wave; stage kt-1 no longer read
     if (kt + 1 < kt1) issue(kt + 1);
     const uint16_t* st = lds + (kt & 1) * kLStageElems;
-    f32x16 acc[2][2];
+    f32x16 acc[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < kLBK / 16; ++kk) {
       const int c = kk * 2 + khalf;
-      bf16x8 tf[2], ef[3][2];
+      bf16x8 tf[2], ef[3];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) tf[mb] = *reinterpret_cast<const bf16x8*>(st + roff(wm * 64 + mb * 32 + l32, c));
 #pragma unroll
       for (int p = 0; p < 3; ++p)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          ef[p][nb] = *reinterpret_cast<const bf16x8*>(st + roff(kLT + p * kLE + wn * 64 + nb * 32 + l32, c));
+        ef[p] = *reinterpret_cast<const bf16x8*>(st + roff(kLT + p * kLE + wn * 32 + l32, c));
 #pragma unroll
       for (int p = 0; p < 3; ++p)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[p][nb], tf[mb], acc[mb][nb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[p], tf[mb], acc[mb], 0, 0, 0);
     }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) zsum[a][b][v] += acc[a][b][v];
+      for (int v = 0; v < 16; ++v) zsum[a][v] += acc[a][v];
   }
-  // lane holds token t0 + 64 wm + 32 mb + l32 and experts e0 + 64 wn + 32 nb + 8 q + 4 khalf + (0..3)
+  // lane holds token t0 + 64 wm + 32 mb + l32 and experts e0 + 32 wn + 8 q + 4 khalf + (0..3)
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int t = t0 + wm * 64 + mb * 32 + l32;
     if (t >= T) continue;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + wn * 32 + q * 8 + khalf * 4;
+      if (z_part) {   // a slice's partial logits, summed in slice order by logit_reduce_kernel
+        float* zrow = z_part + ((int64_t)blockIdx.z * T + t) * N;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = e0 + wn * 64 + nb * 32 + q * 8 + khalf * 4;
-        if (z_part) {   // a slice's partial logits, summed in slice order by logit_reduce_kernel
-          float* zrow = z_part + ((int64_t)blockIdx.z * T + t) * N;
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (e + v < N) zrow[e + v] = zsum[mb][nb][q * 4 + v];
-          continue;
-        }
-        float4 o;
-        o.x = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 0]));
-        o.y = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 1]));
-        o.z = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 2]));
-        o.w = 1.0f / (1.0f + expf(-zsum[mb][nb][q * 4 + 3]));
-        if (e + 3 < N && (N & 3) == 0) {
-          *reinterpret_cast<float4*>(s_out + (int64_t)t * N + e) = o;
-        } else {
-          const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (e + v < N) s_out[(int64_t)t * N + e + v] = ov[v];
-        }
+        for (int v = 0; v < 4; ++v)
+          if (e + v < N) zrow[e + v] = zsum[mb][q * 4 + v];
+        continue;
       }
+      float4 o;
+      o.x = 1.0f / (1.0f + expf(-zsum[mb][q * 4 + 0]));
+      o.y = 1.0f / (1.0f + expf(-zsum[mb][q * 4 + 1]));
+      o.z = 1.0f / (1.0f + expf(-zsum[mb][q * 4 + 2]));
+      o.w = 1.0f / (1.0f + expf(-zsum[mb][q * 4 + 3]));
+      if (e + 3 < N && (N & 3) == 0) {
+        *reinterpret_cast<float4*>(s_out + (int64_t)t * N + e) = o;
+      } else {
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (e + v < N) s_out[(int64_t)t * N + e + v] = ov[v];
+      }
+    }
   }
 }
 
@@ -575,7 +566,7 @@ hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float*
   const int splits = route_logit_splits(s);
   const int nk = d / kLBK, nk_per = (int)ceil_div(nk, splits);
   hipLaunchKernelGGL(router_logits_kernel, dim3((unsigned)ceil_div(T, kLT), (unsigned)(npad / kLE), (unsigned)splits),
-                     dim3(256), lds_bytes, st, u, w.e_hi, w.e_mid, w.e_lo, T, d, N, w.scores, nk_per,
+                     dim3(kLWaves * 64), lds_bytes, st, u, w.e_hi, w.e_mid, w.e_lo, T, d, N, w.scores, nk_per,
                      splits > 1 ? w.zpart : nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (splits > 1) {
