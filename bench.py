@@ -92,7 +92,21 @@ def cpu_baseline(cfg, n_tokens):
     return {"value": n_tokens / wall, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n_tokens} of the {cfg.tokens} tokens: float64 route + layer forward "
                       f"({len(np.unique(idx))} distinct routed experts), {wall:.1f} s; weight generation excluded",
-            "seconds": round(wall, 2)}
+            "seconds": round(wall, 2), "host": host_description()}
+
+
+def host_description():
+    """The CPU the baseline ran on: model name and logical CPU counts (all, and usable by this process)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
 
 
 def measured_peaks(torch):

@@ -9,8 +9,8 @@
 // fp32 scale per 1x128 activation tile and per 128x128 weight block:
 // scale = amax / 448 (the E4M3FN maximum; 1 for an all-zero tile), code = E4M3FN
 // round-to-nearest-even of the correctly rounded fp32 quotient x / scale,
-// saturating at +-448.  The conversion is done in integer arithmetic from the
-// OCP OFP8 bit layout (bias 7, 3 mantissa bits, S.1111.111 = NaN).
+// saturating at +-448, by gfx950's packed conversion instruction (fp8_codec.h;
+// OCP OFP8 layout: bias 7, 3 mantissa bits, S.1111.111 = NaN).
 #include "fp8_codec.h"
 #include "moe_internal.h"
 
