@@ -24,9 +24,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 WORKLOADS = {"v3-prefill-bf16-zipf": 3, "v3-prefill-fp8": 4, "v3-decode-bf16": 2, "mid-bf16": 1}
-# counter summaries of the gate/up GEMM (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)
-TRAFFIC = {"v3-prefill-bf16-zipf": "profiles/traffic_gemm_gate_up_v3_prefill_bf16.json",
-           "v3-prefill-fp8": "profiles/traffic_gemm_gate_up_v3_prefill_fp8.json"}
+# per-kernel counter summaries (rocprofv3: FETCH_SIZE / WRITE_SIZE copy-calibrated, MFMA-busy cycles,
+# clock, L2 hit rate), valid while the library's sources hash to the recorded value
+COUNTERS = {"v3-prefill-bf16-zipf": "profiles/counters_v3_prefill_bf16.json",
+            "v3-prefill-fp8": "profiles/counters_v3_prefill_fp8.json"}
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
@@ -42,25 +43,26 @@ def parse():
     p.add_argument("--no-backward", action="store_true", help="skip the layer-backward timing (and the saved-input pair)")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the measured reference peaks (plain copy, large library GEMMs)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the graph replay and the grouped / balance routing timings (profiled runs then "
+                        "hold only the step's own kernels)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one plain 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return p.parse_args()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the gate/up GEMM from the committed counter summary, or None
-    when there is none or the kernel's source changed since the counters were taken."""
+def measured_counters(workload):
+    """The committed counter summary of this workload, or None when there is none or the library's
+    sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, TRAFFIC.get(workload, ""))
-    if workload not in TRAFFIC or not os.path.exists(path):
+    path = os.path.join(ROOT, COUNTERS.get(workload, ""))
+    if workload not in COUNTERS or not os.path.exists(path):
         return None
     t = json.load(open(path))
     h = hashlib.sha256()
     for f in t["source_files"]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != t["source_sha256"]:
-        return None
-    return t["hbm_bytes_per_launch"]
+    return t if h.hexdigest() == t["source_sha256"] else None
 
 
 def cpu_baseline(cfg, n_tokens):
@@ -72,6 +74,7 @@ def cpu_baseline(cfg, n_tokens):
     from synth import bf16_bits_to_f32, host
 
     f = lambda a: bf16_bits_to_f32(a) if a.dtype == np.uint16 else a  # noqa: E731
+    n_tokens = min(n_tokens, cfg.tokens)
     u = f(host.token_rows(cfg, rows=range(n_tokens)))
     E = host.centroids(cfg)
     b = host.bias_vector(cfg)
@@ -234,26 +237,28 @@ def main():
     ms_step = ms_total / args.steps
 
     # the same step captured once in a HIP graph and replayed (launch overhead removed)
-    gbias = bias.clone()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        moe.moe_route(shape, dev["u"], dev["centroids"], gbias, idx, gate, load, ws)
-        moe.moe_forward(shape, dev["u"], weights, idx, gate, out, ws)
-        moe.moe_update_bias(N, T * K, load, gbias, cfg.gamma)
-    graph.replay()
-    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev_g[0].record(stream)
-    for _ in range(args.steps):
+    graph_ms = None
+    if not args.no_extras:
+        gbias = bias.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.moe_route(shape, dev["u"], dev["centroids"], gbias, idx, gate, load, ws)
+            moe.moe_forward(shape, dev["u"], weights, idx, gate, out, ws)
+            moe.moe_update_bias(N, T * K, load, gbias, cfg.gamma)
         graph.replay()
-    ev_g[1].record(stream)
-    torch.cuda.synchronize()
-    graph_ms = ev_g[0].elapsed_time(ev_g[1]) / args.steps
-    del graph
+        ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev_g[0].record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        ev_g[1].record(stream)
+        torch.cuda.synchronize()
+        graph_ms = round(ev_g[0].elapsed_time(ev_g[1]) / args.steps, 4)
+        del graph
 
     # group-limited routing (8 equal expert groups, 4 eligible per token) on the same batch and
     # bias, timed outside the step: the cost of the limit next to the plain route
     route_grouped = None
-    if N % 8 == 0 and 4 * (N // 8) >= K:
+    if N % 8 == 0 and 4 * (N // 8) >= K and not args.no_extras:
         gidx, ggate, gload = torch.empty_like(idx), torch.empty_like(gate), torch.empty_like(load)
         ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         reps = 10
@@ -273,7 +278,7 @@ def main():
     # routing plus the sequence-wise balance statistic (sequences of up to 4096 tokens)
     route_balance = None
     seq = min(T, 4096)
-    if T % seq == 0:
+    if T % seq == 0 and not args.no_extras:
         bl = torch.empty((T // seq,), dtype=torch.float32, device="cuda")
         bidx, bgate, bload = torch.empty_like(idx), torch.empty_like(gate), torch.empty_like(load)
         ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -384,10 +389,18 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
 
-    def hbm(nbytes, ms):
+    counters = measured_counters(args.workload)
+
+    def hbm(nbytes, ms, stage):
         gbs = nbytes / (ms * 1e-3) / 1e9
-        return {"bytes": int(nbytes), "ms": round(ms, 4), "achieved_GBs": round(gbs, 1),
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        out_s = {"bytes": int(nbytes), "ms": round(ms, 4), "achieved_GBs": round(gbs, 1),
+                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if counters and stage in counters["stage_bytes"]:
+            # the stage kernels' measured traffic (FETCH + WRITE, copy-calibrated) over the same time
+            tb = counters["stage_bytes"][stage]
+            out_s["traffic_bytes"] = tb
+            out_s["traffic_GBs"] = round(tb / (ms * 1e-3) / 1e9, 1)
+        return out_s
 
     # algorithmic bytes of the memory-side stages (the row gather of the permutation is fused
     # into the gate/up GEMM's loads, so the permutation itself only moves indices)
@@ -395,11 +408,11 @@ def main():
     permute_bytes = T * K * 4 + N * 4 + 2 * rows * 4
     quant_bytes = T * d * (elem + 1) + T * (d // 128) * 4
     combine_bytes = T * d * elem * (K + Ns + 2) + T * K * 8
-    hbm_stages = {"route": hbm(route_bytes, float(st[:, 0].mean())),
-                  "permute": hbm(permute_bytes, float(st[:, 1].mean())),
-                  "combine": hbm(combine_bytes, float(st[:, 5].mean()))}
+    hbm_stages = {"route": hbm(route_bytes, float(st[:, 0].mean()), "route"),
+                  "permute": hbm(permute_bytes, float(st[:, 1].mean()), "permute"),
+                  "combine": hbm(combine_bytes, float(st[:, 5].mean()), "combine")}
     if cfg.dtype == "fp8":
-        hbm_stages["quantize_act"] = hbm(quant_bytes, float(st[:, 2].mean()))
+        hbm_stages["quantize_act"] = hbm(quant_bytes, float(st[:, 2].mean()), "quantize_act")
     route_ms = float(st[:, 0].mean())
     # the logit contraction runs as three bf16 MFMA products (hi, mid, lo parts of the centroids)
     route_compute = {"flops_fp32_equivalent": flops_router,
@@ -418,7 +431,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_median": round(float(np.median(step_ms_all)), 4),
-        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_ms_per_step": graph_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -429,7 +442,10 @@ def main():
         "tflops": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
         "mfma_peak_frac_step": round(flops_step / (ms_step * 1e-3) / 1e12 / peak, 4),
         "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", **roof,
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": counters["hbm_bytes_per_launch_gate_up"] if counters else None,
+                     "counters": {k: counters["kernels"][counters["gate_up_gemm"]].get(k)
+                                  for k in ("mfma_busy_frac", "clock_GHz", "l2_hit_rate", "l2_read_latency_cycles")}
+                     if counters else None,
                      "avg_ms": round(g1_ms, 4), "flops_per_launch": flops_gemm1,
                      "algorithmic_bytes_per_launch": int(g1_bytes),
                      "mfma_bound_ms": round(t_mfma * 1e3, 4), "hbm_bound_ms": round(t_hbm * 1e3, 4),
