@@ -671,9 +671,7 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   static_assert(!SWIGLU || NBW % 2 == 0, "SwiGLU pairs gate and up blocks");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   // ---- logical tile of this workgroup (see the file comment)
-  const int b = blockIdx.x;
-  constexpr int kSpan = kXcds * C::kXcdChunk;
-  const int64_t L = (int64_t)(b / kSpan) * kSpan + (b % kXcds) * C::kXcdChunk + (b / kXcds) % C::kXcdChunk;
+  const int64_t L = xcd_logical(blockIdx.x, C::kXcdChunk);
   int seg, nt, tile_rows, nk;
   int64_t m0;
   {
@@ -683,15 +681,11 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
     if (seg < 0) return;
     const int seg_first = TM == kTileM ? g.seg_off[seg] / kTileM : g.pair_off[seg];
     const int seg_count = TM == kTileM ? g.seg_off[seg + 1] / kTileM - seg_first : g.pair_off[seg + 1] - seg_first;
-    const int64_t lam = L - (int64_t)seg_first * NT;
-    const int grp = (int)(lam / (kGroupM * NT));
-    const int gm = min(kGroupM, seg_count - grp * kGroupM);
-    const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
-    const int local = grp * kGroupM + rem % gm;
-    nt = rem / gm;
-    m0 = (int64_t)g.seg_off[seg] + (int64_t)local * TM;
     // rows of this tile that belong to the segment (a half tile has 128)
-    tile_rows = TM == kTileM ? TM : min(TM, g.seg_off[seg + 1] - (int)(m0));
+    const WalkTile t = walk_tile(L, NT, kGroupM, TM, seg_first, seg_count, g.seg_off[seg], g.seg_off[seg + 1]);
+    nt = t.nt;
+    m0 = t.m0;
+    tile_rows = t.tile_rows;
     nk = g.K / BK;
   }
 
@@ -886,7 +880,7 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
   const int64_t lda = K, ldw = WKN ? N : K;
   const int G = gridDim.x;
   const int max_slots = (int)g.max_tiles;
-  int L = (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds);
+  int L = persistent_first((int)blockIdx.x, G);
 
   struct Tile {
     int seg, nt, tile_rows;
@@ -918,15 +912,13 @@ __global__ void __launch_bounds__(512) grouped_gemm_bf16_persistent_kernel(GemmO
     if (seg < 0) return t;
     const int seg_first = __builtin_amdgcn_readfirstlane(s_pair_off[seg]);
     const int seg_count = __builtin_amdgcn_readfirstlane(s_pair_off[seg + 1]) - seg_first;
-    const int lam = l - seg_first * NT;
-    const int grp = lam / (kGroupM * NT);
-    const int gm = min(kGroupM, seg_count - grp * kGroupM);
-    const int rem = lam - grp * kGroupM * NT;
-    const int local = grp * kGroupM + rem % gm;
+    const WalkTile w = walk_tile(l, NT, kGroupM, TM, seg_first, seg_count,
+                                 __builtin_amdgcn_readfirstlane(s_seg_off[seg]),
+                                 __builtin_amdgcn_readfirstlane(s_seg_off[seg + 1]));
     t.seg = seg;
-    t.nt = rem / gm;
-    t.m0 = (int64_t)__builtin_amdgcn_readfirstlane(s_seg_off[seg]) + (int64_t)local * TM;
-    t.tile_rows = min(TM, __builtin_amdgcn_readfirstlane(s_seg_off[seg + 1]) - (int)t.m0);
+    t.nt = w.nt;
+    t.m0 = w.m0;
+    t.tile_rows = w.tile_rows;
     return t;
   };
   // per-lane load sources of the tile being loaded (as in the streaming kernel)
@@ -1146,11 +1138,11 @@ hipError_t launch_persistent(const GemmOperands& g, hipStream_t st) {
   const int NT = (int)ceil_div(g.N, EPI == 0 ? 256 : 128);
   if (g.max_pairs * NT == 0) return hipSuccess;
   if (EPI == 2 && g.N % 128 != 0) return hipErrorInvalidValue;   // dg_part holds N / 128 tiles per row
-  // the walk's tile indices (up to two grid strides past the last tile) and the table slots are int
-  if (g.max_tiles * NT + 2 * (int64_t)n_cu >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   // one workgroup per CU (the LDS stages allow no more), a multiple of the 8 x 32 tile block
   const int64_t span = kXcds * SC::kXcdChunk;
   const int64_t grid = std::max<int64_t>(span, (int64_t)n_cu / span * span);
+  // the walk's tile indices (up to two grid strides past the last tile) and the table slots are int
+  if (g.max_tiles * NT + 2 * grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds_bytes, st, g, NT);
   return hipGetLastError();
 }
@@ -1180,7 +1172,7 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
   const int MT = (g.wg_m + TM - 1) / TM;
   const int64_t per = (int64_t)MT * NT;
   const int64_t G = gridDim.x;
-  int64_t L = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+  int64_t L = persistent_first((int)blockIdx.x, (int)G);
   if (L >= n_tiles) return;
 
   // The segment table, copied to LDS behind the operand stages: a tile's description then

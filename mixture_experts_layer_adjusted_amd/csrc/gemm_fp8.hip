@@ -169,23 +169,17 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ float row_red[kTM][4];   // per-row reductions across the four wavefronts of a row
   // ---- logical tile (same XCD-aware order as the bf16 streaming kernels, over 256-row tiles)
-  const int b = blockIdx.x;
-  const int64_t L = (int64_t)(b / (kXcds * kXcdChunk)) * (kXcds * kXcdChunk) + (b % kXcds) * kXcdChunk +
-                    (b / kXcds) % kXcdChunk;
+  const int64_t L = xcd_logical(blockIdx.x, kXcdChunk);
   const int64_t slot = L / NT;
   if (slot >= g.max_tiles) return;
   const int seg = g.pair_seg[slot];
   if (seg < 0) return;
   const int seg_first = g.pair_off[seg];
-  const int seg_count = g.pair_off[seg + 1] - seg_first;
-  const int64_t lam = L - (int64_t)seg_first * NT;
-  const int grp = (int)(lam / (kGroupM * NT));
-  const int gm = min(kGroupM, seg_count - grp * kGroupM);
-  const int rem = (int)(lam - (int64_t)grp * kGroupM * NT);
-  const int local = grp * kGroupM + rem % gm;
-  const int nt = rem / gm;
-  const int64_t m0 = (int64_t)g.seg_off[seg] + (int64_t)local * kTM;
-  const int tile_rows = min(kTM, g.seg_off[seg + 1] - (int)m0);  // 256, or 128 for a half tile
+  const WalkTile wt = walk_tile(L, NT, kGroupM, kTM, seg_first, g.pair_off[seg + 1] - seg_first, g.seg_off[seg],
+                                g.seg_off[seg + 1]);
+  const int nt = wt.nt;
+  const int64_t m0 = wt.m0;
+  const int tile_rows = wt.tile_rows;  // 256, or 128 for a half tile
   const int nk = g.K / kBK;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -508,7 +502,7 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
   const int MT = (g.wg_m + kTM - 1) / kTM;
   const int per = MT * NT;
   const int G = gridDim.x;
-  int L = (int)(blockIdx.x % kXcds) * (G / kXcds) + (int)(blockIdx.x / kXcds);
+  int L = persistent_first((int)blockIdx.x, G);
   if (L >= n_tiles) return;
 
   int32_t* seg_off = reinterpret_cast<int32_t*>(lds + kStages * kStageBytes);

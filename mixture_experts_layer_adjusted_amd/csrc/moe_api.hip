@@ -41,8 +41,7 @@ WorkspacePlan plan_workspace(const moe_shape& s) {
   const bool fp8 = s.dtype == MOE_DTYPE_FP8_B128;
   p.route_blocks = ceil_div(T, kRouteTokens);
   p.chunks = ceil_div(T, kChunkTokens);
-  // sum_e ceil(load_e / M) <= (T*K + N*(M-1)) / M, plus N_s full-token segments
-  p.max_tiles = (T * K + N * (kTileM - 1)) / kTileM + Ns * ceil_div(T, kTileM);
+  p.max_tiles = walk_max_tiles(T, K, N, Ns);
   p.max_rows = p.max_tiles * kTileM;
   const size_t A = 256;
   size_t o = 0;
@@ -119,7 +118,7 @@ static moe_status check_shape(const moe_shape* s) {
   if (s->dtype == MOE_DTYPE_FP8_B128 && (s->hidden % 128 != 0 || s->inter % 128 != 0)) return MOE_ERR_UNSUPPORTED;
   const int64_t T = s->tokens, K = s->top_k;
   if (T * K >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
-  const int64_t max_tiles = (T * K + (int64_t)s->n_routed * (kTileM - 1)) / kTileM + s->n_shared * ceil_div(T, kTileM);
+  const int64_t max_tiles = walk_max_tiles(T, K, s->n_routed, s->n_shared);
   if (max_tiles * kTileM >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   // the FP8 GEMMs address u codes [T, d], H codes [rows, I] and one expert's weight codes with
   // 32-bit byte offsets (the bf16 GEMMs fall back to a 64-bit-addressed kernel instead)
@@ -195,7 +194,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.N = s.inter;
   g1.act_rows = s.tokens;
   g1.max_tiles = p.max_tiles;
-  g1.max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + s.n_routed + s.n_shared) / 2);
+  g1.max_pairs = walk_max_pairs(p.max_tiles, s.n_routed + s.n_shared);
   g1.small_segments = (int64_t)s.tokens * s.top_k < (int64_t)kTileM * s.n_routed;
   g1.out = wsb + p.h;
   g1.out_scale = fp8 ? reinterpret_cast<float*>(wsb + p.h_scale) : nullptr;
@@ -414,7 +413,7 @@ static moe_status fp8_backward(const moe_shape& s, const WorkspacePlan& p, char*
   float* dab_ts = reinterpret_cast<float*>(at(p.bwd_dab_ts));
   uint8_t* x_t = reinterpret_cast<uint8_t*>(at(p.bwd_x_t));
   float* x_ts = reinterpret_cast<float*>(at(p.bwd_x_ts));
-  const int64_t max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + Nr + Ns) / 2);
+  const int64_t max_pairs = walk_max_pairs(p.max_tiles, Nr + Ns);
 
   auto wgrad = [&](const uint8_t* a_t, const float* a_s, int M, const uint8_t* b_t, const float* b_s, int N,
                    void* out_r, void* out_s) {
@@ -642,7 +641,7 @@ static moe_status backward_impl(const moe_shape* shape, const void* u, const flo
   };
   const int32_t* pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
   const int32_t* pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
-  const int64_t max_pairs = std::min<int64_t>(p.max_tiles, (p.max_tiles + Nr + Ns) / 2);
+  const int64_t max_pairs = walk_max_pairs(p.max_tiles, Nr + Ns);
   auto grouped = [&](const void* act, const int32_t* rt, int64_t act_rows, const uint16_t* w_r, const uint16_t* w_s,
                      int K, int N, void* out) {
     GemmOperands g{};

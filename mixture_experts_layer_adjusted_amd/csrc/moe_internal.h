@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "tile_walk.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -12,6 +14,7 @@ namespace moe {
 // Rows per M-tile of the grouped GEMMs.  Every expert segment of the permuted
 // layout starts on a multiple of kTileM rows.
 constexpr int kTileM = 128;
+static_assert(kTileM == kWalkTileM, "the tile walk's M-tile");
 // Tokens per routing workgroup, and per permutation chunk.
 constexpr int kRouteTokens = 32;
 constexpr int kChunkTokens = 256;
