@@ -34,7 +34,7 @@
 // 256 weight rows (gate/up: 128 gate + the matching 128 up features; down: 256 output
 // features).  Wavefront (wm, wn) of the 2 x 4 grid owns 128 rows x 64 weight rows as 8 x 4
 // blocks of 16 x 16.  One K-step is one 128-byte scale block of every row, staged in LDS
-// with a 16-byte-chunk XOR swizzle (conflict-free 16-lane reads) by direct global->LDS loads
+// with its 16-byte chunks reordered and XOR-swizzled (conflict-free reads) by direct global->LDS loads
 // one K-step ahead, in the XCD-aware tile order of the bf16 kernels.  The weight-gradient form
 // tiles each segment's M x N output in 256 x 256 blocks.
 #include "fp8_codec.h"
@@ -69,14 +69,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// A staged operand row holds one 128-byte K block as eight 16-byte chunks.  A fragment read
+// gives lane (l16, kq) chunks 2 kq and 2 kq + 1 of row l16, and one 16x16x128 read instruction
+// therefore touches chunks {0, 2, 4, 6} (or {1, 3, 5, 7}) of 16 rows.  Stored in K order that
+// pattern costs the LDS two passes per instruction (measured: 8 LDS cycles per 1 KB read against 4
+// for contiguous or 32-row patterns, under any XOR swizzle of the rows), so chunk 2 kq + h is kept
+// at slot 4 h + kq instead, and each read takes 64 contiguous bytes of every row; the slots of a
+// row are then XOR-swizzled by row / 2 (conflict-free 16-lane reads).  The lanes' registers hold
+// the same bytes as with the plain order.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int kslot(int q) { return ((q & 1) << 2) | (q >> 1); }     // slot of K chunk q
+__device__ __forceinline__ int kchunk(int s) { return ((s & 3) << 1) | (s >> 2); }    // K chunk of slot s
 
 // K-major weight tile (input-gradient products): 128 K rows of 256 feature bytes; the 16-byte
 // feature chunk c of row r sits at slot c ^ kn8_swz(r), so that the 32 rows one transposing read
 // touches (8 j + 0..7 in each K quarter) fall on each bank group twice
 __device__ __forceinline__ int kn8_swz(int r) { return (r & 7) | (((r >> 5) & 1) << 3); }
 __device__ __forceinline__ int kn8_off(int r, int col) { return r * 256 + (((col >> 4) ^ kn8_swz(r)) << 4) + (col & 15); }
-__device__ __forceinline__ int boff(int r, int c) { return r * kBK + ((c ^ swz(r)) << 4); }  // c: 16-byte chunk
+// byte offset of K chunk q of staged row r
+__device__ __forceinline__ int boff(int r, int q) { return r * kBK + ((kslot(q) ^ swz(r)) << 4); }
+// global byte offset, within its row, of the chunk that LDS slot s of row r holds
+__device__ __forceinline__ int src_chunk(int r, int s) { return kchunk(s ^ swz(r)) << 4; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -94,7 +107,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-// 32 bytes of row r starting at 16-byte chunk c (c even): two swizzled 16-byte reads
+// 32 bytes of row r starting at K chunk c (c even): two 16-byte reads
 __device__ __forceinline__ i32x8 frag32(const uint8_t* st, int r, int c) {
   u32x4 a = *reinterpret_cast<const u32x4*>(st + boff(r, c));
   u32x4 b = *reinterpret_cast<const u32x4*>(st + boff(r, c + 1));
@@ -202,7 +215,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
 
   // ---- direct-load sources as 32-bit byte offsets (the launcher checks the sizes): wave w fills
   // activation rows [32w, 32w+32) and weight-tile rows [32w, 32w+32), 8 rows of 128 bytes per
-  // load; lane l covers row l >> 3 of its load and slot l & 7 (logical chunk slot ^ swz(row))
+  // load; lane l covers row l >> 3 of its load and slot l & 7, which holds K chunk src_chunk(row, slot)
   const int lrow = lane >> 3, lslot = lane & 7;
   uint32_t aoff[kADma];
 #pragma unroll
@@ -211,7 +224,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     const int64_t r = m0 + (row < tile_rows ? row : 0);  // rows past a half tile: a valid row
     int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;  // padding row: any valid row (outputs never read)
-    aoff[i] = (uint32_t)(tok * K) + ((lslot ^ swz(row)) << 4);
+    aoff[i] = (uint32_t)(tok * K) + src_chunk(row, lslot);
   }
   uint32_t woff[kWDma];
 #pragma unroll
@@ -227,32 +240,40 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;  // 0..255 within the weight tile
       int n = n0 + (SWIGLU ? (r & (kWRows / 2 - 1)) : r);
       if (n >= N) n = N - 1;  // beyond the last feature: any valid row (outputs masked)
-      woff[i] = (uint32_t)n * (uint32_t)K + ((lslot ^ swz(kTM + r)) << 4);
+      woff[i] = (uint32_t)n * (uint32_t)K + src_chunk(kTM + r, lslot);
     }
   }
   // gate rows (waves 0-3) come from W0, up rows (waves 4-7) from W1
   const uint8_t* wbase = (SWIGLU && wave >= kWaves / 2) ? W1 : W0;
   // ---- scale sources: lanes 0..31 of wave w load the activation scales of rows [32w, 32w+32)
   // into the stage's scale area; wave 7's lanes 32 and 33 load the scales of the tile's two
-  // 128-row weight blocks, landing right after the 256 row scales
-  const float* ssrc = nullptr;
+  // 128-row weight blocks, landing right after the 256 row scales.  The loads are buffer loads
+  // (counted by vmcnt only, so that the waits for the fragment reads can stay partial) at a
+  // per-lane byte offset from the scale array each lane reads: act_scale, S0, or S1 (the up
+  // projection's scales, lane 33 of the SwiGLU forms; K-major weights past kn_split)
+  uint32_t s_off = 0;
   if (lane < 32) {
     const int row = wave * 32 + lane;
     const int64_t r = m0 + (row < tile_rows ? row : 0);
     int64_t tok = g.row_token ? (int64_t)g.row_token[r] : r;
     if (tok < 0) tok = 0;
-    ssrc = g.act_scale + tok * KB;
+    s_off = (uint32_t)(tok * KB) * 4;
   } else if (wave == kWaves - 1 && lane < 34) {
     const int nb = lane - 32;
     if (SWIGLU) {
-      ssrc = (nb == 0 ? S0 : S1) + (size_t)(n0 / kBK) * KB;  // gate block, then the matching up block
+      s_off = (uint32_t)((n0 / kBK) * KB) * 4;  // gate block (S0), then the matching up block (S1)
     } else if (WKN) {
-      ssrc = S0 + min(n0 + nb * kBK, N - 1) / kBK;  // row 0 of the [K/128][N/128] scales; see issue_stage
+      s_off = (uint32_t)(min(n0 + nb * kBK, N - 1) / kBK) * 4;  // row 0 of the [K/128][N/128] scales
     } else {
-      const int n = min(n0 + nb * kBK, N - 1);
-      ssrc = S0 + (size_t)(n / kBK) * KB;
+      s_off = (uint32_t)((min(n0 + nb * kBK, N - 1) / kBK) * KB) * 4;
     }
   }
+  const __amdgpu_buffer_rsrc_t as_buf =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.act_scale), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s0_buf = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(S0), (short)0, -1,
+                                                                         0x00020000);
+  const __amdgpu_buffer_rsrc_t s1_buf =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(S1 ? S1 : S0), (short)0, -1, 0x00020000);
   // operand loads in buffer form (address = base + 32-bit lane offset + the K-step's offset in a
   // scalar; the launcher keeps both matrices below 4 GiB): measured faster than the global form
   const __amdgpu_buffer_rsrc_t act_buf = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(act), (short)0, -1,
@@ -275,13 +296,25 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           w_buf, (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, woff[i], wk, 0,
           0);
-    // every wave has active lanes here, so every wave issues this load; K-major weight scales
-    // step by a row of N/128 blocks per K block
-    const float* sp = ssrc + kt;
-    if (WKN && lane >= 32 && ssrc)
-      sp = kt < kn_split / kBK ? ssrc + (int64_t)kt * (N / kBK)
-                               : (S1 - S0) + ssrc + (int64_t)(kt - kn_split / kBK) * (N / kBK);
-    if (ssrc) __builtin_amdgcn_global_load_lds(sp, (lds_void_t*)(st + kDataBytes + wave * 128), 4, 0, 0);
+    // scales: one dword per lane at the lane's offset plus the K block's (K-major weight scales
+    // step by a row of N/128 blocks per K block)
+    lds_void_t* sdst = (lds_void_t*)(st + kDataBytes + wave * 128);
+    if (lane < 32) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(as_buf, sdst, 4, s_off, (uint32_t)kt * 4, 0, 0);
+    } else if (wave == kWaves - 1 && lane < 34) {
+      if constexpr (WKN) {
+        const int split = kn_split / kBK;
+        if (kt < split)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(s0_buf, sdst, 4, s_off, (uint32_t)(kt * (N / kBK)) * 4, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(s1_buf, sdst, 4, s_off, (uint32_t)((kt - split) * (N / kBK)) * 4,
+                                                   0, 0);
+      } else if (SWIGLU && lane == 33) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s1_buf, sdst, 4, s_off, (uint32_t)kt * 4, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s0_buf, sdst, 4, s_off, (uint32_t)kt * 4, 0, 0);
+      }
+    }
   };
 
   // weight rows of the wave's four 16-row blocks, and the 128-row scale block each falls in
@@ -550,12 +583,12 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
 #pragma unroll
     for (int i = 0; i < kADma; ++i) {
       const int row = wave * (kTM / kWaves) + i * kRowsPerDma + lrow;
-      aoff[i] = (uint32_t)(t.m0 + (row < t.tile_rows ? row : 0)) * lda32 + ((lslot ^ swz(row)) << 4);
+      aoff[i] = (uint32_t)(t.m0 + (row < t.tile_rows ? row : 0)) * lda32 + src_chunk(row, lslot);
     }
 #pragma unroll
     for (int i = 0; i < kWDma; ++i) {
       const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;
-      woff[i] = (uint32_t)min(n0 + r, N - 1) * ldw32 + ((lslot ^ swz(kTM + r)) << 4);
+      woff[i] = (uint32_t)min(n0 + r, N - 1) * ldw32 + src_chunk(kTM + r, lslot);
     }
     act_base = static_cast<const uint8_t*>(g.act) + t.k_base;
     w_base = static_cast<const uint8_t*>(g.w_routed[0]) + t.k_base;
