@@ -326,6 +326,9 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // logits tile: 256 threads, waves (wm, wn) in 2 x 2 own 64 tokens x 64 experts; two LDS stages
+// kBuf: operand loads in buffer form (a base per matrix, 32-bit byte offsets; u below 4 GiB),
+// else in global form
+template <bool kBuf>
 __global__ void __launch_bounds__(kLWaves * 64) router_logits_kernel(const uint16_t* __restrict__ u,
                                                                      const uint16_t* __restrict__ ehi,
                                                                      const uint16_t* __restrict__ emid,
@@ -338,36 +341,47 @@ __global__ void __launch_bounds__(kLWaves * 64) router_logits_kernel(const uint1
   const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 grid: 64 tokens x 32 experts (of each part) per wave
   const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
   const int lrow = lane >> 3, lslot = lane & 7;
-  // DMA sources: wave w fills token rows [16w, 16w+16) and, for each part, expert rows [16w, 16w+16)
-  const uint16_t* src[8];
+  // DMA sources (element offsets from each matrix's base): wave w fills token rows [16w, 16w+16)
+  // and, for each part, expert rows [16w, 16w+16)
+  int64_t off[8];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wave * 16 + i * 8 + lrow;
     const int t = min(t0 + row, T - 1);  // rows past T: any valid row (outputs discarded)
-    src[i] = u + (int64_t)t * d + ((lslot ^ rswz(row)) << 3);
+    off[i] = (int64_t)t * d + ((lslot ^ rswz(row)) << 3);
   }
 #pragma unroll
   for (int p = 0; p < 3; ++p) {
-    const uint16_t* base = p == 0 ? ehi : (p == 1 ? emid : elo);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = wave * 16 + i * 8 + lrow;         // expert row within the part
       const int lrow_lds = kLT + p * kLE + row;          // LDS row
-      src[2 + p * 2 + i] = base + (int64_t)(e0 + row) * d + ((lslot ^ rswz(lrow_lds)) << 3);
+      off[2 + p * 2 + i] = (int64_t)(e0 + row) * d + ((lslot ^ rswz(lrow_lds)) << 3);
     }
+  }
+  const uint16_t* base[4] = {u, ehi, emid, elo};
+  __amdgpu_buffer_rsrc_t buf[4];
+  uint32_t voff[8];
+  if constexpr (kBuf) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) buf[m] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base[m]), (short)0, -1,
+                                                                            0x00020000);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) voff[j] = (uint32_t)(off[j] * 2);
   }
   auto issue = [&](int kt) {
     uint16_t* st = lds + (kt & 1) * kLStageElems;
     const int k0 = kt * kLBK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + k0, (lds_void_t*)(st + (wave * 16 + i * 8) * kLBK), 16, 0, 0);
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(src[2 + p * 2 + i] + k0,
-                                         (lds_void_t*)(st + (kLT + p * kLE + wave * 16 + i * 8) * kLBK), 16, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const int m = j < 2 ? 0 : 1 + (j - 2) / 2;   // matrix: u, then the three parts
+      const int lds_row = j < 2 ? wave * 16 + j * 8 : kLT + (m - 1) * kLE + wave * 16 + (j & 1) * 8;
+      lds_void_t* dst = (lds_void_t*)(st + lds_row * kLBK);
+      if constexpr (kBuf)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buf[m], dst, 16, voff[j], (uint32_t)k0 * 2, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(base[m] + off[j] + k0, dst, 16, 0, 0);
+    }
   };
   float zsum[2][16];
 #pragma unroll
@@ -561,11 +575,13 @@ hipError_t launch_route_mfma(const moe_shape& s, const uint16_t* u, const float*
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t lds_bytes = 2 * kLStageElems * sizeof(uint16_t);
-  if ((err = ensure_dynamic_lds(reinterpret_cast<const void*>(&router_logits_kernel), (int)lds_bytes)) != hipSuccess)
-    return err;
+  // buffer-form loads address u and the split centroids with 32-bit byte offsets
+  const bool buf = (int64_t)T * d * 2 < (int64_t(1) << 32) && npad * d * 2 < (int64_t(1) << 32);
+  auto kern = buf ? &router_logits_kernel<true> : &router_logits_kernel<false>;
+  if ((err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)lds_bytes)) != hipSuccess) return err;
   const int splits = route_logit_splits(s);
   const int nk = d / kLBK, nk_per = (int)ceil_div(nk, splits);
-  hipLaunchKernelGGL(router_logits_kernel, dim3((unsigned)ceil_div(T, kLT), (unsigned)(npad / kLE), (unsigned)splits),
+  hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(T, kLT), (unsigned)(npad / kLE), (unsigned)splits),
                      dim3(kLWaves * 64), lds_bytes, st, u, w.e_hi, w.e_mid, w.e_lo, T, d, N, w.scores, nk_per,
                      splits > 1 ? w.zpart : nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
