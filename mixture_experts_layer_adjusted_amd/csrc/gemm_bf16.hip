@@ -776,7 +776,10 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   }
   const int l32 = lane & 31, khalf = lane >> 5;
   const int mrow0 = wm * RW;
-  const bool active = mrow0 < tile_rows;   // false only for the upper half of a half tile
+  // rows of the tile holding the segment's rows (all of them when no real row counts are given);
+  // a wavefront with none idles (the upper half of a half tile, or segment padding)
+  const int real_rows = g.seg_rows ? min(tile_rows, max(0, g.seg_rows[seg] - (int)(m0 - g.seg_off[seg]))) : tile_rows;
+  const bool active = mrow0 < real_rows;
   constexpr bool kAccInAgprs = MB * NBW * 16 > 128;
 
   constexpr int kAhead = C::kStages - 1;

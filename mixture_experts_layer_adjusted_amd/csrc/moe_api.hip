@@ -186,6 +186,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g1.s_shared[1] = w->sh_up_scale;
   g1.tile_seg = reinterpret_cast<const int32_t*>(wsb + p.tile_seg);
   g1.seg_off = reinterpret_cast<const int32_t*>(wsb + p.seg_off);
+  g1.seg_rows = reinterpret_cast<const int32_t*>(wsb + p.seg_rows);
   g1.pair_seg = reinterpret_cast<const int32_t*>(wsb + p.pair_seg);
   g1.pair_off = reinterpret_cast<const int32_t*>(wsb + p.pair_off);
   g1.n_routed = s.n_routed;
@@ -217,6 +218,7 @@ static moe_status forward_impl(const moe_shape* shape, const void* u, const moe_
   g2.s_shared[0] = w->sh_down_scale;
   g2.tile_seg = g1.tile_seg;
   g2.seg_off = g1.seg_off;
+  g2.seg_rows = g1.seg_rows;
   g2.pair_seg = g1.pair_seg;
   g2.pair_off = g1.pair_off;
   g2.n_routed = s.n_routed;

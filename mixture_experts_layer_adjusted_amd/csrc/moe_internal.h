@@ -125,6 +125,10 @@ struct GemmOperands {
   const float* s_shared[2];
   const int32_t* tile_seg;
   const int32_t* seg_off;    // [N_r + N_s + 1] first padded row of each segment
+  // [N_r + N_s] real rows of each segment, or null.  When given, the one-tile bf16 kernel idles the
+  // wavefronts whose rows all lie in a segment's padding, as it does the upper half of a half tile
+  // (those output rows, which nothing reads, are then not written)
+  const int32_t* seg_rows;
   const int32_t* pair_seg;   // [max_tiles] segment of each 256-row tile (pairs of M-tiles; a segment
                              // with an odd M-tile count ends in a half tile)
   const int32_t* pair_off;   // [N_r + N_s + 1] first 256-row tile of each segment
