@@ -27,7 +27,8 @@ WORKLOADS = {"v3-prefill-bf16-zipf": 3, "v3-prefill-fp8": 4, "v3-decode-bf16": 2
 # per-kernel counter summaries (rocprofv3: FETCH_SIZE / WRITE_SIZE copy-calibrated, MFMA-busy cycles,
 # clock, L2 hit rate), valid while the library's sources hash to the recorded value
 COUNTERS = {"v3-prefill-bf16-zipf": "profiles/counters_v3_prefill_bf16.json",
-            "v3-prefill-fp8": "profiles/counters_v3_prefill_fp8.json"}
+            "v3-prefill-fp8": "profiles/counters_v3_prefill_fp8.json",
+            "v3-decode-bf16": "profiles/counters_v3_decode_bf16.json"}
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
