@@ -114,6 +114,37 @@ def test_determinism_bitwise():
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
 
 
+@pytest.mark.parametrize("cfg", [
+    # decode-sized segments (T K_r < 128 N_r): 128-row tiles whose wavefronts over padding idle
+    _edge("poison-small-segments", 77, 384, 8, 3, 1, 384, cid=85),
+    _edge("poison-decode-like", 64, 256, 64, 4, 1, 256, cid=86),
+    # persistent 256-row tiles, half tiles included
+    _edge("poison-persistent", 1000, 256, 8, 2, 1, 256, cid=87),
+    _edge("poison-fp8", 200, 256, 16, 4, 1, 128, dtype="fp8", cid=88),
+], ids=lambda c: c.name)
+def test_forward_ignores_poisoned_workspace(cfg):
+    """A workspace filled with zeros, then with 0xFF bytes (NaN in every bf16, fp32 and E4M3
+    slot) before route + forward gives bit-identical, finite routing and outputs: no padding row,
+    unwritten row or row past the last segment reaches a token's output."""
+    print(f"poisoned workspace: {cfg.name} T={cfg.tokens} N={cfg.n_routed} K={cfg.top_k} {cfg.dtype}", flush=True)
+    dev = host_to_device(host.make_host_inputs(cfg))
+    if cfg.dtype == "fp8":
+        dev = quantize_fp8_weights(dev, cfg)
+    r = Runner(cfg, dev)
+    outs = []
+    for fill in (0x00, 0xFF):
+        r.ws.fill_(fill)
+        r.out.view(torch.uint8).fill_(fill)
+        r.route()
+        r.forward()
+        outs.append((r.idx.clone(), r.gate.clone(), r.out.clone()))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[1][2].float()).all()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+    assert torch.equal(outs[0][2].view(torch.uint8), outs[1][2].view(torch.uint8))
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("cfg", [
