@@ -14,8 +14,8 @@
 //  2. logits: one bf16 MFMA GEMM (v_mfma_f32_32x32x16_bf16) over tokens x experts with the three
 //     parts as three B operands, 128 x 128 tiles on 8 wavefronts (two per SIMD, each 64 tokens x
 //     32 experts of every part), LDS stages filled by direct global->LDS loads;
-//     each 64-wide K-step starts a fresh accumulator that is then added to an fp32 running sum
-//     (blocked summation keeps the logit error near 1e-7 of the sum of |terms|); s = sigmoid(z)
+//     every two 64-wide K-steps start a fresh accumulator that is then added to an fp32 running
+//     sum (blocked summation keeps the logit error near 1e-7 of the sum of |terms|); s = sigmoid(z)
 //     is written to the workspace; with fewer than 128 output tiles (decode-sized batches) the
 //     contraction splits into up to 16 K-slices whose partial logits a second kernel adds in
 //     slice order;
@@ -39,6 +39,8 @@
 //  4. the workgroup's picks are counted per expert by a plain scan of its LDS
 //     copy (no atomics) and written as one row of partial counts; a second
 //     kernel sums the partial rows in a fixed order into expert_load.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -392,16 +394,20 @@ __global__ void __launch_bounds__(kLWaves * 64) router_logits_kernel(const uint1
   // K-steps [kt0, kt1) of the contraction: all of it, or slice blockIdx.z when it is split
   const int kt0 = blockIdx.z * nk_per, kt1 = min(d / kLBK, kt0 + nk_per);
   if (kt0 < kt1) issue(kt0);   // a slice past the end contributes zeros
-  for (int kt = kt0; kt < kt1; ++kt) {
+  // one K-step's MFMAs on stage kt into acc (which the first of them starts from zero when
+  // `fresh`); the partial logits of every two K-steps are then added to the fp32 running sum
+  f32x16 acc[2];
+  auto kstep = [&](int kt, auto fresh) {
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();  // stage kt landed for every wave; stage kt-1 no longer read
     if (kt + 1 < kt1) issue(kt + 1);
     const uint16_t* st = lds + (kt & 1) * kLStageElems;
-    f32x16 acc[2];
+    if constexpr (decltype(fresh)::value) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
+    }
 #pragma unroll
     for (int kk = 0; kk < kLBK / 16; ++kk) {
       const int c = kk * 2 + khalf;
@@ -417,6 +423,10 @@ __global__ void __launch_bounds__(kLWaves * 64) router_logits_kernel(const uint1
         for (int mb = 0; mb < 2; ++mb)
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[p], tf[mb], acc[mb], 0, 0, 0);
     }
+  };
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    kstep(kt, std::true_type{});
+    if (kt + 1 < kt1) kstep(kt + 1, std::false_type{});
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
