@@ -51,7 +51,7 @@ constexpr int kWRows = 256;
 constexpr int kStages = 2;
 constexpr int kDataBytes = (kTM + kWRows) * kBK;      // 64 KB of operands per stage
 constexpr int kScaleBytes = 2048;                      // 256 row scales + 2 weight-block scales, padded
-constexpr int kStageBytes = kDataBytes + kScaleBytes;
+constexpr int kStageBytes = kDataBytes + kScaleBytes;   // per stage of the ring, operands and scales
 constexpr int kRowsPerDma = 8;                         // 128-byte rows one wave-wide 1 KB load fills
 constexpr int kADma = kTM / kRowsPerDma / kWaves;      // 4
 constexpr int kWDma = kWRows / kRowsPerDma / kWaves;   // 4
@@ -91,6 +91,28 @@ __device__ __forceinline__ int boff(int r, int q) { return r * kBK + ((kslot(q) 
 // global byte offset, within its row, of the chunk that LDS slot s of row r holds
 __device__ __forceinline__ int src_chunk(int r, int s) { return kchunk(s ^ swz(r)) << 4; }
 
+// LDS ring of the forward and input-gradient kernels: kStages operand stages of kDataBytes,
+// then kStages scale areas of kScaleBytes.  An operand stage then spans exactly 64 KB, so each
+// fragment read below is a per-lane base plus a constant within the LDS instructions' 16-bit
+// offset, and a K-step adds its stage's start to four bases (measured: the SwiGLU GEMM's integer
+// VALU per K-step 34 -> 6 instructions, 2-4% faster at T=8192).
+__device__ __forceinline__ int stage_off(int s) { return (s % kStages) * kDataBytes; }
+__device__ __forceinline__ int scale_off(int s) { return kStages * kDataBytes + (s % kStages) * kScaleBytes; }
+
+// Byte offsets, within a stage, of the two 16-byte halves (K chunks 2 kq and 2 kq + 1) of the
+// lane's fragment of token block 0 (rows mrow0 + l16) and weight block 0 (weight-tile rows
+// wrow0 + l16).  mrow0, wrow0 and kTM are multiples of 16, so every row 16 b + l16 has the
+// swizzle of l16 and block b lies 16 b rows further on.
+struct FragBase {
+  uint32_t x0, x1, w0, w1;
+};
+__device__ __forceinline__ FragBase frag_base(int mrow0, int wrow0, int l16, int kq) {
+  const int s = swz(l16);
+  const uint32_t c0 = (uint32_t)((kslot(2 * kq) ^ s) << 4), c1 = (uint32_t)((kslot(2 * kq + 1) ^ s) << 4);
+  const uint32_t xr = (uint32_t)(mrow0 + l16) * kBK, wr = (uint32_t)(kTM + wrow0 + l16) * kBK;
+  return {xr + c0, xr + c1, wr + c0, wr + c1};
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
@@ -111,6 +133,13 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ i32x8 frag32(const uint8_t* st, int r, int c) {
   u32x4 a = *reinterpret_cast<const u32x4*>(st + boff(r, c));
   u32x4 b = *reinterpret_cast<const u32x4*>(st + boff(r, c + 1));
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// the same 32 bytes from the halves at st + o0 + off and st + o1 + off (o0, o1 from frag_base)
+__device__ __forceinline__ i32x8 frag_at(const uint8_t* st, uint32_t o0, uint32_t o1, int off) {
+  u32x4 a = *reinterpret_cast<const u32x4*>(st + o0 + off);
+  u32x4 b = *reinterpret_cast<const u32x4*>(st + o1 + off);
   return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
@@ -279,7 +308,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   const __amdgpu_buffer_rsrc_t act_buf = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(act), (short)0, -1,
                                                                           0x00020000);
   auto issue_stage = [&](int kt) {
-    uint8_t* st = lds + (kt % kStages) * kStageBytes;
+    uint8_t* st = lds + stage_off(kt);
     const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < kADma; ++i)
@@ -298,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
           0);
     // scales: one dword per lane at the lane's offset plus the K block's (K-major weight scales
     // step by a row of N/128 blocks per K block)
-    lds_void_t* sdst = (lds_void_t*)(st + kDataBytes + wave * 128);
+    lds_void_t* sdst = (lds_void_t*)(lds + scale_off(kt) + wave * 128);
     if (lane < 32) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(as_buf, sdst, 4, s_off, (uint32_t)kt * 4, 0, 0);
     } else if (wave == kWaves - 1 && lane < 34) {
@@ -332,6 +361,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   const int l16 = lane & 15, kq = lane >> 4;  // token of the 16x16 block; K quarter and feature group
   const int mrow0 = wm * (kTM / 2);
   const bool active = mrow0 < tile_rows;      // false only for the upper half of a half tile
+  const int wrow0 = wrow[0];                  // wrow[nb] - wrow0 is a constant
+  const FragBase fb = frag_base(mrow0, wrow0, l16, kq);
 
   f32x4 acc[kMB][kNB];
 #pragma unroll
@@ -347,8 +378,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
     __builtin_amdgcn_s_barrier();
     if (kt + 1 < nk) issue_stage(kt + 1);
     if (active) {
-      const uint8_t* st = lds + (kt % kStages) * kStageBytes;
-      const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
+      const uint8_t* st = lds + stage_off(kt);
+      const float* sc = reinterpret_cast<const float*>(lds + scale_off(kt));
       i32x8 wf[kNB];
       float sw[kNB];
 #pragma unroll
@@ -369,22 +400,22 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
           }
           wf[nb] = f;
         } else {
-          wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
+          wf[nb] = frag_at(st, fb.w0, fb.w1, (wrow[nb] - wrow0) * kBK);
         }
         sw[nb] = sc[kTM + wblk[nb]];
       }
       // token fragments one block ahead, so that each block's LDS reads are in flight while the
       // previous block's MFMAs run
-      i32x8 xf_next = frag32(st, mrow0 + l16, kq * 2);
-      float sa_next = sc[mrow0 + l16];
+      const float* sa_row = sc + mrow0 + l16;
+      i32x8 xf_next = frag_at(st, fb.x0, fb.x1, 0);
+      float sa_next = sa_row[0];
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         const i32x8 xf = xf_next;
         const float sa = sa_next;
         if (mb + 1 < kMB) {
-          const int rn = mrow0 + (mb + 1) * 16 + l16;
-          xf_next = frag32(st, rn, kq * 2);
-          sa_next = sc[rn];
+          xf_next = frag_at(st, fb.x0, fb.x1, (mb + 1) * 16 * kBK);
+          sa_next = sa_row[(mb + 1) * 16];
         }
         // plain-store form: keeps the compiler from sinking those reads below the MFMAs (which it
         // otherwise does, exposing each block's LDS latency again; down GEMM 2.12 -> 2.02 ms at
@@ -505,8 +536,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_kernel(GemmOperands
   } else {
     // whole row spans through stage nk mod 2: the last K-step read the other stage, and every
     // wavefront passed that step's barrier after its reads of this one (nk = 1: never used)
-    store_tile_staged16(acc, lds + (nk % kStages) * kStageBytes, static_cast<uint16_t*>(g.out), m0, n0, N, tile_rows,
-                        wave, wm, wn, lane);
+    store_tile_staged16(acc, lds + stage_off(nk), static_cast<uint16_t*>(g.out), m0, n0, N, tile_rows, wave, wm, wn,
+                        lane);
   }
 }
 
@@ -608,7 +639,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_persistent_kernel(G
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.act_scale), (short)0, -1, 0x00020000);
   // K-step kt of the prepared tile into LDS stage `stage`
   auto issue = [&](int kt, int stage) {
-    uint8_t* st = lds + (stage % kStages) * kStageBytes;
+    uint8_t* st = lds + stage_off(stage);
     const uint32_t k0 = (uint32_t)kt * kBK;
 #pragma unroll
     for (int i = 0; i < kADma; ++i)
@@ -622,7 +653,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_persistent_kernel(G
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           w_buf, (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, woff[i], k0, 0,
           0);
-    lds_void_t* sdst = (lds_void_t*)(st + kDataBytes + wave * 128);
+    lds_void_t* sdst = (lds_void_t*)(lds + scale_off(stage) + wave * 128);
     if (lane < 32) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(as_buf, sdst, 4, s_off, (uint32_t)kt * 4, 0, 0);
     } else if (wave == kWaves - 1 && lane < 34) {
@@ -641,6 +672,7 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_persistent_kernel(G
   }
   const int l16 = lane & 15, kq = lane >> 4;
   const int mrow0 = wm * (kTM / 2);
+  const FragBase fb = frag_base(mrow0, wrow[0], l16, kq);
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   int L = persistent_first((int)blockIdx.x, G);
@@ -669,27 +701,27 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_persistent_kernel(G
       wait_vmcnt<0>();
     auto compute = [&]() {
       if (active) {
-        const uint8_t* st = lds + (step % kStages) * kStageBytes;
-        const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
+        const uint8_t* st = lds + stage_off(step);
+        const float* sc = reinterpret_cast<const float*>(lds + scale_off(step));
         i32x8 wf[kNB];
         float sw[kNB];
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-          wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
+          wf[nb] = frag_at(st, fb.w0, fb.w1, nb * 16 * kBK);
           sw[nb] = sc[kTM + wblk[nb]];
         }
         // token fragments one block ahead, so that each block's LDS reads are in flight while the
         // previous block's MFMAs run
-        i32x8 xf_next = frag32(st, mrow0 + l16, kq * 2);
-        float sa_next = sc[mrow0 + l16];
+        const float* sa_row = sc + mrow0 + l16;
+        i32x8 xf_next = frag_at(st, fb.x0, fb.x1, 0);
+        float sa_next = sa_row[0];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
           const i32x8 xf = xf_next;
           const float sa = sa_next;
           if (mb + 1 < kMB) {
-            const int rn = mrow0 + (mb + 1) * 16 + l16;
-            xf_next = frag32(st, rn, kq * 2);
-            sa_next = sc[rn];
+            xf_next = frag_at(st, fb.x0, fb.x1, (mb + 1) * 16 * kBK);
+            sa_next = sa_row[(mb + 1) * 16];
           }
           __builtin_amdgcn_sched_barrier(0);   // as in the one-tile plain-store form
 #pragma unroll
@@ -731,8 +763,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_fp8_persistent_kernel(G
     // whole row spans through the stage the last K-step read (the next tile's first K-step fills
     // the other one), once every wavefront is done reading it
     lds_barrier();
-    stores_behind = store_tile_staged16(acc, lds + ((step - 1) % kStages) * kStageBytes, static_cast<uint16_t*>(g.out),
-                                        cur.m0, cur.nt * kWRows, N, cur.tile_rows, wave, wm, wn, lane);
+    stores_behind = store_tile_staged16(acc, lds + stage_off(step - 1), static_cast<uint16_t*>(g.out), cur.m0,
+                                        cur.nt * kWRows, N, cur.tile_rows, wave, wm, wn, lane);
     const Tile nxt = describe(Ln, seg_next);
     if (nxt.seg < 0) break;
     cur = nxt;
