@@ -86,8 +86,6 @@ __device__ __forceinline__ int kchunk(int s) { return ((s & 3) << 1) | (s >> 2);
 // touches (8 j + 0..7 in each K quarter) fall on each bank group twice
 __device__ __forceinline__ int kn8_swz(int r) { return (r & 7) | (((r >> 5) & 1) << 3); }
 __device__ __forceinline__ int kn8_off(int r, int col) { return r * 256 + (((col >> 4) ^ kn8_swz(r)) << 4) + (col & 15); }
-// byte offset of K chunk q of staged row r
-__device__ __forceinline__ int boff(int r, int q) { return r * kBK + ((kslot(q) ^ swz(r)) << 4); }
 // global byte offset, within its row, of the chunk that LDS slot s of row r holds
 __device__ __forceinline__ int src_chunk(int r, int s) { return kchunk(s ^ swz(r)) << 4; }
 
@@ -129,14 +127,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-// 32 bytes of row r starting at K chunk c (c even): two 16-byte reads
-__device__ __forceinline__ i32x8 frag32(const uint8_t* st, int r, int c) {
-  u32x4 a = *reinterpret_cast<const u32x4*>(st + boff(r, c));
-  u32x4 b = *reinterpret_cast<const u32x4*>(st + boff(r, c + 1));
-  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-}
-
-// the same 32 bytes from the halves at st + o0 + off and st + o1 + off (o0, o1 from frag_base)
+// 32 bytes of a staged row, K chunks 2 kq and 2 kq + 1: the halves at st + o0 + off and
+// st + o1 + off (o0, o1 from frag_base)
 __device__ __forceinline__ i32x8 frag_at(const uint8_t* st, uint32_t o0, uint32_t o1, int off) {
   u32x4 a = *reinterpret_cast<const u32x4*>(st + o0 + off);
   u32x4 b = *reinterpret_cast<const u32x4*>(st + o1 + off);
@@ -827,12 +819,11 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
     return t;
   };
   // per-lane load sources of the tile being loaded (as in grouped_gemm_fp8_kernel): 32-bit byte
-  // offsets from the wave-uniform bases act_base / w_base; lanes 0..31 load activation-row scales,
-  // lanes 32..63 weight-row scales, wave w's 64 dwords landing at [64w, 64w + 64)
-  uint32_t aoff[kADma], woff[kWDma];
-  const uint8_t* act_base = nullptr;
-  const uint8_t* w_base = nullptr;
-  const float* ssrc = nullptr;
+  // offsets; waves 0-3 load the scales of activation rows [64w, 64w + 64) into scale slots
+  // [64w, 64w + 64), waves 4-7 those of weight rows [64(w - 4), 64(w - 4) + 64) into slots
+  // 256 + the row (one scale array per wave, so that the array is wave-uniform)
+  uint32_t aoff[kADma], woff[kWDma], s_off = 0;
+  int k_base = 0;   // the tile's first K column (segment start), the loads' scalar offset base
   // (32-bit offset arithmetic: the launcher checks wg_m * lda and N * ldw against 2^32)
   const uint32_t lda32 = (uint32_t)lda, ldw32 = (uint32_t)ldw;
   auto prepare = [&](const Tile& t) {
@@ -852,38 +843,52 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
       const int r = wave * (kWRows / kWaves) + i * kRowsPerDma + lrow;
       woff[i] = (uint32_t)min(n0 + r, N - 1) * ldw32 + src_chunk(kTM + r, lslot);
     }
-    act_base = static_cast<const uint8_t*>(g.act) + t.k_base;
-    w_base = static_cast<const uint8_t*>(g.w_routed[0]) + t.k_base;
-    if (ln < 32) {
-      const int row = wave * 32 + ln;
-      ssrc = g.act_scale + (int64_t)(t.m0 + (row < t.tile_rows ? row : 0)) * (lda / kBK) + t.k_base / kBK;
-    } else {
-      ssrc = g.s_routed[0] + (int64_t)min(n0 + wave * 32 + ln - 32, N - 1) * (ldw / kBK) + t.k_base / kBK;
-    }
+    k_base = t.k_base;
+    // scale byte offsets (before the K block): activation rows from act_scale, weight rows from
+    // s_routed[0]
+    const int srow = (wave & 3) * 64 + ln;
+    if (wave < 4)
+      s_off = (uint32_t)(t.m0 + (srow < t.tile_rows ? srow : 0)) * (lda32 / kBK) * 4;
+    else
+      s_off = (uint32_t)min(n0 + srow, N - 1) * (ldw32 / kBK) * 4;
   };
+  // operand and scale loads in buffer form: a wave-uniform base, the lane's 32-bit offset and the
+  // K-step's offset in a scalar
+  const __amdgpu_buffer_rsrc_t act_buf =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.act), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_buf =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.w_routed[0]), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t as_buf =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.act_scale), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ws_buf =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.s_routed[0]), (short)0, -1, 0x00020000);
   int issued = 0, consumed = 0;
   auto issue = [&](int kt) {
-    uint8_t* st = lds + (issued % kStages) * kStageBytes;
-    const int k0 = kt * kBK;
+    uint8_t* st = lds + stage_off(issued);
+    const uint32_t k0 = (uint32_t)(k_base + kt * kBK);
 #pragma unroll
     for (int i = 0; i < kADma; ++i)
-      __builtin_amdgcn_global_load_lds(act_base + k0 + aoff[i],
-                                       (lds_void_t*)(st + (wave * (kTM / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
-                                       0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(act_buf,
+                                               (lds_void_t*)(st + (wave * (kTM / kWaves) + i * kRowsPerDma) * kBK),
+                                               16, aoff[i], k0, 0, 0);
 #pragma unroll
     for (int i = 0; i < kWDma; ++i)
-      __builtin_amdgcn_global_load_lds(
-          w_base + k0 + woff[i], (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, 0,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_buf, (lds_void_t*)(st + (kTM + wave * (kWRows / kWaves) + i * kRowsPerDma) * kBK), 16, woff[i], k0, 0,
           0);
-    __builtin_amdgcn_global_load_lds(ssrc + kt, (lds_void_t*)(st + kDataBytes + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 4 ? as_buf : ws_buf,
+                                             (lds_void_t*)(lds + scale_off(issued) + wave * 256), 4, s_off,
+                                             (uint32_t)(k_base / kBK + kt) * 4, 0, 0);
     ++issued;
   };
 
-  int wrow[kNB];
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) wrow[nb] = wn * 64 + nb * 16;
   const int l16 = lane & 15, kq = lane >> 4;
   const int mrow0 = wm * (kTM / 2);
+  const FragBase fb = frag_base(mrow0, wn * 64, l16, kq);
+  // scale slots of activation row mrow0 + 16 mb + l16 and of the lane's four weight rows
+  // wn * 64 + 16 nb + 4 kq + (0..3)
+  const int sa_base = mrow0 + l16;
+  const int sw_base = kTM + wn * 64 + 4 * kq;
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   Tile cur = describe(L);
@@ -926,27 +931,25 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
       else
         prefetch_next();
       if (active) {
-        const uint8_t* st = lds + (consumed % kStages) * kStageBytes;
-        const float* sc = reinterpret_cast<const float*>(st + kDataBytes);
+        const uint8_t* st = lds + stage_off(consumed);
+        const float* sc = reinterpret_cast<const float*>(lds + scale_off(consumed));
         i32x8 wf[kNB];
         f32x4 swr[kNB];   // scales of the lane's four weight rows (one group of 32)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-          wf[nb] = frag32(st, kTM + wrow[nb] + l16, kq * 2);
-          const int j = wrow[nb] + kq * 4;
-          swr[nb] = *reinterpret_cast<const f32x4*>(sc + 64 * (j >> 5) + 32 + (j & 31));
+          wf[nb] = frag_at(st, fb.w0, fb.w1, nb * 16 * kBK);
+          swr[nb] = *reinterpret_cast<const f32x4*>(sc + sw_base + 16 * nb);
         }
         // token fragments one block ahead (as in grouped_gemm_fp8_kernel)
-        i32x8 xf_next = frag32(st, mrow0 + l16, kq * 2);
-        float sa_next = sc[64 * ((mrow0 + l16) >> 5) + ((mrow0 + l16) & 31)];
+        i32x8 xf_next = frag_at(st, fb.x0, fb.x1, 0);
+        float sa_next = sc[sa_base];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
           const i32x8 xf = xf_next;
           const float sa = sa_next;
           if (mb + 1 < kMB) {
-            const int rn = mrow0 + (mb + 1) * 16 + l16;
-            xf_next = frag32(st, rn, kq * 2);
-            sa_next = sc[64 * (rn >> 5) + (rn & 31)];
+            xf_next = frag_at(st, fb.x0, fb.x1, (mb + 1) * 16 * kBK);
+            sa_next = sc[sa_base + (mb + 1) * 16];
           }
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
@@ -976,7 +979,7 @@ __global__ void __launch_bounds__(kThreads) grouped_wgrad_fp8_kernel(GemmOperand
       const int e = shared ? cur.seg - g.n_routed : cur.seg;
       uint16_t* out = static_cast<uint16_t*>(shared ? g.out2 : g.out) + (int64_t)e * g.wg_m * N;
       lds_barrier();   // every wavefront is done reading the stage
-      stores_behind = store_tile_staged16(acc, lds + (issued % kStages) * kStageBytes, out, cur.m0, cur.nt * kWRows, N,
+      stores_behind = store_tile_staged16(acc, lds + stage_off(issued), out, cur.m0, cur.nt * kWRows, N,
                                           cur.tile_rows, wave, wm, wn, lane);
     }
     if (!has_next) break;
