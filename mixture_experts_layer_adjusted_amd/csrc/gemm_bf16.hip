@@ -744,19 +744,21 @@ __global__ void __launch_bounds__(WAVES * 64, WGS) grouped_gemm_bf16_stream_kern
   }
   // gate rows come from W0, up rows from W1; the split falls on a wave boundary
   const char* wbase = (SWIGLU && wave * (WROWS / WAVES) >= WROWS / 2) ? W1 : W0;
+  const __amdgpu_buffer_rsrc_t act_buf = raw_buffer(act);
   auto issue_stage = [&](int kt) {
     uint16_t* st = lds + (kt % C::kStages) * C::kStageElems;
     const int k0 = kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < C::kADma; ++i)
-      lds_dma16(act + k0 + aoff[i], st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
+      lds_buf16(act_buf, aoff[i], (uint32_t)k0, st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
     // K-major weights advance by BK rows per step, switching matrix at kn_split
     const int kr0 = kt * BK;
-    const char* wb = !WKN ? wbase + k0
-                          : (kr0 < kn_split ? W0 + (int64_t)kr0 * ldw * 2 : W1 + (int64_t)(kr0 - kn_split) * ldw * 2);
+    const char* wm_base = !WKN ? wbase : (kr0 < kn_split ? W0 : W1);
+    const uint32_t wk = !WKN ? (uint32_t)k0 : (uint32_t)((int64_t)(kr0 < kn_split ? kr0 : kr0 - kn_split) * ldw * 2);
+    const __amdgpu_buffer_rsrc_t w_buf = raw_buffer(wm_base);
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i)
-      lds_dma16(wb + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
+      lds_buf16(w_buf, woff[i], wk, st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
   };
 
   f32x16 acc[MB][NBW];
@@ -1210,8 +1212,7 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
   // per-lane load sources of the tile being loaded, as in the streaming kernel
   const int lrow = lane / C::kChunks, lslot = lane % C::kChunks;
   uint32_t aoff[C::kADma], woff[C::kWDma];
-  const char* act_base = nullptr;
-  const char* w_base = nullptr;
+  uint32_t k_bytes = 0;   // the tile's first K column (segment start) in bytes: the loads' scalar offset
   auto prepare = [&](const Tile& t) {
     const int n0 = t.nt * WROWS;
 #pragma unroll
@@ -1224,19 +1225,22 @@ __global__ void __launch_bounds__(512) grouped_wgrad_bf16_kernel(GemmOperands g,
       const int r = wave * (WROWS / WAVES) + i * C::kRowsPerDma + lrow;
       woff[i] = (uint32_t)((int64_t)min(n0 + r, N - 1) * ldw * 2) + ((lslot ^ C::swz(TM + r)) << 4);
     }
-    act_base = static_cast<const char*>(g.act) + t.k_base * 2;
-    w_base = static_cast<const char*>(g.w_routed[0]) + t.k_base * 2;
+    k_bytes = (uint32_t)(t.k_base * 2);
   };
+  // buffer-form loads: wave-uniform bases, the lane's 32-bit offset, the K offset in a scalar (the
+  // launcher keeps both operand matrices below 4 GiB)
+  const __amdgpu_buffer_rsrc_t act_buf = raw_buffer(g.act);
+  const __amdgpu_buffer_rsrc_t w_buf = raw_buffer(g.w_routed[0]);
   int issued = 0, consumed = 0;
   auto issue = [&](int kt) {
     uint16_t* st = lds + (issued % C::kStages) * C::kStageElems;
-    const int k0 = kt * BK * 2;
+    const uint32_t k0 = k_bytes + (uint32_t)(kt * BK * 2);
 #pragma unroll
     for (int i = 0; i < C::kADma; ++i)
-      lds_dma16(act_base + k0 + aoff[i], st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
+      lds_buf16(act_buf, aoff[i], k0, st + (wave * (TM / WAVES) + i * C::kRowsPerDma) * BK);
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i)
-      lds_dma16(w_base + k0 + woff[i], st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
+      lds_buf16(w_buf, woff[i], k0, st + (TM + wave * (WROWS / WAVES) + i * C::kRowsPerDma) * BK);
     ++issued;
   };
 
@@ -1429,8 +1433,9 @@ hipError_t launch_gemm_bf16_wgrad(const GemmOperands& g, hipStream_t st) { retur
 hipError_t launch_gemm_bf16_dgrad(const GemmOperands& g, hipStream_t st) {
   if (g.K % 64 != 0 || g.N % 128 != 0 || g.kn_split % 64 != 0 || g.kn_split <= 0 || g.kn_split > g.K)
     return hipErrorInvalidValue;
-  // 32-bit byte offsets: the activation matrix; the weight offsets stay within one stage's rows
-  if (g.act_rows * g.K * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  // 32-bit byte offsets: the activation matrix and one stacked weight matrix (K rows of N)
+  if (g.act_rows * g.K * 2 >= (int64_t(1) << 32) || (int64_t)g.N * g.K * 2 >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
   if (MOE_PERSISTENT_GEMM) return launch_persistent<0, true>(g, st);
   return launch_stream<0, 64, 8, 256, 1, 2, 256, true>(g, st);
 }

@@ -543,8 +543,11 @@ static moe_status check_backward_shape(const moe_shape* s) {
       ((int64_t)s->tokens * s->top_k + (int64_t)s->n_routed * (kTileM - 1)) / kTileM * kTileM +
       (int64_t)s->n_shared * ceil_div(s->tokens, kTileM) * kTileM;
   const int64_t widest = std::max<int64_t>(s->hidden, 2 * (int64_t)s->inter);
-  if (max_rows * widest * 2 >= (int64_t(1) << 32) || (int64_t)s->tokens * s->hidden * 2 >= (int64_t(1) << 32))
+  const int64_t lim = int64_t(1) << 32;
+  if (max_rows * widest * 2 >= lim || (int64_t)s->tokens * s->hidden * 2 >= lim)
     return MOE_ERR_UNSUPPORTED;
+  // the input-gradient products read one expert's stacked weights [d, 2I] (bf16) at 32-bit offsets
+  if ((int64_t)s->hidden * 2 * s->inter * 2 >= lim) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
