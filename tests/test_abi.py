@@ -113,6 +113,12 @@ def test_null_and_workspace_errors_before_launch():
     assert lib.moe_backward_workspace_size(ctypes.byref(moe.make_shape(64, 256, 16, 4, 1, 192, moe.MOE_DTYPE_FP8_B128)),
                                            ctypes.byref(n8)) == 2                           # I % 128
     assert lib.moe_backward(ctypes.byref(s8), *args, fake, big, None) == 1                  # no weight scales
+    # one expert's stacked bf16 weights [d, 2I] beyond 32-bit byte offsets: refused up front (a few
+    # tokens keep every activation matrix small)
+    wide = moe.make_shape(1, 65536, 16, 4, 1, 16384, moe.MOE_DTYPE_BF16)
+    assert lib.moe_backward_workspace_size(ctypes.byref(wide), ctypes.byref(n)) == 2
+    narrow = moe.make_shape(1, 65536, 16, 4, 1, 16256, moe.MOE_DTYPE_BF16)
+    assert lib.moe_backward_workspace_size(ctypes.byref(narrow), ctypes.byref(n)) == 0
     # FP8 shapes whose operands exceed the GEMMs' 32-bit byte offsets are refused up front
     huge = moe.make_shape(700000, 7168, 256, 8, 1, 2048, moe.MOE_DTYPE_FP8_B128)
     assert lib.moe_workspace_size(ctypes.byref(huge), ctypes.byref(n8)) == 2
