@@ -16,7 +16,7 @@
 //    segments hold few rows (decode-like batches).  Each wavefront computes 128 x 64 with
 //    v_mfma_f32_32x32x16_bf16; the MFMA's A operand is the weight tile and its B operand the
 //    activation tile, so a lane ends with runs of four consecutive output features of one row.
-//    Two 64 KB LDS stages are filled by direct global->LDS loads (global_load_lds_dwordx4) one
+//    Two 64 KB LDS stages are filled by direct loads into LDS (buffer_load_dwordx4 ... lds) one
 //    K-step ahead; LDS rows are XOR-swizzled in 16-byte chunks so that fragment reads are free
 //    of bank conflicts.  Tiles come in an XCD-aware order: the 8 XCDs of MI355X each receive
 //    workgroups round-robin, so workgroup b runs on XCD b % 8, and logical tiles are handed out
